@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the deflated-ASP NVFP4 W4A4 linear on one MI355X.
+
+One step = the whole per-call path (fused activation prep + 4-bit GEMM with
+the low-rank/bias epilogue) for every layer of the workload, on inputs and
+packed weights already resident in HBM.  The weight packing is offline (once
+per layer) and outside the timed region.  Steps rotate through replicas of
+every buffer (>= 1 GiB in total) so that each step reads from HBM rather than
+from the 256 MB Infinity Cache.
+
+Timing: W warm-up steps, then exactly K steps replayed from one HIP graph,
+bracketed by synchronize() and HIP events on the capture stream.  A second,
+eager pass brackets every kernel launch with HIP events (launch backlog built
+first, so events bracket kernels back to back) to get each kernel's average
+duration for the roofline figure.
+
+Prints one JSON line.  Default workload: the action-expert attention
+projection pair (two layers, M=256 tokens, K=N=1024, rank 32, bf16 in and out).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "deflated-ASP NVFP4 linear effective TFLOP/s + % of roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
+RIDGE = F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def layer_flops(M, N, K, r):
+    """Algorithmic FLOPs of one layer call: 2MNK + 2MKr (u) + 2MKr (deflation) + 2MNr (low rank)."""
+    return 2 * M * N * K + 4 * M * K * r + 2 * M * N * r
+
+
+def layer_bytes(M, N, K, r, xb, yb):
+    """Minimum HBM bytes of one layer call: x, y, codes, scales, W~V, V, s, b (no FP4 activation)."""
+    return M * K * xb + M * N * yb + N * K // 2 + N * K // 16 + 2 * N * r + 4 * K * r + 4 * K + 4 * N
+
+
+def prep_bytes(M, K, r, xb):
+    """Algorithmic bytes of one activation-prep launch: x, s, V in; codes, scales, u out."""
+    return M * K * xb + 4 * K + 4 * K * r + M * K // 2 + M * K // 16 + 4 * M * r
+
+
+def gemm_bytes(M, N, K, r, yb):
+    """Algorithmic bytes of one GEMM launch: both operands' codes and scales, u, W~V, bias, y."""
+    return (M * K // 2 + M * K // 16 + 4 * M * r + N * K // 2 + N * K // 16 + 2 * N * r + 4 * N
+            + M * N * yb)
+
+
+def gemm_flops(M, N, K, r):
+    return 2 * M * N * K + 2 * M * N * r
+
+
+def prep_flops(M, K, r):
+    return 4 * M * K * r
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
+    ap.add_argument("--min-replica-gib", type=float, default=1.0)
+    ap.add_argument("--kernel-timing-steps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle CPU baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the layer shards by token rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from wam_asp_w4a4_amd import binding as B
+    from wam_asp_w4a4_amd import synth
+    from wam_asp_w4a4_amd.layer import PackedLayer
+
+    if not os.path.exists(B.LIB_PATH):
+        from wam_asp_w4a4_amd import build as _build
+        _build.build()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    layers = synth.workload(args.workload)
+    y_dtype = "bf16"
+    yb = 2
+
+    # ---- pack once per layer on the host, upload R replicas of every buffer
+    host = []
+    for lay in layers:
+        pk = PackedLayer.pack_host(lay.w, lay.s, lay.v)
+        xh = synth.bf16_bits(lay.x) if lay.x_dtype == "bf16" else lay.x
+        host.append((lay, pk, xh))
+
+    def replica_bytes():
+        tot = 0
+        for lay, pk, xh in host:
+            tot += xh.nbytes + pk["w_codes"].nbytes + pk["w_scales"].nbytes
+            tot += 0 if pk["wv"] is None else pk["wv"].nbytes
+            tot += lay.M * lay.N * yb + B.asp_workspace_bytes(lay.M, lay.K, lay.r)
+        return tot
+
+    per = replica_bytes()
+    R = int(min(512, max(2, np.ceil(args.min_replica_gib * 2 ** 30 / per))))
+
+    def t(a, dtype=None):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        return (x.view(dtype) if dtype is not None else x).to(dev)
+
+    replicas = []
+    for _ in range(R):
+        rep = []
+        shared_x = {}
+        for lay, pk, xh in host:
+            key = id(lay.x)
+            if key not in shared_x:  # layers that share x share it within a replica
+                shared_x[key] = t(xh, torch.bfloat16 if lay.x_dtype == "bf16" else None)
+            p = PackedLayer(lay.N, lay.K, lay.r, t(pk["w_codes"]), t(pk["w_scales"]),
+                            None if pk["wv"] is None else t(pk["wv"], torch.int16),
+                            None if lay.v is None else t(lay.v), t(lay.s), t(lay.b))
+            y = torch.empty((lay.M, lay.N), dtype=torch.bfloat16, device=dev)
+            ws = p.workspace(lay.M)
+            rep.append((lay, p, shared_x[key], y, ws))
+        replicas.append(rep)
+
+    def step(i):
+        for lay, p, x, y, ws in replicas[i % R]:
+            p.forward(x, y_dtype, workspace=ws, y=y)
+
+    # ---- warm-up, then K steps from one graph
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    flops_step = sum(layer_flops(l.M, l.N, l.K, l.r) for l, _, _ in host)
+    bytes_step = sum(layer_bytes(l.M, l.N, l.K, l.r, 2 if l.x_dtype == "bf16" else 4, yb)
+                     for l, _, _ in host)
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-kernel durations with events around every launch (eager, backlogged)
+    nk = max(1, min(args.kernel_timing_steps, args.steps))
+    big = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    timings = {"prep": [], "gemm": []}
+    evs = []
+    torch.cuda.synchronize()
+    for _ in range(8 + nk // 4):  # GPU backlog so the launches below queue up
+        big = big @ big
+        big = big / big.abs().amax().clamp_min(1.0)
+    for i in range(nk):
+        for lay, p, x, y, ws in replicas[i % R]:
+            M, N, K, r = lay.M, lay.N, lay.K, lay.r
+            xc = ws[: M * K // 2]
+            off = (M * K // 2 + 255) // 256 * 256
+            xs = ws[off: off + M * K // 16]
+            off2 = off + (M * K // 16 + 255) // 256 * 256
+            u = ws[off2: off2 + 4 * M * r].view(torch.float32) if r else None
+            ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            ea.record(stream)
+            B.asp_act_prep(x, B.DTYPES[lay.x_dtype], M, K, r, p.s, p.v, xc, xs, u, None)
+            eb.record(stream)
+            B.asp_gemm_lowrank(xc, xs, u, M, N, K, r, p.w_codes, p.w_scales, p.wv, p.bias, y,
+                               B.DTYPES[y_dtype])
+            ec.record(stream)
+            evs.append((lay, ea, eb, ec))
+    torch.cuda.synchronize()
+    prep_ms = gemm_ms = 0.0
+    prep_b = gemm_b = prep_f = gemm_f = 0
+    for lay, ea, eb, ec in evs:
+        xb = 2 if lay.x_dtype == "bf16" else 4
+        prep_ms += ea.elapsed_time(eb)
+        gemm_ms += eb.elapsed_time(ec)
+        prep_b += prep_bytes(lay.M, lay.K, lay.r, xb)
+        gemm_b += gemm_bytes(lay.M, lay.N, lay.K, lay.r, yb)
+        prep_f += prep_flops(lay.M, lay.K, lay.r)
+        gemm_f += gemm_flops(lay.M, lay.N, lay.K, lay.r)
+    n_launch = len(evs)
+    if gemm_ms >= prep_ms:
+        name, ms, nbytes, nflops = "k_gemm", gemm_ms, gemm_b, gemm_f
+    else:
+        name, ms, nbytes, nflops = "k_act_prep", prep_ms, prep_b, prep_f
+    avg_us = ms / n_launch * 1e3
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = nflops / (ms * 1e-3) / 1e12
+    ai = nflops / nbytes
+    if ai >= RIDGE:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfs / F16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof.update({
+        "traffic": None,
+        "kernel": name,
+        "avg_launch_us": round(avg_us, 3),
+        "launches": n_launch,
+        "algorithmic_bytes_per_launch": nbytes // n_launch,
+        "algorithmic_flops_per_launch": nflops // n_launch,
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_f16_frac": round(tfs / F16_PEAK_TFLOPS, 4),
+        "other_kernel_avg_us": round((prep_ms if name == "k_gemm" else gemm_ms) / n_launch * 1e3, 3),
+    })
+
+    # ---- CPU baseline: the oracle, on the host cores, on a bounded sample
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(layers, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": synth.WORKLOADS[args.workload],
+            "layers": [{"name": l.name, "M": l.M, "K": l.K, "N": l.N, "r": l.r,
+                        "x": l.x_dtype, "y": y_dtype} for l, _, _ in host],
+            "operands": "NVFP4 (E2M1, block 16, E4M3 scales) decoded to exact fp16 for MFMA, fp32 accumulate",
+            "flops_per_step": flops_step,
+            "algorithmic_bytes_per_step": bytes_step,
+            "effective_GBps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+            "replicas": R,
+            "replica_bytes": per,
+            "timing": "one HIP graph of K steps, events on the capture stream",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, budget_s):
+    """Time the oracle's per-call path (activation side + NVFP4 contraction) on the host."""
+    from oracle import asp as oracle_asp
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    packed = [oracle_asp.pack_weight(l.w, l.s, l.v) for l in layers]
+    flops = sum(layer_flops(l.M, l.N, l.K, l.r) for l in layers)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for lay, pk in zip(layers, packed):
+            oracle_asp.forward(lay.x, lay.w, lay.b, lay.s, lay.v, packed=pk)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    return {"value": round(flops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full steps of the same workload (float64 NumPy oracle, weights "
+                      f"pre-packed), {el:.1f} s; cores = BLAS threads"}
+
+
+if __name__ == "__main__":
+    main()

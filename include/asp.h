@@ -1,0 +1,202 @@
+/*
+ * asp.h -- C ABI of libasp: the deflated Action-Subspace-Protection (ASP)
+ * NVFP4 W4A4 linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (model card "FastWAM UR3 3-task -- 4-bit quantisations",
+ * section "What ASP is, and what the deflated form means"; Q-WAM abstract):
+ * for one linear layer with weight W (N x K), bias b (N), smoothing vector s
+ * (K), block Hadamard H and protected basis V (K x r, orthonormal columns),
+ *
+ *     x_tilde = (x / s) H                                (activation side)
+ *     u       = x_tilde V
+ *     y       = u (W_tilde V)^T
+ *             + NVFP4GEMM( x_tilde - u V^T , W_tilde (I - V V^T) )
+ *             + b,            with W_tilde = W diag(s) H  (weight side)
+ *
+ * NVFP4 (same page, method table): E2M1 elements in blocks of 16 consecutive
+ * K elements with one E4M3 scale per block, for both operands.  The low-rank
+ * branch stays in bf16 (same section): u and W_tilde V are rounded to bf16
+ * for their product; the deflation uses the unrounded u.
+ *
+ * Readings this library takes where the pages are silent:
+ *   - H: blocks of 128 consecutive channels, Sylvester order, 1/sqrt(128);
+ *   - block scale S = E4M3FN(amax/6), round to nearest even, saturating at
+ *     448 (no per-tensor second-level scale); element code = E2M1(|v|/S),
+ *     round to nearest, ties to the even code, saturating at 6, sign copied
+ *     from v (a zero scale gives magnitude 0 for the whole block);
+ *   - the deflated operands are rounded to float32 before quantisation.
+ *
+ * Conventions for every entry point:
+ *   - Row-major, K contiguous.  Row vectors: x is M x K, y is M x N.
+ *   - Packed codes: row of `cols` elements -> cols/2 bytes; byte j holds
+ *     element 2j in bits [3:0] and element 2j+1 in bits [7:4].
+ *   - Block scales: one E4M3FN byte per 16 consecutive elements,
+ *     [rows][cols/16].
+ *   - bf16 values are passed as uint16_t bit patterns.
+ *   - Every call returns an asp_status (int32_t).  Nothing throws across the
+ *     ABI.  On failure asp_last_error() gives a thread-local description.
+ *     Arguments are fully validated before anything is launched or written.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller.  The library
+ *     never allocates, frees or retains caller memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device entry
+ *     points only enqueue work and return; faults raised while kernels run
+ *     surface at the caller's next synchronisation with that stream.
+ *   - Device pointers must be 16-byte aligned.  Inputs must be finite.
+ *   - Supported shapes: K a positive multiple of 128; M >= 0 (M == 0 is a
+ *     no-op); N >= 1; 0 <= r <= 64.
+ */
+#ifndef ASP_H
+#define ASP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ASP_OK 0
+#define ASP_ERR_ARG 1         /* null pointer, unknown dtype, bad count */
+#define ASP_ERR_SHAPE 2       /* shape outside the supported set */
+#define ASP_ERR_ALIGN 3       /* device pointer not 16-byte aligned */
+#define ASP_ERR_UNSUPPORTED 4 /* valid request this build does not handle */
+#define ASP_ERR_WORKSPACE 5   /* workspace too small */
+#define ASP_ERR_HIP 6         /* a HIP runtime call failed (launch, query) */
+#define ASP_ERR_INTERNAL 7
+
+/* Element types of x and y. */
+#define ASP_F32 0
+#define ASP_BF16 1
+
+#define ASP_HADAMARD_BLOCK 128
+#define ASP_QUANT_BLOCK 16
+#define ASP_MAX_RANK 64
+
+/* ABI revision of this header; bumps on any signature change. */
+int32_t asp_abi_version(void);
+
+/* Static text for a status code. */
+const char* asp_status_string(int32_t status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* asp_last_error(void);
+
+/* ------------------------------------------------------------------ host */
+
+/*
+ * Bytes of the packed weight buffers for an N x K layer of rank r:
+ * codes N*K/2, scales N*K/16, low-rank factor N*r*2 (bf16).  These are the
+ * model card's 4.00 bits per weight for the codes plus 0.5 bits for the E4M3
+ * scales ("Verification -- NVFP4 deflated ASP", residency table).
+ */
+int32_t asp_packed_sizes(int64_t N, int64_t K, int32_t r, size_t* code_bytes,
+                         size_t* scale_bytes, size_t* wv_bytes);
+
+/*
+ * Host-side weight packer (once per layer; CPU, synchronous).
+ * Computes, in float64, W_tilde = W diag(s) H, L = W_tilde V and the deflated
+ * weight W_d = W_tilde - L V^T (model card, "What ASP is, and what the
+ * deflated form means": the 4-bit weight holds W_tilde (I - V V^T), the
+ * low-rank branch the exact W_tilde V kept in bf16).  W_d is rounded to
+ * float32 and NVFP4-quantised row-wise along K; L is rounded to bf16.
+ *   w          host, N x K float32
+ *   s          host, K float32, all > 0
+ *   v          host, K x r float32 (NULL iff r == 0)
+ *   w_codes    host out, N x K/2 bytes
+ *   w_scales   host out, N x K/16 bytes
+ *   wv         host out, N x r bf16 bits (NULL allowed iff r == 0)
+ *   w_prequant host out, N x K float32 W_d before quantisation, or NULL
+ *   n_threads  worker threads (<= 0: one per hardware thread)
+ */
+int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
+                        const float* s, const float* v, uint8_t* w_codes,
+                        uint8_t* w_scales, uint16_t* wv, float* w_prequant,
+                        int32_t n_threads);
+
+/*
+ * NVFP4 quantiser on the host (the packer's last step, exposed for checks):
+ * rows x cols float32 -> codes (rows x cols/2) and scales (rows x cols/16).
+ * cols must be a positive multiple of 16.  All pointers host.
+ */
+int32_t asp_quantize_nvfp4_host(const float* in, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales);
+
+/* ---------------------------------------------------------------- device */
+
+/*
+ * NVFP4 quantiser on the GPU: same arithmetic and layout as the host one.
+ *   in (device, rows x cols float32) -> codes, scales (device).
+ */
+int32_t asp_quantize_nvfp4(const float* in, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * NVFP4 dequantiser on the GPU: out[i][j] = E2M1(code) * E4M3(scale), float32
+ * (exact: every such product is a float32 value).  All pointers device.
+ */
+int32_t asp_dequantize_nvfp4(const uint8_t* codes, const uint8_t* scales,
+                             int64_t rows, int64_t cols, float* out,
+                             void* stream);
+
+/*
+ * Fused activation prep (every call): smooth-divide x/s, block Hadamard,
+ * u = x_tilde V, deflation x_tilde - u V^T, NVFP4 quantise and pack
+ * (model card, "What ASP is, and what the deflated form means").
+ *   x         device, M x K, element type x_dtype (ASP_F32 or ASP_BF16)
+ *   s         device, K float32
+ *   v         device, K x r float32 (NULL iff r == 0)
+ *   x_codes   device out, M x K/2;  x_scales device out, M x K/16
+ *   u         device out, M x r float32 (NULL allowed iff r == 0)
+ *   prequant  device out, M x K float32 deflated activation before
+ *             quantisation, or NULL (a check hook; costs bandwidth)
+ */
+int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                     int32_t r, const float* s, const float* v,
+                     uint8_t* x_codes, uint8_t* x_scales, float* u,
+                     float* prequant, void* stream);
+
+/*
+ * 4-bit GEMM with fused low-rank and bias epilogue:
+ *   y = DQ(x_codes, x_scales) DQ(w_codes, w_scales)^T + bf16(u) wv^T + bias
+ * The NVFP4 operands are decoded in registers to exact fp16 values (an E2M1
+ * value times an E4M3 scale has at most 6 significant bits) and contracted
+ * on MFMA with float32 accumulation; no dequantised copy of either operand
+ * is written to memory (model card, "Verification -- NVFP4 deflated ASP":
+ * no dequantised weight copy anywhere).
+ *   x_codes, x_scales  device, M x K/2, M x K/16 (asp_act_prep output)
+ *   u                  device, M x r float32 (NULL iff r == 0)
+ *   w_codes, w_scales  device, N x K/2, N x K/16 (asp_pack_weight output)
+ *   wv                 device, N x r bf16 bits (NULL iff r == 0)
+ *   bias               device, N float32, or NULL for none
+ *   y                  device out, M x N, element type y_dtype
+ */
+int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales,
+                         const float* u, int64_t M, int64_t N, int64_t K,
+                         int32_t r, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const uint16_t* wv,
+                         const float* bias, void* y, int32_t y_dtype,
+                         void* stream);
+
+/* Workspace bytes asp_forward needs for M rows (activation codes, scales, u). */
+int32_t asp_workspace_bytes(int64_t M, int64_t K, int32_t r, size_t* bytes);
+
+/*
+ * The whole layer on the GPU: asp_act_prep then asp_gemm_lowrank, enqueued
+ * on `stream`, with the activation codes, scales and u in the caller's
+ * workspace (device, at least asp_workspace_bytes bytes, 256-byte aligned).
+ * Weight-side arguments are asp_pack_weight's outputs uploaded to the device.
+ */
+int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N,
+                    int64_t K, int32_t r, const float* s, const float* v,
+                    const uint8_t* w_codes, const uint8_t* w_scales,
+                    const uint16_t* wv, const float* bias, void* y,
+                    int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ASP_H */

@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every entry point of include/asp.h and
+validates arguments on the host (CPU only: no call here reaches a GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from wam_asp_w4a4_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "asp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(asp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for must in ("asp_pack_weight", "asp_act_prep", "asp_gemm_lowrank", "asp_forward",
+                 "asp_quantize_nvfp4", "asp_dequantize_nvfp4"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing
+    # and the binding wraps each one under the same name
+    assert set(_declared_functions()) <= set(B.SIGNATURES)
+    for n in _declared_functions():
+        assert callable(getattr(B, n))
+
+
+def test_version_and_status_strings():
+    assert B.asp_abi_version() == 1
+    assert B.asp_status_string(0) == "ASP_OK"
+    assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
+    assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
+
+
+def test_sizes_are_four_and_a_half_bits_per_weight():
+    c, s, w = B.asp_packed_sizes(4096, 3072, 32)
+    assert c * 8 == 4 * 4096 * 3072 and s * 8 == 4096 * 3072 // 2 and w == 4096 * 32 * 2
+    ws = B.asp_workspace_bytes(256, 1024, 32)
+    assert ws >= 256 * 512 + 256 * 64 + 256 * 32 * 4
+
+
+@pytest.mark.parametrize("K", [0, 100, 64, -128])
+def test_bad_k_rejected_everywhere(K):
+    for call in (lambda: B.asp_packed_sizes(16, K, 0),
+                 lambda: B.asp_workspace_bytes(4, K, 0),
+                 lambda: B.asp_act_prep(None, 0, 4, K, 0, None, None, None, None, None),
+                 lambda: B.asp_gemm_lowrank(None, None, None, 4, 16, K, 0, None, None, None,
+                                            None, None, 0)):
+        with pytest.raises(B.ASPError) as ei:
+            call()
+        assert ei.value.status == 2 and "K=" in str(ei.value)
+
+
+def test_bad_rank_and_dtype():
+    with pytest.raises(B.ASPError) as ei:
+        B.asp_packed_sizes(16, 128, 65)
+    assert ei.value.status == 2
+    with pytest.raises(B.ASPError) as ei:
+        B.asp_act_prep(None, 7, 4, 128, 0, None, None, None, None, None)
+    assert ei.value.status == 1
+
+
+# Fake device addresses: validation rejects the call before anything touches them.
+FAKE = 0x7F0000000000
+MIS = FAKE + 8
+
+
+def _act_prep(**over):
+    a = dict(x=FAKE, x_dtype=1, M=4, K=128, r=16, s=FAKE, v=FAKE, x_codes=FAKE, x_scales=FAKE,
+             u=FAKE, prequant=None)
+    a.update(over)
+    st = B.lib().asp_act_prep(a["x"], a["x_dtype"], a["M"], a["K"], a["r"], a["s"], a["v"],
+                              a["x_codes"], a["x_scales"], a["u"], a["prequant"], None)
+    return st, B.asp_last_error()
+
+
+def test_act_prep_pointer_validation():
+    assert _act_prep(x=None)[0] == 1
+    assert _act_prep(v=None)[0] == 1           # r > 0 needs V
+    assert _act_prep(u=None)[0] == 1           # r > 0 needs u
+    assert _act_prep(x=MIS)[0] == 3
+    assert _act_prep(prequant=MIS)[0] == 3
+    st, msg = _act_prep(s=None)
+    assert st == 1 and "s is NULL" in msg
+    assert _act_prep(M=0, x=None)[0] == 0     # empty batch: nothing to do, nothing checked
+    assert _act_prep(r=32, K=1 << 14)[0] == 4  # deflation above the per-row LDS budget
+
+
+def test_forward_workspace_and_alignment_checks():
+    lib = B.lib()
+    need = B.asp_workspace_bytes(8, 256, 32)
+
+    def fwd(ws, nbytes, y=FAKE, wv=FAKE):
+        return lib.asp_forward(FAKE, 1, 8, 64, 256, 32, FAKE, FAKE, FAKE, FAKE, wv, None, y, 0,
+                               ws, nbytes, None)
+
+    assert fwd(FAKE, need - 1) == 5
+    assert fwd(FAKE + 16, need) == 3   # workspace must be 256-byte aligned
+    assert fwd(None, need) == 1
+    assert fwd(FAKE, need, y=None) == 1
+    assert fwd(FAKE, need, wv=None) == 1
+    assert "wv" in B.asp_last_error()
+
+
+def test_host_quantizer_validation():
+    a = np.zeros((2, 24), np.float32)
+    with pytest.raises(B.ASPError):
+        B.asp_quantize_nvfp4_host(a, 2, 24, np.zeros(24, np.uint8), np.zeros(3, np.uint8))
+
+
+def test_pack_rejects_nonpositive_smoothing():
+    n, k = 16, 128
+    w = np.ones((n, k), np.float32)
+    s = np.ones(k, np.float32)
+    s[5] = 0.0
+    out = [np.empty((n, k // 2), np.uint8), np.empty((n, k // 16), np.uint8)]
+    with pytest.raises(B.ASPError) as ei:
+        B.asp_pack_weight(n, k, 0, w, s, None, out[0], out[1], None)
+    assert ei.value.status == 1 and "s[5]" in str(ei.value)
+
+
+def test_error_text_is_thread_local_and_cleared():
+    with pytest.raises(B.ASPError):
+        B.asp_packed_sizes(16, 100, 0)
+    assert B.asp_last_error() != ""
+    B.asp_packed_sizes(16, 128, 0)
+    assert B.asp_last_error() == ""

@@ -1,0 +1,257 @@
+"""GPU path vs the oracle, element by element, through the C ABI.
+
+Gates (derived in the design notes):
+* quantiser (standalone kernel and inside the fused prep): codes and scales
+  bit-exact against the oracle quantiser on the same float32 input;
+* dequantiser: exact;
+* GEMM on the oracle's own codes: relative Frobenius error <= 1e-5 (fp32
+  output; only accumulation order differs);
+* whole layer: relative Frobenius error on y <= 2e-3 for fp32 and bf16
+  output, and <= 1e-4 for fp32 output (accumulation order plus rare
+  one-step code flips from float32-vs-float64 pre-quantisation arithmetic).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import asp as OA
+from oracle import formats as OF
+from wam_asp_w4a4_amd import binding as B
+from wam_asp_w4a4_amd import synth
+from wam_asp_w4a4_amd.layer import PackedLayer
+
+from test_host_packer import e4m3_tie_blocks, element_tie_blocks
+from test_oracle_formats import _load_golden
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def x_device(lay):
+    if lay.x_dtype == "bf16":
+        return dev(synth.bf16_bits(lay.x), torch.bfloat16)
+    return dev(lay.x)
+
+
+def rel_fro(a, b):
+    return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+# ------------------------------------------------------------------ quantiser
+
+
+def gpu_quantize(a):
+    a = np.ascontiguousarray(a, np.float32)
+    rows, cols = a.shape
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=DEV)
+    B.asp_quantize_nvfp4(dev(a), rows, cols, codes, scales)
+    return host(codes), host(scales)
+
+
+def test_quantize_golden_blocks():
+    for name, block, scale, packed in _load_golden():
+        c, s = gpu_quantize(block[None, :])
+        assert int(s[0, 0]) == scale, name
+        assert bytes(c[0].tolist()) == packed, name
+
+
+@pytest.mark.parametrize("maker", [e4m3_tie_blocks, element_tie_blocks])
+def test_quantize_tie_points(maker):
+    a = maker()
+    c, s = gpu_quantize(a)
+    oc, os_ = OF.quantize_nvfp4(a)
+    assert np.array_equal(s, os_)
+    assert np.array_equal(c, oc)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (257, 512), (1000, 2064)])
+def test_quantize_random_ragged(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    a = rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-12, 8, (rows, 1)))
+    a[::3, ::7] = 0.0
+    a[1::5, 3::11] = -0.0
+    a = a.astype(np.float32)
+    c, s = gpu_quantize(a)
+    oc, os_ = OF.quantize_nvfp4(a)
+    assert np.array_equal(s, os_) and np.array_equal(c, oc)
+
+
+def test_dequantize_exact():
+    rng = np.random.default_rng(1)
+    rows, cols = 300, 256
+    codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8)
+    out = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    B.asp_dequantize_nvfp4(dev(codes), dev(scales), rows, cols, out)
+    want = OF.dequantize_nvfp4(codes, scales)
+    assert np.array_equal(host(out).astype(np.float64), want)
+
+
+# ------------------------------------------------------------ activation prep
+
+
+def gpu_act_prep(lay):
+    M, K, r = lay.M, lay.K, lay.r
+    xc = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((M, K // 16), dtype=torch.uint8, device=DEV)
+    u = torch.empty((M, max(r, 1)), dtype=torch.float32, device=DEV) if r else None
+    pre = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    B.asp_act_prep(x_device(lay), B.DTYPES[lay.x_dtype], M, K, r, dev(lay.s),
+                   dev(lay.v) if r else None, xc, xs, u, pre)
+    return host(xc), host(xs), (host(u) if r else None), host(pre)
+
+
+def prep_cases():
+    c0 = synth.workload(0)[0]
+    c1 = synth.workload(1)[0]
+    c2 = synth.workload(2)[1]  # ffn.2: K = 4096, post-GELU input
+    r0 = synth.make_layer("r0", 77, 384, 64, 0, seed=3, dtype="bf16")
+    r16 = synth.make_layer("r16", 5, 256, 32, 16, seed=4, dtype="f32")
+    r64 = synth.make_layer("r64", 33, 1024, 32, 64, seed=6, dtype="bf16")
+    return [c0, c1, c2, r0, r16, r64]
+
+
+@pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
+def test_act_prep_against_oracle(lay):
+    xc, xs, u, pre = gpu_act_prep(lay)
+    # 1. quantiser bit-exact on the kernel's own float32 pre-quantisation values
+    oc, os_ = OF.quantize_nvfp4(pre)
+    assert np.array_equal(xs, os_)
+    assert np.array_equal(xc, oc)
+    # 2. the pre-quantisation values and u against the float64 oracle
+    act = OA.activation_side(lay.x, lay.s, lay.v)
+    xt_scale = np.abs(act["x_tilde"]).max()
+    assert np.abs(pre - act["x_deflated"]).max() <= 2e-6 * xt_scale
+    if lay.r:
+        assert np.abs(u - act["u"]).max() <= 2e-6 * np.abs(act["u"]).max() + 1e-6 * xt_scale
+    # 3. end-to-end code agreement (reported convention: fraction of codes off)
+    mism = OF.unpack_codes(xc) != OF.unpack_codes(act["x_codes"])
+    assert mism.mean() <= 1e-3, mism.mean()
+    assert np.mean(xs != act["x_scales"]) <= 1e-3
+
+
+# ----------------------------------------------------------------------- GEMM
+
+
+def gemm_on_oracle_codes(lay, y_dtype):
+    pk = OA.pack_weight(lay.w, lay.s, lay.v)
+    act = OA.activation_side(lay.x, lay.s, lay.v)
+    M, N, K, r = lay.M, lay.N, lay.K, lay.r
+    u32 = act["u"].astype(np.float32)
+    y = torch.empty((M, N), dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16,
+                    device=DEV)
+    wv = synth.bf16_bits(pk["wv"].astype(np.float32)) if r else None
+    B.asp_gemm_lowrank(dev(act["x_codes"]), dev(act["x_scales"]), dev(u32) if r else None,
+                       M, N, K, r, dev(pk["w_codes"]), dev(pk["w_scales"]),
+                       dev(wv, torch.int16) if r else None, dev(lay.b), y, B.DTYPES[y_dtype])
+    want = OA.output_from_codes(act["x_codes"], act["x_scales"], u32.astype(np.float64),
+                                pk["w_codes"], pk["w_scales"], pk["wv"], lay.b)
+    got = host(y.float())
+    return got, want
+
+
+def gemm_cases():
+    return [synth.workload(0)[0], synth.workload(1)[0],
+            synth.make_layer("ragged", 200, 384, 200, 33, seed=8, dtype="f32"),
+            synth.make_layer("tiny", 1, 128, 16, 0, seed=9, dtype="f32")]
+
+
+@pytest.mark.parametrize("lay", gemm_cases(), ids=lambda l: f"{l.name}-M{l.M}-N{l.N}-K{l.K}-r{l.r}")
+def test_gemm_on_oracle_codes(lay):
+    got, want = gemm_on_oracle_codes(lay, "f32")
+    assert rel_fro(got, want) <= 1e-5
+    got16, _ = gemm_on_oracle_codes(lay, "bf16")
+    # the bf16 output is the RNE cast of an fp32 result: within one bf16 step of it
+    assert np.all(np.abs(got16 - got) <= np.abs(got) * 2.0 ** -8 + 1e-30)
+    assert rel_fro(got16, want) <= 2e-3
+
+
+# -------------------------------------------------------------- whole layer
+
+
+def forward_gpu(lay, y_dtype="f32", rows=None):
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
+    x = x_device(lay)
+    if rows is not None:
+        x = x[rows].contiguous()
+    y = p.forward(x, y_dtype)
+    return host(y.float()), p
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_forward_workloads(cfg):
+    for lay in synth.workload(cfg):
+        want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
+        got, _ = forward_gpu(lay, "f32")
+        e32 = rel_fro(got, want)
+        got16, _ = forward_gpu(lay, "bf16")
+        e16 = rel_fro(got16, want)
+        print(f"workload {cfg} {lay.name}: rel err fp32 {e32:.3e} bf16 {e16:.3e}")
+        assert e32 <= 1e-4
+        assert e16 <= 2e-3
+
+
+def test_forward_sampled_rows_of_mot_layers():
+    # one attention and one FFN layer of each expert, oracle on sampled rows
+    # (rows are independent, so a row subset of y is the oracle of that subset)
+    idx = [0, 8, 9, 300 + 150, 300 + 158, 300 + 159]
+    rng = np.random.default_rng(0)
+    for lay in synth.mot_layer_set(only=set(idx)):
+        rows = np.sort(rng.choice(lay.M, size=min(48, lay.M), replace=False))
+        p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
+        got = host(p.forward(x_device(lay), "f32"))[rows]
+        want = OA.forward(lay.x[rows], lay.w, lay.b, lay.s, lay.v)
+        assert rel_fro(got, want) <= 1e-4, lay.name
+
+
+@pytest.mark.parametrize("M,N,K,r", [(1, 16, 128, 0), (37, 48, 256, 1), (200, 200, 384, 16),
+                                     (129, 130, 128, 33), (64, 64, 512, 64), (300, 16, 1280, 32)])
+def test_ragged_shapes(M, N, K, r):
+    lay = synth.make_layer("edge", M, K, N, r, seed=M + N + K + r, dtype="bf16")
+    want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
+    got, _ = forward_gpu(lay, "f32")
+    assert rel_fro(got, want) <= 1e-4
+
+
+def test_empty_batch_is_a_noop():
+    lay = synth.make_layer("e", 4, 256, 32, 16, seed=1, dtype="f32")
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
+    y = torch.full((0, 32), 7.0, device=DEV)
+    x = torch.empty((0, 256), device=DEV)
+    out = p.forward(x, "f32", y=y, workspace=torch.empty(256, dtype=torch.uint8, device=DEV))
+    assert out.shape == (0, 32)
+
+
+def test_no_bias_and_determinism():
+    lay = synth.workload(1)[1]
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, None, DEV)
+    x = x_device(lay)
+    y1 = host(p.forward(x, "f32"))
+    y2 = host(p.forward(x, "f32"))
+    assert np.array_equal(y1, y2)
+    want = OA.forward(lay.x, lay.w, None, lay.s, lay.v)
+    assert rel_fro(y1, want) <= 1e-4
+
+
+def test_row_independence_bitwise():
+    lay = synth.workload(1)[0]
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
+    x = x_device(lay)
+    full = host(p.forward(x, "f32"))
+    rows = [3, 100, 255, 17, 128]
+    part = host(p.forward(x[rows].contiguous(), "f32"))
+    assert np.array_equal(full[rows], part)

@@ -1,0 +1,120 @@
+"""Host half of the library against the oracle (CPU only).
+
+* asp_quantize_nvfp4_host: bit-exact codes and scales vs the oracle quantiser
+  on the hand-derived golden blocks, on every E4M3 tie point and its float32
+  neighbours, and on random data with planted zeros and grid values.
+* asp_pack_weight: given the packer's own float32 deflated weight, codes and
+  scales are bit-exact vs the oracle quantiser; the float32 deflated weight
+  and the bf16 low-rank factor match the oracle's (float64 summation order
+  may move a value by one unit in the last place on rare elements).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import asp as OA
+from oracle import formats as OF
+from wam_asp_w4a4_amd import binding as B
+from wam_asp_w4a4_amd import synth
+from wam_asp_w4a4_amd.layer import PackedLayer
+
+from test_oracle_formats import _load_golden
+
+
+def host_quantize(a):
+    a = np.ascontiguousarray(a, np.float32)
+    rows, cols = a.shape
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    B.asp_quantize_nvfp4_host(a, rows, cols, codes, scales)
+    return codes, scales
+
+
+def test_golden_blocks():
+    for name, block, scale, packed in _load_golden():
+        c, s = host_quantize(block[None, :])
+        assert int(s[0, 0]) == scale, name
+        assert bytes(c[0].tolist()) == packed, name
+
+
+def e4m3_tie_blocks():
+    """Blocks whose amax/6 is every E4M3 midpoint, and the float32 values around it."""
+    pos = OF.E4M3_VALUES[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    rows = []
+    for m in list(mids) + [464.0, 448.0, 2.0 ** -10, 2.0 ** -9]:
+        amax = np.float32(6.0 * m)
+        for a in (amax, np.nextafter(amax, np.float32(0)), np.nextafter(amax, np.float32(np.inf))):
+            blk = np.zeros(16, np.float32)
+            blk[0] = a
+            blk[1] = -a / np.float32(3.0)
+            blk[2:] = np.linspace(-a, a, 14, dtype=np.float32) * np.float32(0.37)
+            rows.append(blk)
+    return np.stack(rows)
+
+
+def element_tie_blocks():
+    """Blocks with scale 2^e * 1.mmm and elements at every E2M1 midpoint times it."""
+    rows = []
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for sc_code in range(1, 0x7F, 3):
+        sd = OF.E4M3_VALUES[sc_code]
+        blk = np.zeros(16, np.float64)
+        blk[0] = 6.0 * sd
+        blk[1:8] = mids * sd
+        blk[8:15] = -mids * sd
+        b32 = blk.astype(np.float32)
+        if np.array_equal(b32.astype(np.float64), blk):
+            rows.append(b32)
+            rows.append(np.nextafter(b32, np.float32(np.inf)))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("maker", [e4m3_tie_blocks, element_tie_blocks])
+def test_tie_points_bit_exact(maker):
+    a = maker()
+    c, s = host_quantize(a)
+    oc, os_ = OF.quantize_nvfp4(a)
+    assert np.array_equal(s, os_)
+    assert np.array_equal(c, oc)
+
+
+def test_random_bit_exact():
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((300, 512)) * np.exp(rng.uniform(-12, 8, (300, 1)))
+    a[::3, ::7] = 0.0
+    a[1::5, 3::11] = -0.0
+    a[2::4, 5] = 6.0  # grid values
+    a = a.astype(np.float32)
+    c, s = host_quantize(a)
+    oc, os_ = OF.quantize_nvfp4(a)
+    assert np.array_equal(s, os_) and np.array_equal(c, oc)
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_packer_matches_oracle(cfg):
+    for lay in synth.workload(cfg):
+        p = PackedLayer.pack_host(lay.w, lay.s, lay.v, want_prequant=True)
+        # bit-exact quantiser on the packer's own float32 deflated weight
+        oc, os_ = OF.quantize_nvfp4(p["w_prequant"])
+        assert np.array_equal(p["w_codes"], oc) and np.array_equal(p["w_scales"], os_)
+        o = OA.pack_weight(lay.w, lay.s, lay.v)
+        pre_mis = np.mean(p["w_prequant"] != o["w_prequant"])
+        assert pre_mis <= 1e-5, pre_mis
+        ulp = np.abs(p["w_prequant"].view(np.int32).astype(np.int64)
+                     - o["w_prequant"].view(np.int32).astype(np.int64))
+        assert ulp.max() <= 1
+        code_mis = np.mean(p["w_codes"] != o["w_codes"])
+        assert code_mis <= 1e-5
+        wv = synth.bf16_bits(o["wv"].astype(np.float32))
+        assert np.mean(p["wv"] != wv) <= 1e-4
+
+
+def test_packer_rank_zero_and_threads():
+    lay = synth.make_layer("r0", 4, 256, 48, 0, seed=5, dtype="f32")
+    p1 = PackedLayer.pack_host(lay.w, lay.s, None, n_threads=1)
+    p8 = PackedLayer.pack_host(lay.w, lay.s, None, n_threads=8)
+    assert np.array_equal(p1["w_codes"], p8["w_codes"])
+    o = OA.pack_weight(lay.w, lay.s, None)
+    assert np.array_equal(p1["w_codes"], o["w_codes"])
+    assert np.array_equal(p1["w_scales"], o["w_scales"])

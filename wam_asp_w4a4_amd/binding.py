@@ -1,0 +1,165 @@
+"""ctypes binding of libasp's C entry points (argument marshalling only).
+
+Every function has the name and argument order of its C counterpart in
+``include/asp.h``.  Array arguments may be torch tensors (device or host,
+contiguous) or NumPy arrays (host); ``None`` passes NULL.  The stream argument
+defaults to torch's current stream on the tensors' device.  A non-zero status
+raises :class:`ASPError` with the library's own message.
+
+The library is loaded on first use; a missing build raises at once -- there is
+no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
+
+ASP_F32 = 0
+ASP_BF16 = 1
+DTYPES = {"f32": ASP_F32, "bf16": ASP_BF16}
+
+# name -> (restype, argtypes); mirrors include/asp.h
+_i32, _i64, _sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+_psz = ctypes.POINTER(ctypes.c_size_t)
+SIGNATURES = {
+    "asp_abi_version": (_i32, []),
+    "asp_status_string": (ctypes.c_char_p, [_i32]),
+    "asp_last_error": (ctypes.c_char_p, []),
+    "asp_packed_sizes": (_i32, [_i64, _i64, _i32, _psz, _psz, _psz]),
+    "asp_pack_weight": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32]),
+    "asp_quantize_nvfp4_host": (_i32, [_p, _i64, _i64, _p, _p]),
+    "asp_quantize_nvfp4": (_i32, [_p, _i64, _i64, _p, _p, _p]),
+    "asp_dequantize_nvfp4": (_i32, [_p, _p, _i64, _i64, _p, _p]),
+    "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "asp_gemm_lowrank": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
+    "asp_workspace_bytes": (_i32, [_i64, _i64, _i32, _psz]),
+    "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32,
+                           _p, _sz, _p]),
+}
+
+_lib = None
+
+
+class ASPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libasp (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m wam_asp_w4a4_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        if handle.asp_abi_version() != 1:
+            raise RuntimeError("libasp ABI version mismatch")
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = lib().asp_last_error().decode()
+        raise ASPError(status, msg)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("NumPy arrays must be C-contiguous")
+        return a.ctypes.data
+    if not a.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return a.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream
+    import torch
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+# ------------------------------------------------------------------- host
+
+
+def asp_abi_version() -> int:
+    return lib().asp_abi_version()
+
+
+def asp_status_string(status: int) -> str:
+    return lib().asp_status_string(status).decode()
+
+
+def asp_last_error() -> str:
+    return lib().asp_last_error().decode()
+
+
+def asp_packed_sizes(N: int, K: int, r: int):
+    c, s, w = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().asp_packed_sizes(N, K, r, ctypes.byref(c), ctypes.byref(s), ctypes.byref(w)))
+    return c.value, s.value, w.value
+
+
+def asp_workspace_bytes(M: int, K: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().asp_workspace_bytes(M, K, r, ctypes.byref(b)))
+    return b.value
+
+
+def asp_pack_weight(N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant=None, n_threads=0):
+    _check(lib().asp_pack_weight(N, K, r, _ptr(w), _ptr(s), _ptr(v), _ptr(w_codes),
+                                 _ptr(w_scales), _ptr(wv), _ptr(w_prequant), n_threads))
+
+
+def asp_quantize_nvfp4_host(inp, rows, cols, codes, scales):
+    _check(lib().asp_quantize_nvfp4_host(_ptr(inp), rows, cols, _ptr(codes), _ptr(scales)))
+
+
+# ----------------------------------------------------------------- device
+
+
+def asp_quantize_nvfp4(inp, rows, cols, codes, scales, stream=None):
+    _check(lib().asp_quantize_nvfp4(_ptr(inp), rows, cols, _ptr(codes), _ptr(scales),
+                                    _stream(stream, inp)))
+
+
+def asp_dequantize_nvfp4(codes, scales, rows, cols, out, stream=None):
+    _check(lib().asp_dequantize_nvfp4(_ptr(codes), _ptr(scales), rows, cols, _ptr(out),
+                                      _stream(stream, out)))
+
+
+def asp_act_prep(x, x_dtype, M, K, r, s, v, x_codes, x_scales, u, prequant=None, stream=None):
+    _check(lib().asp_act_prep(_ptr(x), x_dtype, M, K, r, _ptr(s), _ptr(v), _ptr(x_codes),
+                              _ptr(x_scales), _ptr(u), _ptr(prequant), _stream(stream, x)))
+
+
+def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
+                     stream=None):
+    _check(lib().asp_gemm_lowrank(_ptr(x_codes), _ptr(x_scales), _ptr(u), M, N, K, r,
+                                  _ptr(w_codes), _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y),
+                                  y_dtype, _stream(stream, y)))
+
+
+def asp_forward(x, x_dtype, M, N, K, r, s, v, w_codes, w_scales, wv, bias, y, y_dtype,
+                workspace, workspace_bytes, stream=None):
+    _check(lib().asp_forward(_ptr(x), x_dtype, M, N, K, r, _ptr(s), _ptr(v), _ptr(w_codes),
+                             _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y), y_dtype,
+                             _ptr(workspace), workspace_bytes, _stream(stream, y)))

@@ -1,0 +1,91 @@
+"""Device-resident packed layer: host packing through libasp, torch for memory.
+
+``PackedLayer.pack`` runs the library's host packer (``asp_pack_weight``) and
+uploads its outputs; ``PackedLayer.forward`` allocates y and a workspace with
+torch and calls ``asp_forward``.  All arithmetic happens inside libasp.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class PackedLayer:
+    N: int
+    K: int
+    r: int
+    w_codes: torch.Tensor    # N x K/2 uint8
+    w_scales: torch.Tensor   # N x K/16 uint8
+    wv: torch.Tensor | None  # N x r int16 (bf16 bits), None when r == 0
+    v: torch.Tensor | None   # K x r float32
+    s: torch.Tensor          # K float32
+    bias: torch.Tensor | None
+
+    @staticmethod
+    def pack_host(w: np.ndarray, s: np.ndarray, v: np.ndarray | None, n_threads: int = 0,
+                  want_prequant: bool = False) -> dict:
+        """Run the host packer; returns NumPy buffers."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        n, k = w.shape
+        r = 0 if v is None else v.shape[1]
+        v = None if v is None else np.ascontiguousarray(v, dtype=np.float32)
+        nc, ns, nw = B.asp_packed_sizes(n, k, r)
+        out = {
+            "w_codes": np.empty((n, k // 2), np.uint8),
+            "w_scales": np.empty((n, k // 16), np.uint8),
+            "wv": np.empty((n, r), np.uint16) if r else None,
+            "w_prequant": np.empty((n, k), np.float32) if want_prequant else None,
+        }
+        assert out["w_codes"].nbytes == nc and out["w_scales"].nbytes == ns
+        B.asp_pack_weight(n, k, r, w, s, v, out["w_codes"], out["w_scales"], out["wv"],
+                          out["w_prequant"], n_threads)
+        return out
+
+    @classmethod
+    def from_host(cls, packed: dict, s, v, bias, device="cuda") -> "PackedLayer":
+        n, kh = packed["w_codes"].shape
+        k = kh * 2
+        r = 0 if v is None else v.shape[1]
+
+        def up(a, dtype=None):
+            if a is None:
+                return None
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if dtype is not None:
+                t = t.view(dtype)
+            return t.to(device)
+
+        return cls(n, k, r, up(packed["w_codes"]), up(packed["w_scales"]),
+                   up(packed["wv"], torch.int16), up(v if v is None else np.asarray(v, np.float32)),
+                   up(np.asarray(s, np.float32)),
+                   up(None if bias is None else np.asarray(bias, np.float32)))
+
+    @classmethod
+    def pack(cls, w, s, v, bias, device="cuda", n_threads: int = 0) -> "PackedLayer":
+        return cls.from_host(cls.pack_host(w, s, v, n_threads), s, v, bias, device)
+
+    def workspace(self, M: int) -> torch.Tensor:
+        n = B.asp_workspace_bytes(M, self.K, self.r)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.w_codes.device)
+
+    def forward(self, x: torch.Tensor, y_dtype: str = "f32", workspace=None, y=None,
+                stream=None) -> torch.Tensor:
+        M = x.shape[0]
+        x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
+        if x.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError("x must be float32 or bfloat16")
+        if y is None:
+            y = torch.empty((M, self.N), device=x.device,
+                            dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16)
+        ws = self.workspace(M) if workspace is None else workspace
+        B.asp_forward(x, x_dtype, M, self.N, self.K, self.r, self.s, self.v, self.w_codes,
+                      self.w_scales, self.wv, self.bias, y, B.DTYPES[y_dtype], ws, ws.numel(),
+                      stream)
+        return y
