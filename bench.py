@@ -117,7 +117,8 @@ def main():
         for lay, pk, xh in host:
             tot += xh.nbytes + pk["w_codes"].nbytes + pk["w_scales"].nbytes
             tot += 0 if pk["wv"] is None else pk["wv"].nbytes
-            tot += lay.M * lay.N * yb + B.asp_workspace_bytes(lay.M, lay.K, lay.r)
+            tot += pk["prep"].nbytes
+            tot += lay.M * lay.N * yb + B.asp_workspace_bytes(lay.M, lay.N, lay.K, lay.r)
         return tot
 
     per = replica_bytes()
@@ -137,7 +138,7 @@ def main():
                 shared_x[key] = t(xh, torch.bfloat16 if lay.x_dtype == "bf16" else None)
             p = PackedLayer(lay.N, lay.K, lay.r, t(pk["w_codes"]), t(pk["w_scales"]),
                             None if pk["wv"] is None else t(pk["wv"], torch.int16),
-                            None if lay.v is None else t(lay.v), t(lay.s), t(lay.b))
+                            t(pk["prep"]), t(lay.b))
             y = torch.empty((lay.M, lay.N), dtype=torch.bfloat16, device=dev)
             ws = p.workspace(lay.M)
             rep.append((lay, p, shared_x[key], y, ws))
@@ -175,23 +176,28 @@ def main():
     # ---- per-kernel durations with events around every launch (eager, backlogged)
     nk = max(1, min(args.kernel_timing_steps, args.steps))
     big = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-    timings = {"prep": [], "gemm": []}
     evs = []
     torch.cuda.synchronize()
-    for _ in range(8 + nk // 4):  # GPU backlog so the launches below queue up
+    # GPU backlog (about 0.1 ms of matmul per launch pair queued below) so the
+    # timed launches queue up behind it and their events bracket them tightly
+    for _ in range(16 + nk * len(layers)):
         big = big @ big
         big = big / big.abs().amax().clamp_min(1.0)
     for i in range(nk):
         for lay, p, x, y, ws in replicas[i % R]:
             M, N, K, r = lay.M, lay.N, lay.K, lay.r
+            up = lambda b: (b + 255) // 256 * 256
             xc = ws[: M * K // 2]
-            off = (M * K // 2 + 255) // 256 * 256
+            off = up(M * K // 2)
             xs = ws[off: off + M * K // 16]
-            off2 = off + (M * K // 16 + 255) // 256 * 256
+            off2 = off + up(M * K // 16)
             u = ws[off2: off2 + 4 * M * r].view(torch.float32) if r else None
+            off3 = off2 + up(4 * M * r)
+            scratch = ws[off3:]
             ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             ea.record(stream)
-            B.asp_act_prep(x, B.DTYPES[lay.x_dtype], M, K, r, p.s, p.v, xc, xs, u, None)
+            B.asp_act_prep(x, B.DTYPES[lay.x_dtype], M, K, r, p.prep, xc, xs, u, None, scratch,
+                           scratch.numel())
             eb.record(stream)
             B.asp_gemm_lowrank(xc, xs, u, M, N, K, r, p.w_codes, p.w_scales, p.wv, p.bias, y,
                                B.DTYPES[y_dtype])

@@ -123,6 +123,25 @@ int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
 int32_t asp_quantize_nvfp4_host(const float* in, int64_t rows, int64_t cols,
                                 uint8_t* codes, uint8_t* scales);
 
+/* Bytes of a layer's prep constants for K channels and rank r. */
+int32_t asp_prep_pack_bytes(int64_t K, int32_t r, size_t* bytes);
+
+/*
+ * Per-layer constants of the activation prep (CPU, once per layer), from the
+ * smoothing vector and the basis that define the layer's transforms (model
+ * card, "What ASP is, and what the deflated form means": x_tilde = (x/s) H,
+ * u = x_tilde V).  The buffer holds, in float64-derived form:
+ *   1 / (s sqrt(128)) per channel (float32);
+ *   V'' = diag(1/s) H V, so that u = x V'' (bf16 high and low parts);
+ *   V itself, for the deflation (bf16 high and low parts).
+ * Its layout is private to the library; upload it unchanged.
+ *   s          host, K float32, all > 0
+ *   v          host, K x r float32 (NULL iff r == 0)
+ *   prep_pack  host out, asp_prep_pack_bytes(K, r) bytes
+ */
+int32_t asp_pack_prep(int64_t K, int32_t r, const float* s, const float* v,
+                      uint8_t* prep_pack);
+
 /* ---------------------------------------------------------------- device */
 
 /*
@@ -140,22 +159,27 @@ int32_t asp_dequantize_nvfp4(const uint8_t* codes, const uint8_t* scales,
                              int64_t rows, int64_t cols, float* out,
                              void* stream);
 
+/* Workspace bytes asp_act_prep needs (partial sums of u; 0 when r == 0). */
+int32_t asp_act_prep_workspace_bytes(int64_t M, int64_t K, int32_t r,
+                                     size_t* bytes);
+
 /*
  * Fused activation prep (every call): smooth-divide x/s, block Hadamard,
  * u = x_tilde V, deflation x_tilde - u V^T, NVFP4 quantise and pack
  * (model card, "What ASP is, and what the deflated form means").
- *   x         device, M x K, element type x_dtype (ASP_F32 or ASP_BF16)
- *   s         device, K float32
- *   v         device, K x r float32 (NULL iff r == 0)
- *   x_codes   device out, M x K/2;  x_scales device out, M x K/16
- *   u         device out, M x r float32 (NULL allowed iff r == 0)
- *   prequant  device out, M x K float32 deflated activation before
- *             quantisation, or NULL (a check hook; costs bandwidth)
+ *   x          device, M x K, element type x_dtype (ASP_F32 or ASP_BF16)
+ *   prep_pack  device, the layer's asp_pack_prep output
+ *   x_codes    device out, M x K/2;  x_scales device out, M x K/16
+ *   u          device out, M x r float32 (NULL allowed iff r == 0)
+ *   prequant   device out, M x K float32 deflated activation before
+ *              quantisation, or NULL (a check hook; costs bandwidth)
+ *   workspace  device scratch of asp_act_prep_workspace_bytes bytes (NULL
+ *              allowed when that is 0); contents undefined afterwards
  */
 int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K,
-                     int32_t r, const float* s, const float* v,
-                     uint8_t* x_codes, uint8_t* x_scales, float* u,
-                     float* prequant, void* stream);
+                     int32_t r, const uint8_t* prep_pack, uint8_t* x_codes,
+                     uint8_t* x_scales, float* u, float* prequant,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * 4-bit GEMM with fused low-rank and bias epilogue:
@@ -179,17 +203,19 @@ int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales,
                          const float* bias, void* y, int32_t y_dtype,
                          void* stream);
 
-/* Workspace bytes asp_forward needs for M rows (activation codes, scales, u). */
-int32_t asp_workspace_bytes(int64_t M, int64_t K, int32_t r, size_t* bytes);
+/* Workspace bytes asp_forward needs (activation codes, scales, u, prep scratch). */
+int32_t asp_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
+                            size_t* bytes);
 
 /*
  * The whole layer on the GPU: asp_act_prep then asp_gemm_lowrank, enqueued
  * on `stream`, with the activation codes, scales and u in the caller's
  * workspace (device, at least asp_workspace_bytes bytes, 256-byte aligned).
- * Weight-side arguments are asp_pack_weight's outputs uploaded to the device.
+ * prep_pack, w_codes, w_scales and wv are the layer's asp_pack_prep and
+ * asp_pack_weight outputs uploaded to the device.
  */
 int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N,
-                    int64_t K, int32_t r, const float* s, const float* v,
+                    int64_t K, int32_t r, const uint8_t* prep_pack,
                     const uint8_t* w_codes, const uint8_t* w_scales,
                     const uint16_t* wv, const float* bias, void* y,
                     int32_t y_dtype, void* workspace, size_t workspace_bytes,

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == 1
+    assert B.asp_abi_version() == 2
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
@@ -47,14 +47,15 @@ def test_version_and_status_strings():
 def test_sizes_are_four_and_a_half_bits_per_weight():
     c, s, w = B.asp_packed_sizes(4096, 3072, 32)
     assert c * 8 == 4 * 4096 * 3072 and s * 8 == 4096 * 3072 // 2 and w == 4096 * 32 * 2
-    ws = B.asp_workspace_bytes(256, 1024, 32)
+    ws = B.asp_workspace_bytes(256, 1024, 1024, 32)
     assert ws >= 256 * 512 + 256 * 64 + 256 * 32 * 4
 
 
 @pytest.mark.parametrize("K", [0, 100, 64, -128])
 def test_bad_k_rejected_everywhere(K):
     for call in (lambda: B.asp_packed_sizes(16, K, 0),
-                 lambda: B.asp_workspace_bytes(4, K, 0),
+                 lambda: B.asp_workspace_bytes(4, 16, K, 0),
+                 lambda: B.asp_prep_pack_bytes(K, 0),
                  lambda: B.asp_act_prep(None, 0, 4, K, 0, None, None, None, None, None),
                  lambda: B.asp_gemm_lowrank(None, None, None, 4, 16, K, 0, None, None, None,
                                             None, None, 0)):
@@ -70,6 +71,9 @@ def test_bad_rank_and_dtype():
     with pytest.raises(B.ASPError) as ei:
         B.asp_act_prep(None, 7, 4, 128, 0, None, None, None, None, None)
     assert ei.value.status == 1
+    with pytest.raises(B.ASPError) as ei:
+        B.asp_pack_prep(128, 4, np.ones(128, np.float32), None, np.zeros(16, np.uint8))
+    assert ei.value.status == 1
 
 
 # Fake device addresses: validation rejects the call before anything touches them.
@@ -78,32 +82,36 @@ MIS = FAKE + 8
 
 
 def _act_prep(**over):
-    a = dict(x=FAKE, x_dtype=1, M=4, K=128, r=16, s=FAKE, v=FAKE, x_codes=FAKE, x_scales=FAKE,
-             u=FAKE, prequant=None)
+    a = dict(x=FAKE, x_dtype=1, M=4, K=128, r=16, pack=FAKE, x_codes=FAKE, x_scales=FAKE,
+             u=FAKE, prequant=None, ws=FAKE, ws_bytes=1 << 20)
     a.update(over)
-    st = B.lib().asp_act_prep(a["x"], a["x_dtype"], a["M"], a["K"], a["r"], a["s"], a["v"],
-                              a["x_codes"], a["x_scales"], a["u"], a["prequant"], None)
+    st = B.lib().asp_act_prep(a["x"], a["x_dtype"], a["M"], a["K"], a["r"], a["pack"],
+                              a["x_codes"], a["x_scales"], a["u"], a["prequant"], a["ws"],
+                              a["ws_bytes"], None)
     return st, B.asp_last_error()
 
 
 def test_act_prep_pointer_validation():
     assert _act_prep(x=None)[0] == 1
-    assert _act_prep(v=None)[0] == 1           # r > 0 needs V
+    assert _act_prep(pack=None)[0] == 1
     assert _act_prep(u=None)[0] == 1           # r > 0 needs u
     assert _act_prep(x=MIS)[0] == 3
     assert _act_prep(prequant=MIS)[0] == 3
-    st, msg = _act_prep(s=None)
-    assert st == 1 and "s is NULL" in msg
+    st, msg = _act_prep(x_codes=None)
+    assert st == 1 and "x_codes is NULL" in msg
     assert _act_prep(M=0, x=None)[0] == 0     # empty batch: nothing to do, nothing checked
-    assert _act_prep(r=32, K=1 << 14)[0] == 4  # deflation above the per-row LDS budget
+    assert _act_prep(ws=None)[0] == 1          # r > 0 needs scratch for the u partial sums
+    need = B.asp_act_prep_workspace_bytes(4, 128, 16)
+    assert need > 0 and B.asp_act_prep_workspace_bytes(4, 128, 0) == 0
+    assert _act_prep(ws_bytes=need - 1)[0] == 5
 
 
 def test_forward_workspace_and_alignment_checks():
     lib = B.lib()
-    need = B.asp_workspace_bytes(8, 256, 32)
+    need = B.asp_workspace_bytes(8, 64, 256, 32)
 
     def fwd(ws, nbytes, y=FAKE, wv=FAKE):
-        return lib.asp_forward(FAKE, 1, 8, 64, 256, 32, FAKE, FAKE, FAKE, FAKE, wv, None, y, 0,
+        return lib.asp_forward(FAKE, 1, 8, 64, 256, 32, FAKE, FAKE, FAKE, wv, None, y, 0,
                                ws, nbytes, None)
 
     assert fwd(FAKE, need - 1) == 5

@@ -118,3 +118,46 @@ def test_packer_rank_zero_and_threads():
     o = OA.pack_weight(lay.w, lay.s, None)
     assert np.array_equal(p1["w_codes"], o["w_codes"])
     assert np.array_equal(p1["w_scales"], o["w_scales"])
+
+
+def _bf16_pair_value(hi, lo):
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return f(hi) + f(lo)
+
+
+@pytest.mark.parametrize("K,r", [(512, 32), (384, 17), (256, 0), (1024, 64)])
+def test_prep_pack_constants(K, r):
+    """The prep constants reproduce 1/(s sqrt 128), diag(1/s) H V and V to ~2^-16."""
+    from oracle import hadamard as OH
+    lay = synth.make_layer("p", 4, K, 16, r, seed=K + r, dtype="f32")
+    pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
+    B.asp_pack_prep(K, r, lay.s, lay.v, pack)
+    up = lambda b: (b + 255) // 256 * 256
+    rp16, rp32 = (r + 15) // 16 * 16, (r + 31) // 32 * 32
+    off_vth = up(4 * K)
+    off_vtl = off_vth + up(2 * rp32 * K)
+    off_vh = off_vtl + up(2 * rp32 * K)
+    off_vl = off_vh + up(2 * K * rp16)
+    assert pack.nbytes == off_vl + up(2 * K * rp16)
+    cvec = pack[:4 * K].view(np.float32)
+    want_c = (1.0 / (lay.s.astype(np.float64) * np.sqrt(128.0))).astype(np.float32)
+    assert np.array_equal(cvec, want_c)
+    if r == 0:
+        return
+    vth = pack[off_vth:off_vth + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
+    vtl = pack[off_vtl:off_vtl + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
+    vh = pack[off_vh:off_vh + 2 * K * rp16].view(np.uint16).reshape(K, rp16)
+    vl = pack[off_vl:off_vl + 2 * K * rp16].view(np.uint16).reshape(K, rp16)
+    v64 = lay.v.astype(np.float64)
+    vpp = OH.block_rotate(v64.T).T / lay.s.astype(np.float64)[:, None]   # diag(1/s) H V
+    got = _bf16_pair_value(vth[:r], vtl[:r]).T
+    assert np.abs(got - vpp).max() <= 2.0 ** -15 * np.abs(vpp).max()
+    assert np.all(vth[r:] == 0) and np.all(vtl[r:] == 0)
+    gotv = _bf16_pair_value(vh[:, :r], vl[:, :r])
+    assert np.abs(gotv - v64).max() <= 2.0 ** -15 * np.abs(v64).max()
+    assert np.all(vh[:, r:] == 0)
+    # u from the constants equals the oracle's x_tilde V
+    x = lay.x.astype(np.float64)
+    from oracle import asp as OAsp
+    act = OAsp.activation_side(lay.x, lay.s, lay.v)
+    assert np.abs(x @ got - act["u"]).max() <= 1e-4 * np.abs(act["u"]).max()

@@ -33,12 +33,15 @@ SIGNATURES = {
     "asp_packed_sizes": (_i32, [_i64, _i64, _i32, _psz, _psz, _psz]),
     "asp_pack_weight": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32]),
     "asp_quantize_nvfp4_host": (_i32, [_p, _i64, _i64, _p, _p]),
+    "asp_prep_pack_bytes": (_i32, [_i64, _i32, _psz]),
+    "asp_pack_prep": (_i32, [_i64, _i32, _p, _p, _p]),
     "asp_quantize_nvfp4": (_i32, [_p, _i64, _i64, _p, _p, _p]),
     "asp_dequantize_nvfp4": (_i32, [_p, _p, _i64, _i64, _p, _p]),
-    "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "asp_act_prep_workspace_bytes": (_i32, [_i64, _i64, _i32, _psz]),
+    "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "asp_gemm_lowrank": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
-    "asp_workspace_bytes": (_i32, [_i64, _i64, _i32, _psz]),
-    "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32,
+    "asp_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
+    "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32,
                            _p, _sz, _p]),
 }
 
@@ -63,7 +66,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
-        if handle.asp_abi_version() != 1:
+        if handle.asp_abi_version() != 2:
             raise RuntimeError("libasp ABI version mismatch")
         _lib = handle
     return _lib
@@ -118,10 +121,26 @@ def asp_packed_sizes(N: int, K: int, r: int):
     return c.value, s.value, w.value
 
 
-def asp_workspace_bytes(M: int, K: int, r: int) -> int:
+def asp_workspace_bytes(M: int, N: int, K: int, r: int) -> int:
     b = ctypes.c_size_t()
-    _check(lib().asp_workspace_bytes(M, K, r, ctypes.byref(b)))
+    _check(lib().asp_workspace_bytes(M, N, K, r, ctypes.byref(b)))
     return b.value
+
+
+def asp_act_prep_workspace_bytes(M: int, K: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().asp_act_prep_workspace_bytes(M, K, r, ctypes.byref(b)))
+    return b.value
+
+
+def asp_prep_pack_bytes(K: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().asp_prep_pack_bytes(K, r, ctypes.byref(b)))
+    return b.value
+
+
+def asp_pack_prep(K, r, s, v, prep_pack):
+    _check(lib().asp_pack_prep(K, r, _ptr(s), _ptr(v), _ptr(prep_pack)))
 
 
 def asp_pack_weight(N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant=None, n_threads=0):
@@ -146,9 +165,11 @@ def asp_dequantize_nvfp4(codes, scales, rows, cols, out, stream=None):
                                       _stream(stream, out)))
 
 
-def asp_act_prep(x, x_dtype, M, K, r, s, v, x_codes, x_scales, u, prequant=None, stream=None):
-    _check(lib().asp_act_prep(_ptr(x), x_dtype, M, K, r, _ptr(s), _ptr(v), _ptr(x_codes),
-                              _ptr(x_scales), _ptr(u), _ptr(prequant), _stream(stream, x)))
+def asp_act_prep(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant=None,
+                 workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().asp_act_prep(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(x_codes),
+                              _ptr(x_scales), _ptr(u), _ptr(prequant), _ptr(workspace),
+                              workspace_bytes, _stream(stream, x)))
 
 
 def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
@@ -158,8 +179,8 @@ def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bi
                                   y_dtype, _stream(stream, y)))
 
 
-def asp_forward(x, x_dtype, M, N, K, r, s, v, w_codes, w_scales, wv, bias, y, y_dtype,
+def asp_forward(x, x_dtype, M, N, K, r, prep_pack, w_codes, w_scales, wv, bias, y, y_dtype,
                 workspace, workspace_bytes, stream=None):
-    _check(lib().asp_forward(_ptr(x), x_dtype, M, N, K, r, _ptr(s), _ptr(v), _ptr(w_codes),
+    _check(lib().asp_forward(_ptr(x), x_dtype, M, N, K, r, _ptr(prep_pack), _ptr(w_codes),
                              _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y), y_dtype,
                              _ptr(workspace), workspace_bytes, _stream(stream, y)))

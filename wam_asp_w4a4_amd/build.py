@@ -46,12 +46,18 @@ def build(verbose: bool = False) -> str:
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     with tempfile.TemporaryDirectory(prefix="asp_build_") as tmp:
-        jobs = [
-            [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "asp_kernels.hip"),
-             "-o", os.path.join(tmp, "asp_kernels.o")],
-            ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "asp_host.cpp"),
-             "-o", os.path.join(tmp, "asp_host.o")],
-        ]
+        objs = []
+        jobs = []
+        for name in sorted(os.listdir(CSRC)):
+            src = os.path.join(CSRC, name)
+            obj = os.path.join(tmp, name + ".o")
+            if name.endswith(".hip"):
+                jobs.append([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
+            elif name.endswith(".cpp"):
+                jobs.append(["g++", *HOST_FLAGS, "-c", src, "-o", obj])
+            else:
+                continue
+            objs.append(obj)
         with ThreadPoolExecutor(len(jobs)) as ex:
             outs = list(ex.map(_run, jobs))
         if verbose:
@@ -59,8 +65,7 @@ def build(verbose: bool = False) -> str:
                 if o.strip():
                     print(o, file=sys.stderr)
         tmp_lib = os.path.join(tmp, "libasp.so")
-        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-pthread",
-              os.path.join(tmp, "asp_kernels.o"), os.path.join(tmp, "asp_host.o"),
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-pthread", *objs,
               "-o", tmp_lib])
         shutil.move(tmp_lib, LIB + ".new")
         os.replace(LIB + ".new", LIB)

@@ -1,0 +1,376 @@
+// 4-bit GEMM with fused low-rank + bias epilogue on gfx950 (CDNA4):
+//
+//   y = DQ(x_codes, x_scales) DQ(w_codes, w_scales)^T + bf16(u) wv^T + bias
+//
+// the NVFP4GEMM term and the bf16 low-rank branch of the deflated contract
+// (model card "FastWAM UR3 3-task -- 4-bit quantisations", section "What ASP
+// is, and what the deflated form means"; the branch "stays in bf16 by
+// design").
+//
+// gfx950's block-scaled FP4 MFMA takes one power-of-two (E8M0) scale per 32
+// K-elements; NVFP4 has one E4M3 scale (4 significant bits) per 16.  Both
+// operands are therefore decoded in registers to exact fp16 (E2M1 value x
+// E4M3 scale has at most 6 significant bits and lies in [2^-10, 2688]) and
+// contracted on v_mfma_f32_32x32x16_f16: one MFMA K-step is exactly one NVFP4
+// block, and only fp32 accumulation order differs from exact arithmetic.  The
+// low-rank branch adds ceil(r/16) bf16 MFMA K-steps into the same
+// accumulators; bias and the output cast follow.
+//
+// Decoding costs two VALU instructions per 8 elements per operand fragment;
+// three waves share each SIMD so that one wave's decode overlaps another's
+// MFMAs.  Codes and scales are staged through double-buffered LDS in stages of
+// 256 K-elements (16 MFMA K-steps per workgroup barrier).  Tile rows are padded
+// so that the 32 rows a fragment reads hit distinct banks, and each lane reads
+// the one 32-bit code word it needs per K-step one step ahead of its use, so
+// the LDS latency hides behind the current K-step's decode and MFMAs.  Scale
+// bytes are converted to fp16 once, when a stage is written to LDS.
+#include "asp_device.h"
+
+namespace asp {
+namespace {
+
+constexpr int BK = 256;                 // K elements per stage (16 NVFP4 blocks / K-steps)
+constexpr int KSTEPS = BK / 16;
+constexpr int CROW = BK / 2;            // code bytes per row per stage
+constexpr int ROWB = CROW + 8;          // padded LDS code row (136 B = 34 dwords)
+constexpr int SROWB = KSTEPS * 2 + 4;   // padded LDS scale row: 16 fp16 + 4 (36 B = 9 dwords)
+
+template <int WM, int WN, int TM, int TN>
+struct Cfg {
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = WM * TM * 32;
+  static constexpr int BN = WN * TN * 32;
+  static constexpr int ROWS = BM + BN;                    // tile rows staged per stage
+  static constexpr int SEGS = CROW / 16;                  // 16-byte code loads per row
+  static constexpr int CODE_LOADS = ROWS * SEGS;
+  static constexpr int CL_PER_T = (CODE_LOADS + NT - 1) / NT;
+  static constexpr int SC_PER_T = (ROWS + NT - 1) / NT;   // one row's 16 scale bytes each
+  static constexpr int CODES = ROWS * ROWB;
+  static constexpr int STAGE = CODES + ROWS * SROWB;
+  static constexpr int LDS = 2 * STAGE;
+};
+
+// Map a linear workgroup id to a tile.  Consecutive workgroups go to
+// different XCDs (round-robin dispatch), so ids are first regrouped so that
+// each XCD's share is a contiguous run, then the run is rastered in groups of
+// GROUP_M tile rows so that neighbouring workgroups on one XCD share A rows
+// and B columns in its L2.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GROUP_M = 4;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) {
+    const int per = total >> 3;
+    bid = (bid & 7) * per + (bid >> 3);
+  }
+  const int group = bid / (GROUP_M * tiles_n);
+  const int first = group * GROUP_M;
+  const int gsize = min(GROUP_M, tiles_m - first);
+  const int in = bid - group * GROUP_M * tiles_n;
+  tm = first + in % gsize;
+  tn = in / gsize;
+}
+
+// two E4M3 scale bytes (bits 0..15 of w) as two exact fp16 values
+__device__ __forceinline__ uint32_t scale_pair_f16(uint32_t w) {
+  const float a = e4m3_decode(w & 0xFFu), b = e4m3_decode((w >> 8) & 0xFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));  // exact: no rounding
+}
+
+template <int WM, int WN, int TM, int TN>
+__global__ void __launch_bounds__(WM * WN * 64)
+    k_gemm(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+           const float* __restrict__ u, int M, int N, int K, int r,
+           const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+           const uint16_t* __restrict__ wv, const float* __restrict__ bias, void* __restrict__ y,
+           int y_bf16, int tiles_m, int tiles_n) {
+  using C = Cfg<WM, WN, TM, TN>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int half = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int64_t KB = K / 2, KS = K / 16;
+
+  // staging assignments: code load i -> tile row i / SEGS, 16-byte segment i % SEGS
+  const uint8_t* csrc[C::CL_PER_T];
+  int cdst[C::CL_PER_T];
+  bool cok[C::CL_PER_T];
+#pragma unroll
+  for (int j = 0; j < C::CL_PER_T; ++j) {
+    const int i = tid + j * C::NT;
+    cok[j] = i < C::CODE_LOADS;
+    const int ii = cok[j] ? i : 0;
+    const int row = ii / C::SEGS, seg = ii % C::SEGS;
+    cdst[j] = row * ROWB + seg * 16;
+    const int64_t g = row < C::BM ? min(m0 + row, M - 1) : min(n0 + row - C::BM, N - 1);
+    csrc[j] = (row < C::BM ? xc : wc) + g * KB + seg * 16;
+  }
+  const uint8_t* ssrc[C::SC_PER_T];
+  int sdst[C::SC_PER_T];
+  bool sok[C::SC_PER_T];
+#pragma unroll
+  for (int j = 0; j < C::SC_PER_T; ++j) {
+    const int row = tid + j * C::NT;
+    sok[j] = row < C::ROWS;
+    const int rr = sok[j] ? row : 0;
+    sdst[j] = C::CODES + rr * SROWB;
+    const int64_t g = rr < C::BM ? min(m0 + rr, M - 1) : min(n0 + rr - C::BM, N - 1);
+    ssrc[j] = (rr < C::BM ? xs : ws) + g * KS;
+  }
+
+  uint4 rc[C::CL_PER_T];
+  uint4 rs[C::SC_PER_T];
+  // A last stage over only 128 K-elements (K % 256 == 128) loads the valid
+  // half and zero-fills the rest: zero codes with zero scales add nothing.
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < C::CL_PER_T; ++j) {
+      const int seg = (cdst[j] % ROWB) / 16;
+      const bool in_k = (int64_t)kc * CROW + seg * 16 < KB;
+      rc[j] = (cok[j] && in_k) ? *reinterpret_cast<const uint4*>(csrc[j] + (int64_t)kc * CROW)
+                               : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::SC_PER_T; ++j) {
+      if (!sok[j]) continue;
+      const uint8_t* p = ssrc[j] + (int64_t)kc * KSTEPS;
+      if ((int64_t)kc * KSTEPS + KSTEPS <= KS) {
+        rs[j] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        const uint2 h = *reinterpret_cast<const uint2*>(p);
+        rs[j] = make_uint4(h.x, h.y, 0, 0);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* base = smem + buf * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < C::CL_PER_T; ++j)
+      if (cok[j]) {
+        *reinterpret_cast<uint2*>(base + cdst[j]) = make_uint2(rc[j].x, rc[j].y);
+        *reinterpret_cast<uint2*>(base + cdst[j] + 8) = make_uint2(rc[j].z, rc[j].w);
+      }
+#pragma unroll
+    for (int j = 0; j < C::SC_PER_T; ++j)
+      if (sok[j]) {
+        // 16 E4M3 scales -> 16 exact fp16, converted once per stage
+        uint32_t* d = reinterpret_cast<uint32_t*>(base + sdst[j]);
+        const uint32_t q[4] = {rs[j].x, rs[j].y, rs[j].z, rs[j].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          d[2 * p] = scale_pair_f16(q[p]);
+          d[2 * p + 1] = scale_pair_f16(q[p] >> 16);
+        }
+      }
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // per-lane LDS offsets of this wave's fragment rows (code word of K-step ks
+  // at + 4 * (2 ks + half); fp16 scale of K-steps 2p, 2p+1 at + 4 p)
+  int aoff[TM], boff[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) aoff[i] = ((wm * TM + i) * 32 + l32);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) boff[j] = (C::BM + (wn * TN + j) * 32 + l32);
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const uint8_t* base = smem + (kc & 1) * C::STAGE;
+    uint32_t aw[TM], bw[TN], asw[TM], bsw[TN];
+    auto read_words = [&](int ks, uint32_t (&a)[TM], uint32_t (&b)[TN]) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const uint32_t*>(base + aoff[i] * ROWB + 4 * (2 * ks + half));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const uint32_t*>(base + boff[j] * ROWB + 4 * (2 * ks + half));
+    };
+    auto read_scales = [&](int p) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        asw[i] = *reinterpret_cast<const uint32_t*>(base + C::CODES + aoff[i] * SROWB + 4 * p);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bsw[j] = *reinterpret_cast<const uint32_t*>(base + C::CODES + boff[j] * SROWB + 4 * p);
+    };
+    read_words(0, aw, bw);
+    read_scales(0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint32_t an[TM], bn[TN];
+      if (ks + 1 < KSTEPS) read_words(ks + 1, an, bn);  // one K-step ahead
+      half8_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const half2_t s2 = __builtin_bit_cast(half2_t, asw[i]);
+        af[i] = decode8(aw[i], (ks & 1) ? s2[1] : s2[0]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const half2_t s2 = __builtin_bit_cast(half2_t, bsw[j]);
+        bf[j] = decode8(bw[j], (ks & 1) ? s2[1] : s2[0]);
+      }
+      if ((ks & 1) && ks + 1 < KSTEPS) read_scales((ks + 1) >> 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < KSTEPS) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) aw[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bw[j] = bn[j];
+      }
+    }
+    // The other buffer held stage kc-1, which every wave finished reading
+    // before the barrier that ended the previous iteration, so it can be
+    // refilled now; one barrier per stage publishes it.
+    if (kc + 1 < nk) {
+      sstore((kc + 1) & 1);
+      if (kc + 2 < nk) gload(kc + 2);
+      __syncthreads();
+    }
+  }
+
+  // low-rank branch: bf16(u) (M x r) times wv^T (r x N), K-steps of 16.  The
+  // operand rows are fetched with vector loads when r is a multiple of 8.
+  for (int c0 = 0; c0 < r; c0 += 16) {
+    bf16x8_t la[TM], lb[TN];
+    const int cb = c0 + half * 8;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = min(m0 + (wm * TM + i) * 32 + l32, M - 1);
+      float f[8];
+      if ((r & 7) == 0) {
+        const float4 p = *reinterpret_cast<const float4*>(u + m * r + cb);
+        const float4 q = *reinterpret_cast<const float4*>(u + m * r + cb + 4);
+        f[0] = p.x; f[1] = p.y; f[2] = p.z; f[3] = p.w; f[4] = q.x; f[5] = q.y; f[6] = q.z; f[7] = q.w;
+        if (cb >= r) for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = cb + e < r ? u[m * r + cb + e] : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) la[i][e] = bf16_from_bits(f32_to_bf16_rne(f[e]));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = min(n0 + (wn * TN + j) * 32 + l32, N - 1);
+      if ((r & 7) == 0) {
+        uint4 q = cb < r ? *reinterpret_cast<const uint4*>(wv + n * r + cb) : make_uint4(0, 0, 0, 0);
+        lb[j] = __builtin_bit_cast(bf16x8_t, q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lb[j][e] = bf16_from_bits(cb + e < r ? wv[n * r + cb + e] : (uint16_t)0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
+  }
+
+  // bias and store; accumulator element v of lane l is row 8*(v/4) + 4*(l/32)
+  // + v%4 and column l%32 of its 32 x 32 tile
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + (wn * TN + j) * 32 + l32;
+    const bool cok2 = col < N;
+    const float bcol = (bias && cok2) ? bias[col] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (!cok2 || row >= M) continue;
+        const float val = acc[i][j][v] + bcol;
+        if (y_bf16)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)row * N + col] = f32_to_bf16_rne(val);
+        else
+          reinterpret_cast<float*>(y)[(int64_t)row * N + col] = val;
+      }
+  }
+}
+
+template <int WM, int WN, int TM, int TN>
+int32_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const float* u, int64_t M, int64_t N,
+                    int64_t K, int32_t r, const uint8_t* wc, const uint8_t* wsc, const uint16_t* wv,
+                    const float* bias, void* y, int32_t y_dtype, hipStream_t stream) {
+  using C = Cfg<WM, WN, TM, TN>;
+  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
+  if (tiles_m * tiles_n > INT32_MAX)
+    return fail(ASP_ERR_SHAPE, "M=%lld N=%lld too large for one launch", (long long)M, (long long)N);
+  hipLaunchKernelGGL((k_gemm<WM, WN, TM, TN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(C::NT), 0,
+                     stream, xc, xs, u, (int)M, (int)N, (int)K, (int)r, wc, wsc, wv, bias, y,
+                     (int)(y_dtype == ASP_BF16), (int)tiles_m, (int)tiles_n);
+  return launch_status("gemm");
+}
+
+}  // namespace
+
+int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype) {
+  ASP_TRY(check_mk(M, K));
+  ASP_TRY(check_rank(r));
+  if (N < 1 || N > INT32_MAX) return fail(ASP_ERR_SHAPE, "N=%lld outside [1, 2^31)", (long long)N);
+  if (y_dtype != ASP_F32 && y_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "y_dtype=%d", y_dtype);
+  return ASP_OK;
+}
+
+int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
+                  int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
+                  const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
+                  int32_t y_dtype, hipStream_t stream) {
+  ASP_TRY(gemm_check(M, N, K, r, y_dtype));
+  if (M == 0) return ASP_OK;
+  ASP_TRY(check_ptr(x_codes, "x_codes", true));
+  ASP_TRY(check_ptr(x_scales, "x_scales", true));
+  ASP_TRY(check_ptr(u, "u", r > 0));
+  ASP_TRY(check_ptr(w_codes, "w_codes", true));
+  ASP_TRY(check_ptr(w_scales, "w_scales", true));
+  ASP_TRY(check_ptr(wv, "wv", r > 0));
+  ASP_TRY(check_ptr(bias, "bias", false));
+  ASP_TRY(check_ptr(y, "y", true));
+  // Tile choice.  Large layers use 64 x 64 per-wave tiles with 12 waves per
+  // workgroup (3 waves per SIMD hide the LDS and decode latency) on a
+  // 256 x 192 workgroup tile -- 256 tiles, one per CU, for a 4096 x 3072
+  // output.  Small layers use 64 x 64 tiles of 4 waves.
+  const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
+  if (t192 >= 128)
+    return launch_gemm<4, 3, 2, 2>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
+                                   y, y_dtype, stream);
+  return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y,
+                                 y_dtype, stream);
+}
+
+}  // namespace asp
+
+using namespace asp;
+
+extern "C" {
+
+int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales, const float* u,
+                         int64_t M, int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
+                         int32_t y_dtype, void* stream) {
+  clear_error();
+  return gemm_impl(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
+                   (hipStream_t)stream);
+}
+
+}  // extern "C"

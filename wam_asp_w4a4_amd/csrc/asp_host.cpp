@@ -133,7 +133,7 @@ using namespace asp;
 
 extern "C" {
 
-int32_t asp_abi_version(void) { return 1; }
+int32_t asp_abi_version(void) { return 2; }
 
 const char* asp_status_string(int32_t status) {
   switch (status) {
@@ -165,14 +165,50 @@ int32_t asp_packed_sizes(int64_t N, int64_t K, int32_t r, size_t* code_bytes,
   return ASP_OK;
 }
 
-int32_t asp_workspace_bytes(int64_t M, int64_t K, int32_t r, size_t* bytes) {
+int32_t asp_prep_pack_bytes(int64_t K, int32_t r, size_t* bytes) {
   clear_error();
   if (int32_t st = check_k(K)) return st;
   if (int32_t st = check_rank(r)) return st;
-  if (M < 0) return fail(ASP_ERR_SHAPE, "M=%lld must be >= 0", (long long)M);
   if (!bytes) return fail(ASP_ERR_ARG, "null output pointer");
-  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-  *bytes = up((size_t)M * K / 2) + up((size_t)M * K / 16) + up((size_t)M * r * 4);
+  *bytes = prep_pack_layout(K, r).total;
+  return ASP_OK;
+}
+
+int32_t asp_pack_prep(int64_t K, int32_t r, const float* s, const float* v, uint8_t* prep_pack) {
+  clear_error();
+  if (int32_t st = check_k(K)) return st;
+  if (int32_t st = check_rank(r)) return st;
+  if (!s || !prep_pack) return fail(ASP_ERR_ARG, "null pointer");
+  if (r > 0 && !v) return fail(ASP_ERR_ARG, "r=%d needs v", r);
+  for (int64_t k = 0; k < K; ++k)
+    if (!(s[k] > 0.0f) || !isfinite(s[k]))
+      return fail(ASP_ERR_ARG, "s[%lld]=%g must be finite and > 0", (long long)k, (double)s[k]);
+  const PrepPackLayout L = prep_pack_layout(K, r);
+  memset(prep_pack, 0, L.total);
+  float* cvec = reinterpret_cast<float*>(prep_pack + L.cvec);
+  uint16_t* vth = reinterpret_cast<uint16_t*>(prep_pack + L.vt_hi);
+  uint16_t* vtl = reinterpret_cast<uint16_t*>(prep_pack + L.vt_lo);
+  uint16_t* vh = reinterpret_cast<uint16_t*>(prep_pack + L.v_hi);
+  uint16_t* vl = reinterpret_cast<uint16_t*>(prep_pack + L.v_lo);
+  const double root = sqrt(128.0);
+  for (int64_t k = 0; k < K; ++k) cvec[k] = (float)(1.0 / ((double)s[k] * root));
+  auto bf16_value = [](uint16_t b) { return (double)bits_f32((uint32_t)b << 16); };
+  std::vector<double> col(K);
+  for (int c = 0; c < r; ++c) {
+    // V'' = diag(1/s) H V, one column at a time
+    for (int64_t k = 0; k < K; ++k) col[k] = (double)v[k * r + c];
+    for (int64_t b = 0; b < K; b += 128) fwht128(&col[b]);
+    for (int64_t k = 0; k < K; ++k) {
+      const double vpp = col[k] / (double)s[k];
+      const uint16_t hi = bf16_from_double(vpp);
+      vth[(int64_t)c * K + k] = hi;
+      vtl[(int64_t)c * K + k] = bf16_from_double(vpp - bf16_value(hi));
+      const double vv = (double)v[k * r + c];
+      const uint16_t vhi = bf16_from_double(vv);
+      vh[k * L.rp16 + c] = vhi;
+      vl[k * L.rp16 + c] = bf16_from_double(vv - bf16_value(vhi));
+    }
+  }
   return ASP_OK;
 }
 

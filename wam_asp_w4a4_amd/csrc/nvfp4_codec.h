@@ -43,36 +43,39 @@ ASP_HD float bits_f32(uint32_t u) {
   return f;
 }
 
-// E4M3FN code (0x00..0x7E) of a non-negative finite float, RNE, saturating.
+// E4M3FN code (0x00..0x7E) of a non-negative float, RNE, saturating.  Both
+// the subnormal and the normal path are evaluated and the result selected, so
+// the function compiles to straight-line code on the GPU.
 ASP_HD uint32_t e4m3_encode(float q) {
-  if (!(q < 448.0f)) return 0x7Eu;  // saturate (also >= 448 exactly)
-  if (q < 0.015625f) {              // below 2^-6: subnormal step 2^-9
-    // q * 512 is exact (power-of-two scaling of a normal float32); rint is
-    // round-half-even.  A result of 8 is the smallest normal, code 0x08.
-    return (uint32_t)rintf(q * 512.0f);
-  }
-  uint32_t b = f32_bits(q);
-  uint32_t exp = (b >> 23) - 120u;  // E4M3 exponent field: (e - 127) + 7
-  uint32_t man = b & 0x7FFFFFu;
-  uint32_t keep = man >> 20;        // top 3 mantissa bits
-  uint32_t rest = man & 0xFFFFFu;   // 20 dropped bits
-  keep += (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
-  uint32_t code = (exp << 3) + keep;  // a carry out of keep bumps the exponent
-  return code > 0x7Eu ? 0x7Eu : code;
+  // below 2^-6 the step is 2^-9: q * 512 is exact (power-of-two scaling of a
+  // float32), rint rounds half to even, and a result of 8 is the smallest
+  // normal, code 0x08.  The clamp keeps the conversion in range for large q.
+  const uint32_t sub = (uint32_t)rintf(fminf(q, 0.015625f) * 512.0f);
+  const uint32_t b = f32_bits(q);
+  const uint32_t exp = (b >> 23) - 120u;  // E4M3 exponent field: (e - 127) + 7
+  const uint32_t man = b & 0x7FFFFFu;
+  const uint32_t keep = man >> 20;        // top 3 mantissa bits
+  const uint32_t rest = man & 0xFFFFFu;   // 20 dropped bits
+  const uint32_t up = (uint32_t)(rest > 0x80000u) | ((uint32_t)(rest == 0x80000u) & keep & 1u);
+  uint32_t nrm = (exp << 3) + keep + up;  // a carry out of keep bumps the exponent
+  nrm = nrm > 0x7Eu ? 0x7Eu : nrm;
+  const uint32_t code = q < 0.015625f ? sub : nrm;
+  return q < 448.0f ? code : 0x7Eu;       // saturate (NaN too)
 }
 
 // Value of a non-negative E4M3FN code (0x00..0x7E) as float32 (exact).
 ASP_HD float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9
-  return bits_f32(((e + 120u) << 23) | (m << 20));
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  const float nrm = bits_f32(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 // E2M1 magnitude code (0..7) of a = |v| for a block whose scale decodes to sd.
 // Each comparison decides one step of the grid 0,.5,1,1.5,2,3,4,6; at a
 // midpoint, '>' keeps the lower (even) code and '>=' takes the upper (even).
+// A zero scale (the block's maximum underflowed) gives magnitude 0.
 ASP_HD uint32_t e2m1_magnitude(float a, float sd) {
-  if (!(sd > 0.0f)) return 0u;
   uint32_t m = 0;
   m += a > 0.25f * sd;   // 0 | 1, tie -> 0
   m += a >= 0.75f * sd;  // 1 | 2, tie -> 2
@@ -81,7 +84,7 @@ ASP_HD uint32_t e2m1_magnitude(float a, float sd) {
   m += a > 2.5f * sd;    // 4 | 5, tie -> 4
   m += a >= 3.5f * sd;   // 5 | 6, tie -> 6
   m += a > 5.0f * sd;    // 6 | 7, tie -> 6
-  return m;
+  return sd > 0.0f ? m : 0u;
 }
 
 // 4-bit code of v (sign bit | magnitude) in a block with decoded scale sd.

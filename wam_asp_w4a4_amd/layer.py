@@ -23,8 +23,7 @@ class PackedLayer:
     w_codes: torch.Tensor    # N x K/2 uint8
     w_scales: torch.Tensor   # N x K/16 uint8
     wv: torch.Tensor | None  # N x r int16 (bf16 bits), None when r == 0
-    v: torch.Tensor | None   # K x r float32
-    s: torch.Tensor          # K float32
+    prep: torch.Tensor       # the layer's prep constants (asp_pack_prep), uint8
     bias: torch.Tensor | None
 
     @staticmethod
@@ -46,13 +45,15 @@ class PackedLayer:
         assert out["w_codes"].nbytes == nc and out["w_scales"].nbytes == ns
         B.asp_pack_weight(n, k, r, w, s, v, out["w_codes"], out["w_scales"], out["wv"],
                           out["w_prequant"], n_threads)
+        out["prep"] = np.empty(B.asp_prep_pack_bytes(k, r), np.uint8)
+        B.asp_pack_prep(k, r, s, v, out["prep"])
         return out
 
     @classmethod
-    def from_host(cls, packed: dict, s, v, bias, device="cuda") -> "PackedLayer":
+    def from_host(cls, packed: dict, bias, device="cuda") -> "PackedLayer":
         n, kh = packed["w_codes"].shape
         k = kh * 2
-        r = 0 if v is None else v.shape[1]
+        r = 0 if packed["wv"] is None else packed["wv"].shape[1]
 
         def up(a, dtype=None):
             if a is None:
@@ -63,16 +64,15 @@ class PackedLayer:
             return t.to(device)
 
         return cls(n, k, r, up(packed["w_codes"]), up(packed["w_scales"]),
-                   up(packed["wv"], torch.int16), up(v if v is None else np.asarray(v, np.float32)),
-                   up(np.asarray(s, np.float32)),
+                   up(packed["wv"], torch.int16), up(packed["prep"]),
                    up(None if bias is None else np.asarray(bias, np.float32)))
 
     @classmethod
     def pack(cls, w, s, v, bias, device="cuda", n_threads: int = 0) -> "PackedLayer":
-        return cls.from_host(cls.pack_host(w, s, v, n_threads), s, v, bias, device)
+        return cls.from_host(cls.pack_host(w, s, v, n_threads), bias, device)
 
     def workspace(self, M: int) -> torch.Tensor:
-        n = B.asp_workspace_bytes(M, self.K, self.r)
+        n = B.asp_workspace_bytes(M, self.N, self.K, self.r)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.w_codes.device)
 
     def forward(self, x: torch.Tensor, y_dtype: str = "f32", workspace=None, y=None,
@@ -85,7 +85,7 @@ class PackedLayer:
             y = torch.empty((M, self.N), device=x.device,
                             dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16)
         ws = self.workspace(M) if workspace is None else workspace
-        B.asp_forward(x, x_dtype, M, self.N, self.K, self.r, self.s, self.v, self.w_codes,
+        B.asp_forward(x, x_dtype, M, self.N, self.K, self.r, self.prep, self.w_codes,
                       self.w_scales, self.wv, self.bias, y, B.DTYPES[y_dtype], ws, ws.numel(),
                       stream)
         return y
