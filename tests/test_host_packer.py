@@ -133,12 +133,12 @@ def test_prep_pack_constants(K, r):
     pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
     B.asp_pack_prep(K, r, lay.s, lay.v, pack)
     up = lambda b: (b + 255) // 256 * 256
-    rp16, rp32 = (r + 15) // 16 * 16, (r + 31) // 32 * 32
+    rp32 = (r + 31) // 32 * 32
     off_vth = up(4 * K)
     off_vtl = off_vth + up(2 * rp32 * K)
     off_vh = off_vtl + up(2 * rp32 * K)
-    off_vl = off_vh + up(2 * K * rp16)
-    assert pack.nbytes == off_vl + up(2 * K * rp16)
+    off_vl = off_vh + up(2 * K * rp32)
+    assert pack.nbytes == off_vl + up(2 * K * rp32)
     cvec = pack[:4 * K].view(np.float32)
     want_c = (1.0 / (lay.s.astype(np.float64) * np.sqrt(128.0))).astype(np.float32)
     assert np.array_equal(cvec, want_c)
@@ -146,8 +146,8 @@ def test_prep_pack_constants(K, r):
         return
     vth = pack[off_vth:off_vth + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
     vtl = pack[off_vtl:off_vtl + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
-    vh = pack[off_vh:off_vh + 2 * K * rp16].view(np.uint16).reshape(K, rp16)
-    vl = pack[off_vl:off_vl + 2 * K * rp16].view(np.uint16).reshape(K, rp16)
+    vh = pack[off_vh:off_vh + 2 * K * rp32].view(np.uint16).reshape(K, rp32)
+    vl = pack[off_vl:off_vl + 2 * K * rp32].view(np.uint16).reshape(K, rp32)
     v64 = lay.v.astype(np.float64)
     vpp = OH.block_rotate(v64.T).T / lay.s.astype(np.float64)[:, None]   # diag(1/s) H V
     got = _bf16_pair_value(vth[:r], vtl[:r]).T

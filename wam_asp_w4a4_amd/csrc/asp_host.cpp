@@ -205,8 +205,8 @@ int32_t asp_pack_prep(int64_t K, int32_t r, const float* s, const float* v, uint
       vtl[(int64_t)c * K + k] = bf16_from_double(vpp - bf16_value(hi));
       const double vv = (double)v[k * r + c];
       const uint16_t vhi = bf16_from_double(vv);
-      vh[k * L.rp16 + c] = vhi;
-      vl[k * L.rp16 + c] = bf16_from_double(vv - bf16_value(vhi));
+      vh[k * L.rp32 + c] = vhi;
+      vl[k * L.rp32 + c] = bf16_from_double(vv - bf16_value(vhi));
     }
   }
   return ASP_OK;

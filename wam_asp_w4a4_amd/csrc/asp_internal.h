@@ -31,9 +31,9 @@ int32_t check_rank(int32_t r);
 //   cvec   K float32          1 / (s_k * sqrt(128))
 //   vt_hi  rp32 x K bf16      V'' = diag(1/s) H V, transposed, high part
 //   vt_lo  rp32 x K bf16      V'' low part (V'' - hi, rounded to bf16)
-//   v_hi   K x rp16 bf16      V, high part
-//   v_lo   K x rp16 bf16      V, low part
-// with rp16 / rp32 = r rounded up to 16 / 32 and the padding zero.
+//   v_hi   K x rp32 bf16      V, high part
+//   v_lo   K x rp32 bf16      V, low part
+// with rp32 = r rounded up to 32 and the padding zero.
 struct PrepPackLayout {
   size_t cvec, vt_hi, vt_lo, v_hi, v_lo, total;
   int rp16, rp32;
@@ -48,8 +48,8 @@ inline PrepPackLayout prep_pack_layout(int64_t K, int32_t r) {
   L.vt_hi = up((size_t)K * 4);
   L.vt_lo = L.vt_hi + up((size_t)L.rp32 * K * 2);
   L.v_hi = L.vt_lo + up((size_t)L.rp32 * K * 2);
-  L.v_lo = L.v_hi + up((size_t)K * L.rp16 * 2);
-  L.total = L.v_lo + up((size_t)K * L.rp16 * 2);
+  L.v_lo = L.v_hi + up((size_t)K * L.rp32 * 2);
+  L.total = L.v_lo + up((size_t)K * L.rp32 * 2);
   return L;
 }
 

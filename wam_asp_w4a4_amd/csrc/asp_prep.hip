@@ -46,6 +46,13 @@ __device__ __forceinline__ void half_swap(uint32_t& x, uint32_t& y) {
   y = r[1];
 }
 
+// Exchange across lane rows (16 lanes): even rows get (x of both rows), odd rows (y of both).
+__device__ __forceinline__ void half_swap16(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8_t, q); }
 
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
@@ -143,8 +150,58 @@ __global__ void __launch_bounds__(256) k_prep_u(const XT* __restrict__ x, int M,
 }
 
 // ---------------------------------------------------------------------------
-// k_prep_quant: workgroup = 4 waves sharing 32 rows; wave w of workgroup
-// (i, j) handles 128-column blocks 4j + w, 4j + w + 4*gridDim.y, ...
+// k_prep_quant: a wave works on units of 16 rows x one 128-column Hadamard
+// block.  Lane l holds row l%16; its lane quarter q = l/16 selects columns.
+//
+//  load layout:  the lane holds columns 64*b + 16*q + j (b = 0..1, j = 0..15):
+//                two runs of 16 consecutive columns, so loads are 32 bytes.
+//  transform:    column bits 0..3 (j) and 6 (b) are butterflied in-register;
+//                bit 4 (lane bit q0) and bit 5 (lane bit q1) across lane rows
+//                with v_permlane16_swap / v_permlane32_swap on value pairs
+//                that differ in column bit 2, resp. 3.  Each swap-butterfly
+//                trades the lane bit with that register bit, which leaves the
+//                lane quarter holding column bits 2..3: tile t = 16 columns,
+//                the lane's 4 consecutive columns 16t + 4q + i -- exactly the
+//                output layout of a 16x16 MFMA with the block's columns as
+//                its rows and the 16 rows of x as its columns.
+//  deflation:    acc_t += V[cols of tile t] (-u)^T via v_mfma_f32_16x16x32_bf16
+//                with bf16 hi/lo splits (hi*hi + hi*lo + lo*hi).
+//  quantise:     tile t is one NVFP4 block; its maximum across the four lane
+//                quarters comes from two cross-lane maxima, and pairs of
+//                tiles' 16-bit code groups are merged into 32-bit words by one
+//                v_permlane16_swap.
+//
+// Workgroup = 4 waves on the same 16 rows; wave w of workgroup (i, j) takes
+// blocks 4j + w, 4j + w + 4*gridDim.y, ...
+
+__device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(y), false, false);
+  const float a = bitsf(r[0]), b = bitsf(r[1]);
+  x = a + b;
+  y = a - b;
+}
+
+__device__ __forceinline__ void load16(const float* p, float* v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 a = reinterpret_cast<const float4*>(p)[k];
+    v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+  }
+}
+
+__device__ __forceinline__ void load16(const uint16_t* p, float* v) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[k];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[8 * k + 2 * e] = bits_f32(w[e] << 16);
+      v[8 * k + 2 * e + 1] = bits_f32(w[e] & 0xFFFF0000u);
+    }
+  }
+}
+
 template <typename XT, int KS>
 __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, int M, int K, int r,
                                                     const float* __restrict__ cvec,
@@ -155,20 +212,21 @@ __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, in
                                                     uint8_t* __restrict__ scales,
                                                     float* __restrict__ u_out,
                                                     float* __restrict__ pre) {
-  constexpr int RP = KS * 16;  // padded rank (row stride of vh / vl)
-  __shared__ float us[32][RP > 0 ? RP + 1 : 1];
+  constexpr int RP = KS * 32;  // padded rank (row stride of vh / vl)
+  __shared__ float us[16][RP > 0 ? RP + 1 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.x * 32;
-  const int m = m0 + l32;
+  const int q = lane >> 4, l16 = lane & 15;
+  const int m0 = blockIdx.x * 16;
+  const int m = m0 + l16;
   const int64_t mc = min(m, M - 1);
   const bool mok = m < M;
   const int nblk = K / 128;
 
-  // -u for the 32 rows, as the bf16 hi/lo B operand of the deflation MFMA
+  // -u for the 16 rows, as the bf16 hi/lo B operand of the deflation MFMA:
+  // lane supplies row l%16, K-elements 8q .. 8q+7 of each 32-step
   bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
   if constexpr (KS > 0) {
-    for (int i = tid; i < 32 * RP; i += 256) {
+    for (int i = tid; i < 16 * RP; i += 256) {
       const int rr = i / RP, c = i % RP;
       float acc = 0.0f;
       if (c < r && m0 + rr < M)
@@ -178,137 +236,125 @@ __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, in
     }
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         uint16_t hi, lo;
-        split_bf16(-us[l32][16 * ks + 8 * h + e], hi, lo);
-        nuh[ks][e] = bf16_from_bits(hi);
-        nul[ks][e] = bf16_from_bits(lo);
+        split_bf16(-us[l16][32 * kk + 8 * q + e], hi, lo);
+        nuh[kk][e] = bf16_from_bits(hi);
+        nul[kk][e] = bf16_from_bits(lo);
       }
   }
 
   for (int b = blockIdx.y * 4 + wave; b < nblk; b += gridDim.y * 4) {
     const int col0 = b * 128;
-    // w[g][e]: column col0 + 16g + 8h + e
-    float w[8][8];
+    // w[bb][j]: column col0 + 64*bb + 16*q + j
+    float w[2][16];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      float cv[8];
-      load8(x + mc * K + col0 + 16 * g + 8 * h, w[g]);
-      load8(cvec + col0 + 16 * g + 8 * h, cv);
+    for (int bb = 0; bb < 2; ++bb) {
+      const int c = col0 + 64 * bb + 16 * q;
+      float cv[16];
+      load16(x + mc * K + c, w[bb]);
+      load16(cvec + c, cv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[g][e] *= cv[e];
+      for (int j = 0; j < 16; ++j) w[bb][j] *= cv[j];
     }
-    // Sylvester butterflies on column bits 0..2 (index e) and 4..6 (index g)
+    // Sylvester butterflies on column bits 0..3 (j) and 6 (bb)
 #pragma unroll
-    for (int hs = 1; hs < 8; hs <<= 1)
+    for (int hs = 1; hs < 16; hs <<= 1)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if ((e & hs) == 0) {
-            const float a = w[g][e], c = w[g][e + hs];
-            w[g][e] = a + c;
-            w[g][e + hs] = a - c;
+        for (int j = 0; j < 16; ++j)
+          if ((j & hs) == 0) {
+            const float a = w[bb][j], c = w[bb][j + hs];
+            w[bb][j] = a + c;
+            w[bb][j + hs] = a - c;
           }
 #pragma unroll
-    for (int gs = 1; gs < 8; gs <<= 1)
+    for (int j = 0; j < 16; ++j) {
+      const float a = w[0][j], c = w[1][j];
+      w[0][j] = a + c;
+      w[1][j] = a - c;
+    }
+    // column bit 4 (lane bit q0) against column bit 2 (j bit 2), then column
+    // bit 5 (lane bit q1) against column bit 3 (j bit 3)
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        if ((g & gs) == 0)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float a = w[g][e], c = w[g + gs][e];
-            w[g][e] = a + c;
-            w[g + gs][e] = a - c;
-          }
-    // column bit 3 lives in the lane half: butterfly across halves on the
-    // pairs (e, e+4).  Afterwards the lane half holds column bit 2 and the
-    // pair slot holds column bit 3 -- the MFMA accumulator layout, where
-    // element v = 4a + b of tile t is column 32t + 8a + 4h + b.
-    f32x16_t acc[4];
+      for (int j = 0; j < 16; ++j)
+        if ((j & 4) == 0) swap16_butterfly(w[bb][j], w[bb][j + 4]);
 #pragma unroll
-    for (int g = 0; g < 8; ++g)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        float lo = w[g][bb], hi = w[g][bb + 4];
-        half_swap_butterfly(lo, hi);
-        const int a = 2 * (g & 1);
-        acc[g >> 1][4 * a + bb] = lo;
-        acc[g >> 1][4 * (a + 1) + bb] = hi;
-      }
+      for (int j = 0; j < 16; ++j)
+        if ((j & 8) == 0) half_swap_butterfly(w[bb][j], w[bb][j + 8]);
+    // now w[bb][j] is column 16*t + 4*q + (j & 3) with tile t = (j >> 2) + 4*bb
+    f32x4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] = w[t >> 2][4 * (t & 3) + i];
     if constexpr (KS > 0) {
-      // x_d = x_tilde - u V^T, transposed: rows of the MFMA are the columns
-      // of this block (A = V rows), its columns are the 32 rows (B = -u).
-      // the four tiles' MFMAs are interleaved so that consecutive MFMAs are
-      // independent (no back-to-back accumulator dependence)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8_t a_hi[4], a_lo[4];
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8_t a_hi[8], a_lo[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t vrow = (int64_t)(col0 + 32 * t + l32) * RP + 16 * ks + 8 * h;
+        for (int t = 0; t < 8; ++t) {
+          const int64_t vrow = (int64_t)(col0 + 16 * t + l16) * RP + 32 * kk + 8 * q;
           a_hi[t] = as_bf16x8(*reinterpret_cast<const uint4*>(vh + vrow));
           a_lo[t] = as_bf16x8(*reinterpret_cast<const uint4*>(vl + vrow));
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[t], nuh[ks], acc[t], 0, 0, 0);
+        for (int t = 0; t < 8; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nuh[kk], acc[t], 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[t], nul[ks], acc[t], 0, 0, 0);
+        for (int t = 0; t < 8; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nul[kk], acc[t], 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[t], nuh[ks], acc[t], 0, 0, 0);
+        for (int t = 0; t < 8; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], nuh[kk], acc[t], 0, 0, 0);
       }
     }
-    // NVFP4: block g = columns col0 + 16g .. +15; this lane holds columns
-    // 16g + 4h + bb (slot 0) and 16g + 8 + 4h + bb (slot 1), the other lane
-    // half the rest.
-    float amax[8];
+    // NVFP4 per tile: maximum over the tile's 16 columns = 4 lane quarters
+    uint32_t sc[8];
+    float sd[8];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int t = g >> 1, a = 2 * (g & 1);
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(acc[t][4 * a + i]));
-      amax[g] = mx;
+    for (int t = 0; t < 8; ++t) {
+      float mx = fmaxf(fmaxf(fabsf(acc[t][0]), fabsf(acc[t][1])),
+                       fmaxf(fabsf(acc[t][2]), fabsf(acc[t][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      sc[t] = block_scale_code(mx);
+      sd[t] = e4m3_decode(sc[t]);
     }
+    uint8_t* crow = codes + mc * (K / 2) + col0 / 2;
 #pragma unroll
-    for (int g = 0; g < 8; g += 2) {
-      uint32_t p = fbits(amax[g]), q = fbits(amax[g + 1]);
-      half_swap(p, q);  // half 0: block g of both halves; half 1: block g+1
-      uint32_t both = fbits(fmaxf(bitsf(p), bitsf(q)));
-      uint32_t both2 = both;
-      half_swap(both, both2);  // everyone: (block g, block g+1)
-      amax[g] = bitsf(both);
-      amax[g + 1] = bitsf(both2);
-    }
-    uint8_t* crow = codes + mc * (K / 2);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int t = g >> 1, a = 2 * (g & 1);
-      const uint32_t sc = block_scale_code(amax[g]);
-      const float sd = e4m3_decode(sc);
+    for (int t = 0; t < 8; t += 2) {
       uint32_t g0 = 0, g1 = 0;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        g0 |= e2m1_code(acc[t][4 * a + bb], sd) << (4 * bb);
-        g1 |= e2m1_code(acc[t][4 * (a + 1) + bb], sd) << (4 * bb);
+      for (int i = 0; i < 4; ++i) {
+        g0 |= e2m1_code(acc[t][i], sd[t]) << (4 * i);
+        g1 |= e2m1_code(acc[t + 1][i], sd[t + 1]) << (4 * i);
       }
-      half_swap(g0, g1);  // half 0: columns 16g+0..3 | 4..7, half 1: 8..11 | 12..15
-      const uint32_t word = g0 | (g1 << 16);
+      // even lane rows: tile t, columns 8*q1 .. +7; odd rows: tile t+1
+      half_swap16(g0, g1);
       if (mok) {
-        *reinterpret_cast<uint32_t*>(crow + (col0 + 16 * g + 8 * h) / 2) = word;
-        if (h == 0) scales[mc * (K / 16) + (col0 + 16 * g) / 16] = (uint8_t)sc;
-        if (pre) {
-          float* prow = pre + mc * K + col0 + 16 * g + 4 * h;
-          reinterpret_cast<float4*>(prow)[0] =
-              make_float4(acc[t][4 * a], acc[t][4 * a + 1], acc[t][4 * a + 2], acc[t][4 * a + 3]);
-          reinterpret_cast<float4*>(prow + 8)[0] =
-              make_float4(acc[t][4 * a + 4], acc[t][4 * a + 5], acc[t][4 * a + 6], acc[t][4 * a + 7]);
-        }
+        const int tt = t + (q & 1);
+        *reinterpret_cast<uint32_t*>(crow + 8 * tt + 4 * (q >> 1)) = g0 | (g1 << 16);
+      }
+    }
+    if (mok) {
+      // lane quarter q stores the scales of tiles 2q and 2q+1
+      const uint32_t pair = (q == 0 ? sc[0] | sc[1] << 8
+                           : q == 1 ? sc[2] | sc[3] << 8
+                           : q == 2 ? sc[4] | sc[5] << 8 : sc[6] | sc[7] << 8);
+      *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) = (uint16_t)pair;
+      if (pre) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          *reinterpret_cast<float4*>(pre + mc * K + col0 + 16 * t + 4 * q) =
+              make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
       }
     }
   }
@@ -347,16 +393,14 @@ int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t*
     ASP_TRY(launch_status("prep_u"));
   }
   const int64_t nblk = K / 128;
-  const dim3 gb((unsigned)((M + 31) / 32), (unsigned)((nblk + 3) / 4));
+  const dim3 gb((unsigned)((M + 15) / 16), (unsigned)((nblk + 3) / 4));
 #define ASP_PREP_QUANT(KS_)                                                                     \
   hipLaunchKernelGGL((k_prep_quant<XT, KS_>), gb, dim3(256), 0, stream, x, (int)M, (int)K, (int)r, \
                      cvec, vh, vl, u_part, S, x_codes, x_scales, u, prequant)
-  switch (L.rp16 / 16) {
+  switch (L.rp32 / 32) {
     case 0: ASP_PREP_QUANT(0); break;
     case 1: ASP_PREP_QUANT(1); break;
-    case 2: ASP_PREP_QUANT(2); break;
-    case 3: ASP_PREP_QUANT(3); break;
-    default: ASP_PREP_QUANT(4); break;
+    default: ASP_PREP_QUANT(2); break;
   }
 #undef ASP_PREP_QUANT
   return launch_status("prep_quant");
