@@ -9,10 +9,9 @@ every buffer (>= 1 GiB in total) so that each step reads from HBM rather than
 from the 256 MB Infinity Cache.
 
 Timing: W warm-up steps, then exactly K steps replayed from one HIP graph,
-bracketed by synchronize() and HIP events on the capture stream.  A second,
-eager pass brackets every kernel launch with HIP events (launch backlog built
-first, so events bracket kernels back to back) to get each kernel's average
-duration for the roofline figure.
+bracketed by synchronize() and HIP events on the launch stream.  For the
+roofline figure each kernel is then timed alone: a graph of its launches over
+the replicas, replayed between two events, gives its average duration.
 
 Prints one JSON line.  Default workload: the action-expert attention
 projection pair (two layers, M=256 tokens, K=N=1024, rank 32, bf16 in and out).
@@ -21,8 +20,10 @@ projection pair (two layers, M=256 tokens, K=N=1024, rank 32, bf16 in and out).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,6 +37,16 @@ METRIC = "deflated-ASP NVFP4 linear effective TFLOP/s + % of roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
 RIDGE = F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+CSRC = os.path.join(ROOT, "wam_asp_w4a4_amd", "csrc")
+# the sources each kernel is built from: a traffic figure measured with
+# hardware counters stays valid only while these files are unchanged
+KERNEL_SOURCES = {
+    "k_prep": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+    "k_gemm": ["asp_gemm.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+}
+WORKLOAD_SLUGS = {0: "single_M64_K512_N512", 1: "action_attn_M256_K1024_N1024",
+                  2: "action_ffn_M256", 3: "video_attn_M4096_K3072_N3072"}
+COPY_CALIBRATION_BYTES = 256 << 20
 
 
 def layer_flops(M, N, K, r):
@@ -77,7 +88,32 @@ def parse():
     ap.add_argument("--kernel-timing-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy three times (the reference "
+                         "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+def kernel_source_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{WORKLOAD_SLUGS[workload]}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_digest(kernel):
+        return None
+    return int(val.group(1))
 
 
 def main():
@@ -151,6 +187,13 @@ def main():
     # ---- warm-up, then K steps from one graph
     for i in range(args.warmup):
         step(i)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -173,52 +216,60 @@ def main():
                      for l, _, _ in host)
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-kernel durations with events around every launch (eager, backlogged)
+    # ---- per-kernel durations: each kernel alone, nk launches cycling through
+    # the replicas, replayed from a graph of its own between two events on the
+    # launch stream (graph replay keeps host launch cost out of the figure)
     nk = max(1, min(args.kernel_timing_steps, args.steps))
-    big = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
-    evs = []
-    torch.cuda.synchronize()
-    # GPU backlog (about 0.1 ms of matmul per launch pair queued below) so the
-    # timed launches queue up behind it and their events bracket them tightly
-    for _ in range(16 + nk * len(layers)):
-        big = big @ big
-        big = big / big.abs().amax().clamp_min(1.0)
+    up = lambda b: (b + 255) // 256 * 256
+    launches = []
     for i in range(nk):
         for lay, p, x, y, ws in replicas[i % R]:
             M, N, K, r = lay.M, lay.N, lay.K, lay.r
-            up = lambda b: (b + 255) // 256 * 256
             xc = ws[: M * K // 2]
             off = up(M * K // 2)
             xs = ws[off: off + M * K // 16]
             off2 = off + up(M * K // 16)
             u = ws[off2: off2 + 4 * M * r].view(torch.float32) if r else None
-            off3 = off2 + up(4 * M * r)
-            scratch = ws[off3:]
-            ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            ea.record(stream)
-            B.asp_act_prep(x, B.DTYPES[lay.x_dtype], M, K, r, p.prep, xc, xs, u, None, scratch,
-                           scratch.numel())
-            eb.record(stream)
-            B.asp_gemm_lowrank(xc, xs, u, M, N, K, r, p.w_codes, p.w_scales, p.wv, p.bias, y,
-                               B.DTYPES[y_dtype])
-            ec.record(stream)
-            evs.append((lay, ea, eb, ec))
-    torch.cuda.synchronize()
-    prep_ms = gemm_ms = 0.0
+            launches.append((lay, p, x, y, xc, xs, u))
+
+    def prep_launch(lay, p, x, y, xc, xs, u):
+        B.asp_act_prep(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None)
+
+    def gemm_launch(lay, p, x, y, xc, xs, u):
+        B.asp_gemm_lowrank(xc, xs, u, lay.M, lay.N, lay.K, lay.r, p.w_codes, p.w_scales, p.wv,
+                           p.bias, y, B.DTYPES[y_dtype])
+
+    def graph_ms(fn):
+        for a in launches[: len(layers)]:  # warm the code path outside the capture
+            fn(*a)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for a in launches:
+                fn(*a)
+        torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ea.record(stream)
+        g.replay()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb)
+
+    prep_ms = graph_ms(prep_launch)   # also leaves valid codes in every workspace used
+    gemm_ms = graph_ms(gemm_launch)
     prep_b = gemm_b = prep_f = gemm_f = 0
-    for lay, ea, eb, ec in evs:
+    for lay, *_ in launches:
         xb = 2 if lay.x_dtype == "bf16" else 4
-        prep_ms += ea.elapsed_time(eb)
-        gemm_ms += eb.elapsed_time(ec)
         prep_b += prep_bytes(lay.M, lay.K, lay.r, xb)
         gemm_b += gemm_bytes(lay.M, lay.N, lay.K, lay.r, yb)
         prep_f += prep_flops(lay.M, lay.K, lay.r)
         gemm_f += gemm_flops(lay.M, lay.N, lay.K, lay.r)
+    evs = launches
     n_launch = len(evs)
     if gemm_ms >= prep_ms:
         name, ms, nbytes, nflops = "k_gemm", gemm_ms, gemm_b, gemm_f
     else:
-        name, ms, nbytes, nflops = "k_act_prep", prep_ms, prep_b, prep_f
+        name, ms, nbytes, nflops = "k_prep", prep_ms, prep_b, prep_f
     avg_us = ms / n_launch * 1e3
     gbs = nbytes / (ms * 1e-3) / 1e9
     tfs = nflops / (ms * 1e-3) / 1e12
@@ -230,8 +281,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
     roof.update({
-        "traffic": None,
+        "traffic": measured_traffic(name, args.workload),
         "kernel": name,
+        "source_digest": kernel_source_digest(name),
         "avg_launch_us": round(avg_us, 3),
         "launches": n_launch,
         "algorithmic_bytes_per_launch": nbytes // n_launch,

@@ -117,10 +117,7 @@ def gpu_act_prep(lay):
     pre = torch.empty((M, K), dtype=torch.float32, device=DEV)
     pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
     B.asp_pack_prep(K, r, lay.s, lay.v, pack)
-    nws = B.asp_act_prep_workspace_bytes(M, K, r)
-    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=DEV)
-    B.asp_act_prep(x_device(lay), B.DTYPES[lay.x_dtype], M, K, r, dev(pack), xc, xs, u, pre,
-                   ws, nws)
+    B.asp_act_prep(x_device(lay), B.DTYPES[lay.x_dtype], M, K, r, dev(pack), xc, xs, u, pre)
     return host(xc), host(xs), (host(u) if r else None), host(pre)
 
 
@@ -189,6 +186,26 @@ def test_gemm_on_oracle_codes(lay):
     # the bf16 output is the RNE cast of an fp32 result: within one bf16 step of it
     assert np.all(np.abs(got16 - got) <= np.abs(got) * 2.0 ** -8 + 1e-30)
     assert rel_fro(got16, want) <= 2e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (1024, 6144, 512)], ids=["small-tiles", "large-tiles"])
+def test_gemm_every_scale_code(M, N, K):
+    """Random codes under every finite E4M3 scale code (subnormal to 448) on
+    both operands: the device's scale decoding and contraction against the
+    float64 dequantised product (fp32 output; accumulation order only)."""
+    rng = np.random.default_rng(M + N + K)
+    xc = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    xs = (np.arange(M * K // 16) % 0x7F).astype(np.uint8)
+    ws = (np.arange(N * K // 16) % 0x7F).astype(np.uint8)
+    rng.shuffle(xs)
+    rng.shuffle(ws)
+    xs, ws = xs.reshape(M, K // 16), ws.reshape(N, K // 16)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    B.asp_gemm_lowrank(dev(xc), dev(xs), None, M, N, K, 0, dev(wc), dev(ws), None, None, y,
+                       B.DTYPES["f32"])
+    want = OF.dequantize_nvfp4(xc, xs) @ OF.dequantize_nvfp4(wc, ws).T
+    assert rel_fro(host(y), want) <= 1e-5
 
 
 # -------------------------------------------------------------- whole layer

@@ -1,9 +1,11 @@
 // Device-side helpers shared by the gfx950 translation units of libasp:
-// vector types, the NVFP4 lane-pair quantiser, operand decoding for MFMA,
+// vector types, the NVFP4 block quantiser, operand decoding for MFMA,
 // launch/argument checks, and the internal launchers each unit exports.
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "asp.h"
 #include "asp_internal.h"
@@ -19,37 +21,49 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1/sqrt(128), rounded to float32
 
-// Quantise the 8 consecutive values a lane holds; lanes (2j, 2j+1) hold one
-// 16-element block.  Returns the 8 packed 4-bit codes (element e in bits
-// 4e..4e+3) and the block's E4M3 scale code.  Every lane of the wave calls it.
-__device__ __forceinline__ uint32_t quantize8_pair(const float (&v)[8], uint32_t& scale) {
+// A float32 quotient of v by the decoded block scale sd that falls on the same
+// side of every E2M1 grid midpoint as the exact v/sd, and on a midpoint exactly
+// when v/sd is one.  q0 = v * rinv (rinv = 1/sd to within an ulp) is within a
+// few ulps of v/sd, so the remainder q0*sd - v is exactly representable (sd has
+// 4 significant bits) and one fma gives it exactly; q1 = q0 - e*rinv is then
+// v/sd to far less than an ulp.  A v/sd that is not a midpoint lies more than
+// half an ulp from every midpoint (a midpoint times sd has at most 7
+// significant bits, so v differs from it by at least an ulp of v), hence q1 is
+// on the same side.  q1 keeps v's sign, -0 included (-0 - +0 = -0), so the
+// hardware conversion copies the sign bit as the format requires; rinv == 0
+// (a zero scale) gives magnitude 0.  Valid for |v| <= ~6.4 sd, which a block's
+// own scale guarantees (larger quotients only arise with the saturated scale
+// 448, where q0 stays finite and the conversion saturates).
+__device__ __forceinline__ float e2m1_quotient(float v, float sd, float rinv) {
+  const float q0 = v * rinv;
+  const float e = __builtin_fmaf(q0, sd, -v);
+  return __builtin_fmaf(-e, rinv, q0);
+}
+
+// NVFP4 block of 16 values held by one lane in column order: its E4M3 scale
+// code and the 8 bytes of packed codes.  v_cvt_scalef32_pk_fp4_f32 with scale
+// 1 rounds to nearest, ties to the even code, and saturates at 6; it writes
+// the code of its first operand into the low nibble of the selected byte.
+__device__ __forceinline__ uint2 quantize_block(const float (&v)[16], uint32_t& scale) {
   float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(v[c]));
   scale = block_scale_code(amax);
   const float sd = e4m3_decode(scale);
-  uint32_t word = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) word |= e2m1_code(v[e], sd) << (4 * e);
-  return word;
-}
-
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0];
-  const float4 b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[2 * e] = bits_f32(w[e] << 16);
-    v[2 * e + 1] = bits_f32(w[e] & 0xFFFF0000u);
-  }
+  const float rinv = sd > 0.0f ? __builtin_amdgcn_rcpf(sd) : 0.0f;
+  auto pk = [&](uint32_t w, int c, auto sel) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, e2m1_quotient(v[c], sd, rinv),
+                                                    e2m1_quotient(v[c + 1], sd, rinv), 1.0f,
+                                                    decltype(sel)::value);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  uint32_t w0 = 0, w1 = 0;
+  w0 = pk(w0, 0, S0{}); w0 = pk(w0, 2, S1{}); w0 = pk(w0, 4, S2{}); w0 = pk(w0, 6, S3{});
+  w1 = pk(w1, 8, S0{}); w1 = pk(w1, 10, S1{}); w1 = pk(w1, 12, S2{}); w1 = pk(w1, 14, S3{});
+  return make_uint2(w0, w1);
 }
 
 // 8 packed E2M1 codes (one K-step's worth for one MFMA lane) times their
@@ -101,10 +115,9 @@ inline int32_t check_mk(int64_t M, int64_t K) {
 }
 
 // Internal launchers (validate, then enqueue on `stream`).
-size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r);
 int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                       const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream);
+                      float* prequant, hipStream_t stream);
 int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype);
 int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
                   int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,

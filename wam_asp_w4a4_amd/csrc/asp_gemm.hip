@@ -16,9 +16,9 @@
 // low-rank branch adds ceil(r/16) bf16 MFMA K-steps into the same
 // accumulators; bias and the output cast follow.
 //
-// Decoding costs two VALU instructions per 8 elements per operand fragment;
-// three waves share each SIMD so that one wave's decode overlaps another's
-// MFMAs.  Codes and scales are staged through double-buffered LDS in stages of
+// Decoding a lane's 8 elements of a fragment costs 8 VALU instructions (four
+// 2-code conversions, four packed fp16 scale multiplies); two waves share each
+// SIMD so that one wave's decode overlaps the other's MFMAs.  Codes and scales are staged through double-buffered LDS in stages of
 // 256 K-elements (16 MFMA K-steps per workgroup barrier).  Tile rows are padded
 // so that the 32 rows a fragment reads hit distinct banks, and each lane reads
 // the one 32-bit code word it needs per K-step one step ahead of its use, so
@@ -71,10 +71,12 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in / gsize;
 }
 
-// two E4M3 scale bytes (bits 0..15 of w) as two exact fp16 values
+// E4M3 scale bytes 0,1 (hi = false) or 2,3 (hi = true) of w as two fp16
+// values: v_cvt_scalef32_pk_f16_fp8 with scale 1 decodes OCP E4M3FN, and every
+// finite E4M3 value (subnormals included) is an fp16 normal, so it is exact.
+template <bool HI>
 __device__ __forceinline__ uint32_t scale_pair_f16(uint32_t w) {
-  const float a = e4m3_decode(w & 0xFFu), b = e4m3_decode((w >> 8) & 0xFFu);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));  // exact: no rounding
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
 template <int WM, int WN, int TM, int TN>
@@ -161,8 +163,8 @@ __global__ void __launch_bounds__(WM * WN * 64)
         const uint32_t q[4] = {rs[j].x, rs[j].y, rs[j].z, rs[j].w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          d[2 * p] = scale_pair_f16(q[p]);
-          d[2 * p + 1] = scale_pair_f16(q[p] >> 16);
+          d[2 * p] = scale_pair_f16<false>(q[p]);
+          d[2 * p + 1] = scale_pair_f16<true>(q[p]);
         }
       }
   };
@@ -346,13 +348,14 @@ int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* 
   ASP_TRY(check_ptr(wv, "wv", r > 0));
   ASP_TRY(check_ptr(bias, "bias", false));
   ASP_TRY(check_ptr(y, "y", true));
-  // Tile choice.  Large layers use 64 x 64 per-wave tiles with 12 waves per
-  // workgroup (3 waves per SIMD hide the LDS and decode latency) on a
-  // 256 x 192 workgroup tile -- 256 tiles, one per CU, for a 4096 x 3072
-  // output.  Small layers use 64 x 64 tiles of 4 waves.
+  // Tile choice.  Large layers: 256 x 192 workgroup tiles (256 tiles, one per
+  // CU, for a 4096 x 3072 output) of 8 waves with 64 x 96 per-wave tiles: five
+  // fragment decodes feed six MFMAs per K-step, and two waves per SIMD overlap
+  // one wave's decode with the other's MFMAs.  Small layers: 64 x 64 tiles of
+  // 4 waves, for as many workgroups as the output allows.
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
   if (t192 >= 128)
-    return launch_gemm<4, 3, 2, 2>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
+    return launch_gemm<4, 2, 2, 3>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
                                    y, y_dtype, stream);
   return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y,
                                  y_dtype, stream);

@@ -1,25 +1,26 @@
 // Fused activation prep on gfx950: x/s, block Hadamard, u = x_tilde V,
 // deflation x_tilde - u V^T, NVFP4 quantise + pack (model card "FastWAM UR3
 // 3-task -- 4-bit quantisations", section "What ASP is, and what the deflated
-// form means").
+// form means").  One kernel, k_prep; a workgroup owns 16 rows of x.
 //
-// Two kernels, because every element of a row's deflated value needs the
-// row's full reduction u = x_tilde V first:
+// Every element of a row's deflated value needs the row's full reduction
+// u = x_tilde V first, so for r > 0 the workgroup covers the whole of K for
+// its rows and works in two phases:
 //
-//  k_prep_u      u partial sums over K-slices.  u = x_tilde V = x (diag(1/s) H V)
-//                = x V'', with V'' a per-layer constant, so this is a thin GEMM
-//                on the raw input: MFMA 32x32x16 bf16, x exact in bf16 (an fp32
-//                x is split into bf16 hi + lo), V'' split into bf16 hi + lo
-//                (about 16 significant bits; the dropped lo*lo term is below
-//                fp32 rounding of the sum).  Slices are summed in a fixed order
-//                by the second kernel, so results are deterministic.
-//  k_prep_quant  one wave per (32 rows, 128-column Hadamard block): load 8
-//                consecutive columns per lane, scale by 1/(s sqrt 128), six
-//                in-register butterfly stages, the seventh across lane halves
-//                with v_permlane32_swap, which also leaves the values in the
-//                32x32 MFMA accumulator layout; the deflation then runs as
-//                MFMA (V bf16 hi/lo) x (-u bf16 hi/lo) accumulated onto
-//                x_tilde; finally the NVFP4 quantiser and the code packing.
+//  phase 1  u.  u = x_tilde V = x (diag(1/s) H V) = x V'', with V'' a per-layer
+//           constant, so each wave contracts the raw rows of its Hadamard
+//           blocks against V'' on MFMA 16x16x32 bf16 (x is exact in bf16; an
+//           fp32 x is split into bf16 high + low; V'' is split into bf16 high +
+//           low, about 16 significant bits, the dropped low*low term lying
+//           below float32 rounding of the sum).  The waves' partial sums meet
+//           in LDS and are added in a fixed order: results are deterministic.
+//  phase 2  per (16 rows, 128-column block): scale by 1/(s sqrt 128), the
+//           Sylvester butterflies in registers and across lane rows, the
+//           deflation on MFMA, the NVFP4 quantiser and the packed stores.
+//           The raw x fragments of phase 1 stay in registers when they fit.
+//
+// With r == 0 there is no phase 1; a workgroup then takes a strip of blocks
+// and the grid also spans K.
 #include "asp_device.h"
 
 namespace asp {
@@ -28,29 +29,37 @@ namespace {
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Butterfly across lane halves for the value pair (x, y) that differ in the
-// column bit held in-register, while the lane-half bit h selects the column
-// bit being transformed.  On return lane half 0 holds x's two outputs and lane
-// half 1 holds y's: the in-register bit and the lane-half bit trade places.
-__device__ __forceinline__ void half_swap_butterfly(float& x, float& y) {
+// v_permlane32_swap / v_permlane16_swap on a value pair (x, y): lanes of the
+// lower half (resp. even 16-lane row) end with (x of own lanes, x of partner
+// lanes), lanes of the upper half (odd row) with (y of partner, y of own).
+// Applied to pairs that differ in one register index bit, it trades that bit
+// with the lane bit.
+__device__ __forceinline__ void swap32(float& x, float& y) {
   const auto r = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(y), false, false);
-  const float a = bitsf(r[0]), b = bitsf(r[1]);
+  x = bitsf(r[0]);
+  y = bitsf(r[1]);
+}
+
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(y), false, false);
+  x = bitsf(r[0]);
+  y = bitsf(r[1]);
+}
+
+// The same exchange followed by the butterfly (a + b, a - b) of the pair that
+// now sits in one lane: one Sylvester stage across lanes.
+__device__ __forceinline__ void swap32_butterfly(float& x, float& y) {
+  swap32(x, y);
+  const float a = x, b = y;
   x = a + b;
   y = a - b;
 }
 
-// Exchange so that lane half 0 gets (x of both halves) and half 1 gets (y of both).
-__device__ __forceinline__ void half_swap(uint32_t& x, uint32_t& y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-  x = r[0];
-  y = r[1];
-}
-
-// Exchange across lane rows (16 lanes): even rows get (x of both rows), odd rows (y of both).
-__device__ __forceinline__ void half_swap16(uint32_t& x, uint32_t& y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-  x = r[0];
-  y = r[1];
+__device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
+  swap16(x, y);
+  const float a = x, b = y;
+  x = a + b;
+  y = a - b;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8_t, q); }
@@ -60,179 +69,182 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16_rne(v - bits_f32((uint32_t)hi << 16));
 }
 
-// ---------------------------------------------------------------------------
-// k_prep_u: workgroup = 4 waves x 32 rows; blockIdx.y selects a K-slice.
-// A operand (rows of x): lane l supplies row l%32, K-elements 8*(l/32)..+7 of
-// each 16-step; B operand (columns of V''): lane l supplies column l%32.
-constexpr int kUChunk = 128;
+// Raw x of one (16 rows, 128 columns) unit as this lane loads it: columns
+// 64*(g >> 1) + 16*q + 8*(g & 1) + e (fragment g = 0..3, e = 0..7) of row l16,
+// q being the lane quarter.
+template <typename XT>
+struct XFrag;
 
-template <typename XT, int CT>
-__global__ void __launch_bounds__(256) k_prep_u(const XT* __restrict__ x, int M, int K, int r,
-                                                const uint16_t* __restrict__ vth,
-                                                const uint16_t* __restrict__ vtl,
-                                                float* __restrict__ u_part, int kslice) {
-  __shared__ uint4 sv[2][CT * 32][kUChunk / 8 + 1];  // V''^T chunk, hi and lo, padded rows
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int row0 = blockIdx.x * 128 + wave * 32;
-  const int64_t mc = min(row0 + l32, M - 1);
-  const int kb = blockIdx.y * kslice, ke = min(K, kb + kslice);
-
-  // one accumulator per product term, so consecutive MFMAs are independent
-  f32x16_t acc[CT], acc2[CT];
+template <>
+struct XFrag<uint16_t> {
+  uint4 f[4];  // 8 bf16 per fragment
+  __device__ __forceinline__ void load(const uint16_t* row, int col0, int q) {
 #pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = acc2[c][v] = 0.0f;
-
-  for (int k0 = kb; k0 < ke; k0 += kUChunk) {
-    // this lane's x fragments for the chunk (issued before the barrier)
-    uint4 xa[8];
-    uint4 xb[8];  // fp32 input: second half of the 8 values
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const XT* p = x + mc * K + k0 + 16 * ks + 8 * h;
-      if constexpr (sizeof(XT) == 2) {
-        xa[ks] = *reinterpret_cast<const uint4*>(p);
-      } else {
-        xa[ks] = reinterpret_cast<const uint4*>(p)[0];
-        xb[ks] = reinterpret_cast<const uint4*>(p)[1];
-      }
-    }
-    // stage V''^T for the chunk: CT*32 rows x 128 k, two pieces, 16 bytes per load
-    for (int i = tid; i < 2 * CT * 32 * (kUChunk / 8); i += 256) {
-      const int piece = i / (CT * 32 * (kUChunk / 8));
-      const int rem = i % (CT * 32 * (kUChunk / 8));
-      const int c = rem / (kUChunk / 8), seg = rem % (kUChunk / 8);
-      const uint16_t* src = piece ? vtl : vth;
-      sv[piece][c][seg] = *reinterpret_cast<const uint4*>(src + (int64_t)c * K + k0 + seg * 8);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8_t a_hi, a_lo;
-      if constexpr (sizeof(XT) == 2) {
-        a_hi = as_bf16x8(xa[ks]);
-      } else {
-        const float f[8] = {bitsf(xa[ks].x), bitsf(xa[ks].y), bitsf(xa[ks].z), bitsf(xa[ks].w),
-                            bitsf(xb[ks].x), bitsf(xb[ks].y), bitsf(xb[ks].z), bitsf(xb[ks].w)};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint16_t hi, lo;
-          split_bf16(f[e], hi, lo);
-          a_hi[e] = bf16_from_bits(hi);
-          a_lo[e] = bf16_from_bits(lo);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-        const bf16x8_t b_hi = as_bf16x8(sv[0][c * 32 + l32][2 * ks + h]);
-        const bf16x8_t b_lo = as_bf16x8(sv[1][c * 32 + l32][2 * ks + h]);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, b_hi, acc[c], 0, 0, 0);
-        acc2[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, b_lo, acc2[c], 0, 0, 0);
-        if constexpr (sizeof(XT) == 4)
-          acc2[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, b_hi, acc2[c], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+    for (int g = 0; g < 4; ++g)
+      f[g] = *reinterpret_cast<const uint4*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
   }
-  // accumulator element v of lane l: row 8*(v/4) + 4*(l/32) + v%4, column l%32
-#pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    const int col = c * 32 + l32;
-    if (col >= r) continue;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = row0 + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (row < M) u_part[((int64_t)blockIdx.y * M + row) * r + col] = acc[c][v] + acc2[c][v];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// k_prep_quant: a wave works on units of 16 rows x one 128-column Hadamard
-// block.  Lane l holds row l%16; its lane quarter q = l/16 selects columns.
-//
-//  load layout:  the lane holds columns 64*b + 16*q + j (b = 0..1, j = 0..15):
-//                two runs of 16 consecutive columns, so loads are 32 bytes.
-//  transform:    column bits 0..3 (j) and 6 (b) are butterflied in-register;
-//                bit 4 (lane bit q0) and bit 5 (lane bit q1) across lane rows
-//                with v_permlane16_swap / v_permlane32_swap on value pairs
-//                that differ in column bit 2, resp. 3.  Each swap-butterfly
-//                trades the lane bit with that register bit, which leaves the
-//                lane quarter holding column bits 2..3: tile t = 16 columns,
-//                the lane's 4 consecutive columns 16t + 4q + i -- exactly the
-//                output layout of a 16x16 MFMA with the block's columns as
-//                its rows and the 16 rows of x as its columns.
-//  deflation:    acc_t += V[cols of tile t] (-u)^T via v_mfma_f32_16x16x32_bf16
-//                with bf16 hi/lo splits (hi*hi + hi*lo + lo*hi).
-//  quantise:     tile t is one NVFP4 block; its maximum across the four lane
-//                quarters comes from two cross-lane maxima, and pairs of
-//                tiles' 16-bit code groups are merged into 32-bit words by one
-//                v_permlane16_swap.
-//
-// Workgroup = 4 waves on the same 16 rows; wave w of workgroup (i, j) takes
-// blocks 4j + w, 4j + w + 4*gridDim.y, ...
-
-__device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(y), false, false);
-  const float a = bitsf(r[0]), b = bitsf(r[1]);
-  x = a + b;
-  y = a - b;
-}
-
-__device__ __forceinline__ void load16(const float* p, float* v) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float4 a = reinterpret_cast<const float4*>(p)[k];
-    v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
-  }
-}
-
-__device__ __forceinline__ void load16(const uint16_t* p, float* v) {
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint4 a = reinterpret_cast<const uint4*>(p)[k];
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  __device__ __forceinline__ void get(int g, float* v) const {
+    const uint32_t w[4] = {f[g].x, f[g].y, f[g].z, f[g].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[8 * k + 2 * e] = bits_f32(w[e] << 16);
-      v[8 * k + 2 * e + 1] = bits_f32(w[e] & 0xFFFF0000u);
+      v[2 * e] = bits_f32(w[e] << 16);
+      v[2 * e + 1] = bits_f32(w[e] & 0xFFFF0000u);
     }
   }
-}
+};
 
-template <typename XT, int KS>
-__global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, int M, int K, int r,
-                                                    const float* __restrict__ cvec,
-                                                    const uint16_t* __restrict__ vh,
-                                                    const uint16_t* __restrict__ vl,
-                                                    const float* __restrict__ u_part, int S,
-                                                    uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales,
-                                                    float* __restrict__ u_out,
-                                                    float* __restrict__ pre) {
-  constexpr int RP = KS * 32;  // padded rank (row stride of vh / vl)
-  __shared__ float us[16][RP > 0 ? RP + 1 : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <>
+struct XFrag<float> {
+  float4 f[8];  // 8 floats per fragment
+  __device__ __forceinline__ void load(const float* row, int col0, int q) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4* p =
+          reinterpret_cast<const float4*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
+      f[2 * g] = p[0];
+      f[2 * g + 1] = p[1];
+    }
+  }
+  __device__ __forceinline__ void get(int g, float* v) const {
+    const float4 a = f[2 * g], b = f[2 * g + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// k_prep.  Lane l of a wave: row l16 = l % 16 of the workgroup's 16 rows, lane
+// quarter q = l / 16.
+//
+// Phase 1 (KS > 0): per block, 4 k-steps of v_mfma_f32_16x16x32_bf16 per 16
+// columns of u: A = raw x (row l16; fragment g supplies k-slots 8q..8q+7 --
+// any fixed pairing of k-slots with columns works as long as B uses the same),
+// B = rows of V''^T (u column l16, the same 8 columns).  Output: u row 4q + i,
+// column l16.
+//
+// Phase 2, per block:
+//  transform:  the lane's 32 values are columns 64*bb + 16*q + j (bb = 0..1,
+//              j = 0..15).  Column bits 0..3 (j) and 6 (bb) are butterflied in
+//              registers; bit 4 (lane bit q0) against register bit j2 with
+//              v_permlane16_swap, bit 5 (lane bit q1) against j3 with
+//              v_permlane32_swap.  Each swap-butterfly trades the lane bit with
+//              the register bit, leaving tile t = (j >> 2) + 4*bb, columns
+//              16t + 4q + (j & 3): the output layout of a 16x16 MFMA with the
+//              block's columns as its rows and the 16 rows of x as its columns.
+//  deflation:  acc_t += V[cols of tile t] (-u)^T, v_mfma_f32_16x16x32_bf16 with
+//              bf16 hi/lo splits (hi*hi + hi*lo + lo*hi).
+//  transpose:  two more swap stages (tile bit 2 with lane bit q1, tile bit 1
+//              with q0) give each lane the whole of tiles 2q and 2q+1, i.e. two
+//              complete NVFP4 blocks: column c of tile 2q+b sits in
+//              acc[b + 2*(c >> 2)][c & 3].
+//  quantise:   per block in one lane: amax, E4M3 scale, codes; one 16-byte
+//              code store and one 2-byte scale store per lane.
+//
+// Blocks of a wave: KS > 0, NB > 0: wave + i*nw for i < NB, raw x held in
+// registers between the phases; KS > 0, NB == 0: wave, wave + nw, ... with x
+// loaded again in phase 2; KS == 0: (blockIdx.y*NB + i)*nw + wave.
+template <typename XT, int KS, int NB>
+__global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, int K, int r,
+                                              const float* __restrict__ cvec,
+                                              const uint16_t* __restrict__ vth,
+                                              const uint16_t* __restrict__ vtl,
+                                              const uint16_t* __restrict__ vh,
+                                              const uint16_t* __restrict__ vl,
+                                              uint8_t* __restrict__ codes,
+                                              uint8_t* __restrict__ scales,
+                                              float* __restrict__ u_out,
+                                              float* __restrict__ pre) {
+  constexpr int RP = KS * 32;  // padded rank: row stride of V, rows of V''^T
+  constexpr int CT = KS * 2;   // 16-column tiles of u
+  constexpr int NH = NB > 0 ? NB : 1;
+  constexpr bool fp32_x = sizeof(XT) == 4;
+  __shared__ float up[KS > 0 ? 8 : 1][16][RP + 1];  // each wave's partial u
+  __shared__ float us[16][RP + 1];                  // u of the 16 rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int m0 = blockIdx.x * 16;
   const int m = m0 + l16;
   const int64_t mc = min(m, M - 1);
   const bool mok = m < M;
-  const int nblk = K / 128;
+  const int nblk = K >> 7;
+  const XT* xrow = x + mc * K;
 
-  // -u for the 16 rows, as the bf16 hi/lo B operand of the deflation MFMA:
-  // lane supplies row l%16, K-elements 8q .. 8q+7 of each 32-step
+  XFrag<XT> xr[NH];
+  auto block_of = [&](int i) {
+    return KS > 0 ? wave + i * nw : ((int)blockIdx.y * NH + i) * nw + wave;
+  };
+
+  // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
+  // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
   bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
+
   if constexpr (KS > 0) {
-    for (int i = tid; i < 16 * RP; i += 256) {
+    f32x4_t ah[CT], al[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ah[c][i] = al[c][i] = 0.0f;
+
+    auto contract = [&](const XFrag<XT>& xf, int col0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int koff = col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1);
+        bf16x8_t a_hi, a_lo;
+        if constexpr (!fp32_x) {
+          a_hi = as_bf16x8(xf.f[g]);
+        } else {
+          float f[8];
+          xf.get(g, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint16_t hi, lo;
+            split_bf16(f[e], hi, lo);
+            a_hi[e] = bf16_from_bits(hi);
+            a_lo[e] = bf16_from_bits(lo);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const int64_t off = (int64_t)(c * 16 + l16) * K + koff;
+          const bf16x8_t b_hi = as_bf16x8(*reinterpret_cast<const uint4*>(vth + off));
+          const bf16x8_t b_lo = as_bf16x8(*reinterpret_cast<const uint4*>(vtl + off));
+          ah[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, ah[c], 0, 0, 0);
+          al[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, al[c], 0, 0, 0);
+          if constexpr (fp32_x)
+            al[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b_hi, al[c], 0, 0, 0);
+        }
+      }
+    };
+
+    if constexpr (NB > 0) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int b = block_of(i);
+        if (b < nblk) xr[i].load(xrow, b * 128, q);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int b = block_of(i);
+        if (b < nblk) contract(xr[i], b * 128);
+      }
+    } else {
+      for (int b = wave; b < nblk; b += nw) {
+        xr[0].load(xrow, b * 128, q);
+        contract(xr[0], b * 128);
+      }
+    }
+    // partial u (rows 4q + i, column 16c + l16) to LDS, then the fixed-order sum
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up[wave][4 * q + i][16 * c + l16] = ah[c][i] + al[c][i];
+    __syncthreads();
+    for (int i = tid; i < 16 * RP; i += blockDim.x) {
       const int rr = i / RP, c = i % RP;
-      float acc = 0.0f;
-      if (c < r && m0 + rr < M)
-        for (int s = 0; s < S; ++s) acc += u_part[((int64_t)s * M + m0 + rr) * r + c];
-      us[rr][c] = acc;
-      if (blockIdx.y == 0 && c < r && m0 + rr < M) u_out[(int64_t)(m0 + rr) * r + c] = acc;
+      float s = 0.0f;
+      for (int w = 0; w < nw; ++w) s += up[w][rr][c];
+      us[rr][c] = s;
+      if (c < r && m0 + rr < M) u_out[(int64_t)(m0 + rr) * r + c] = s;
     }
     __syncthreads();
 #pragma unroll
@@ -246,22 +258,32 @@ __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, in
       }
   }
 
-  for (int b = blockIdx.y * 4 + wave; b < nblk; b += gridDim.y * 4) {
+  auto phase2 = [&](const XFrag<XT>& xf, int b) {
     const int col0 = b * 128;
-    // w[bb][j]: column col0 + 64*bb + 16*q + j
+    // w[bb][j]: column col0 + 64*bb + 16*q + j times 1/(s sqrt 128); the
+    // scaling is folded into the first butterfly stage (pairs j, j+1)
     float w[2][16];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const int c = col0 + 64 * bb + 16 * q;
-      float cv[16];
-      load16(x + mc * K + c, w[bb]);
-      load16(cvec + c, cv);
+      const float4* cp = reinterpret_cast<const float4*>(cvec + col0 + 64 * bb + 16 * q);
+      float cv[16], xv[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) w[bb][j] *= cv[j];
+      for (int k = 0; k < 4; ++k) {
+        const float4 t = cp[k];
+        cv[4 * k] = t.x; cv[4 * k + 1] = t.y; cv[4 * k + 2] = t.z; cv[4 * k + 3] = t.w;
+      }
+      xf.get(2 * bb, xv);
+      xf.get(2 * bb + 1, xv + 8);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const float t = xv[j + 1] * cv[j + 1];
+        w[bb][j] = __builtin_fmaf(xv[j], cv[j], t);
+        w[bb][j + 1] = __builtin_fmaf(xv[j], cv[j], -t);
+      }
     }
-    // Sylvester butterflies on column bits 0..3 (j) and 6 (bb)
+    // Sylvester butterflies on column bits 1..3 (j) and 6 (bb)
 #pragma unroll
-    for (int hs = 1; hs < 16; hs <<= 1)
+    for (int hs = 2; hs < 16; hs <<= 1)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -288,7 +310,7 @@ __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, in
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        if ((j & 8) == 0) half_swap_butterfly(w[bb][j], w[bb][j + 8]);
+        if ((j & 8) == 0) swap32_butterfly(w[bb][j], w[bb][j + 8]);
     // now w[bb][j] is column 16*t + 4*q + (j & 3) with tile t = (j >> 2) + 4*bb
     f32x4_t acc[8];
 #pragma unroll
@@ -316,108 +338,144 @@ __global__ void __launch_bounds__(256) k_prep_quant(const XT* __restrict__ x, in
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], nuh[kk], acc[t], 0, 0, 0);
       }
     }
-    // NVFP4 per tile: maximum over the tile's 16 columns = 4 lane quarters
-    uint32_t sc[8];
-    float sd[8];
+    // lane quarters against tile bits: afterwards the lane holds tiles 2q and
+    // 2q+1 whole
+    float a[8][4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float mx = fmaxf(fmaxf(fabsf(acc[t][0]), fabsf(acc[t][1])),
-                       fmaxf(fabsf(acc[t][2]), fabsf(acc[t][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      sc[t] = block_scale_code(mx);
-      sd[t] = e4m3_decode(sc[t]);
-    }
-    uint8_t* crow = codes + mc * (K / 2) + col0 / 2;
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      uint32_t g0 = 0, g1 = 0;
+      for (int i = 0; i < 4; ++i) a[t][i] = acc[t][i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        g0 |= e2m1_code(acc[t][i], sd[t]) << (4 * i);
-        g1 |= e2m1_code(acc[t + 1][i], sd[t + 1]) << (4 * i);
-      }
-      // even lane rows: tile t, columns 8*q1 .. +7; odd rows: tile t+1
-      half_swap16(g0, g1);
-      if (mok) {
-        const int tt = t + (q & 1);
-        *reinterpret_cast<uint32_t*>(crow + 8 * tt + 4 * (q >> 1)) = g0 | (g1 << 16);
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) swap32(a[t][i], a[t + 4][i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & 2) == 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) swap16(a[j][i], a[j + 2][i]);
+    uint32_t sc[2];
+    uint2 cw[2];
+#pragma unroll
+    for (int bt = 0; bt < 2; ++bt) {
+      float v[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) v[c] = a[bt + 2 * (c >> 2)][c & 3];
+      cw[bt] = quantize_block(v, sc[bt]);
+      if (pre && mok) {
+        float4* pp = reinterpret_cast<float4*>(pre + mc * K + col0 + 32 * q + 16 * bt);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pp[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
       }
     }
     if (mok) {
-      // lane quarter q stores the scales of tiles 2q and 2q+1
-      const uint32_t pair = (q == 0 ? sc[0] | sc[1] << 8
-                           : q == 1 ? sc[2] | sc[3] << 8
-                           : q == 2 ? sc[4] | sc[5] << 8 : sc[6] | sc[7] << 8);
-      *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) = (uint16_t)pair;
-      if (pre) {
+      *reinterpret_cast<uint4*>(codes + mc * (K / 2) + col0 / 2 + 16 * q) =
+          make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
+      *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) =
+          (uint16_t)(sc[0] | (sc[1] << 8));
+    }
+  };
+
+  if constexpr (NB > 0) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          *reinterpret_cast<float4*>(pre + mc * K + col0 + 16 * t + 4 * q) =
-              make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    for (int i = 0; i < NB; ++i) {
+      const int b = block_of(i);
+      if (b < nblk) {
+        if constexpr (KS == 0) xr[i].load(xrow, b * 128, q);
+        phase2(xr[i], b);
       }
+    }
+  } else {
+    for (int b = wave; b < nblk; b += nw) {
+      xr[0].load(xrow, b * 128, q);
+      phase2(xr[0], b);
     }
   }
 }
 
-// K-slices for the u partial sums: enough workgroups to cover the chip,
-// each slice a whole number of 128-element chunks.
-void u_slicing(int64_t M, int64_t K, int* S, int* kslice) {
-  const int64_t row_tiles = (M + 127) / 128;
-  const int64_t chunks = K / kUChunk;
-  int64_t s = (256 + row_tiles - 1) / row_tiles;
-  s = s < 1 ? 1 : (s > chunks ? chunks : s);
-  const int64_t per = (chunks + s - 1) / s;
-  *kslice = (int)(per * kUChunk);
-  *S = (int)((chunks + per - 1) / per);
+// Launch shape.  r > 0: one workgroup per 16 rows, nw <= 8 waves sharing the
+// row's blocks, nb per wave held in registers (nb = 0: reload in phase 2,
+// when more than 4 per wave would be needed).  r == 0: workgroups of up to 4
+// waves, one block per wave, the grid spanning the blocks too.
+struct PrepShape {
+  int nw, nb;
+  dim3 grid;
+};
+
+PrepShape prep_shape(int64_t M, int64_t K, int32_t r) {
+  const int nblk = (int)(K / 128);
+  const unsigned row_groups = (unsigned)((M + 15) / 16);
+  PrepShape s;
+  if (r == 0) {
+    s.nw = nblk < 4 ? nblk : 4;
+    s.nb = 1;
+    s.grid = dim3(row_groups, (unsigned)((nblk + s.nw - 1) / s.nw));
+    return s;
+  }
+  const int nb = (nblk + 7) / 8;
+  s.nb = nb <= 4 ? nb : 0;
+  s.nw = s.nb > 0 ? (nblk + nb - 1) / nb : 8;
+  s.grid = dim3(row_groups, 1);
+  return s;
+}
+
+template <typename XT, int KS>
+void launch_ks(const PrepShape& s, hipStream_t st, const XT* x, int M, int K, int r,
+               const float* cvec, const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh,
+               const uint16_t* vl, uint8_t* xc, uint8_t* xs, float* u, float* pre) {
+  const dim3 blk(64 * s.nw);
+#define ASP_PREP(NB_)                                                                           \
+  hipLaunchKernelGGL((k_prep<XT, KS, NB_>), s.grid, blk, 0, st, x, M, K, r, cvec, vth, vtl, vh, \
+                     vl, xc, xs, u, pre)
+  if constexpr (KS == 0) {
+    ASP_PREP(1);
+  } else {
+    switch (s.nb) {
+      case 0: ASP_PREP(0); break;
+      case 1: ASP_PREP(1); break;
+      case 2: ASP_PREP(2); break;
+      case 3: ASP_PREP(3); break;
+      default: ASP_PREP(4); break;
+    }
+  }
+#undef ASP_PREP
 }
 
 template <typename XT>
 int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t* pack,
-                    uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant, float* u_part,
+                    uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant,
                     hipStream_t stream) {
-  PrepPackLayout L = prep_pack_layout(K, r);
+  const PrepPackLayout L = prep_pack_layout(K, r);
   const float* cvec = reinterpret_cast<const float*>(pack + L.cvec);
   const uint16_t* vth = reinterpret_cast<const uint16_t*>(pack + L.vt_hi);
   const uint16_t* vtl = reinterpret_cast<const uint16_t*>(pack + L.vt_lo);
   const uint16_t* vh = reinterpret_cast<const uint16_t*>(pack + L.v_hi);
   const uint16_t* vl = reinterpret_cast<const uint16_t*>(pack + L.v_lo);
-  int S = 0, kslice = 0;
-  if (r > 0) {
-    u_slicing(M, K, &S, &kslice);
-    const dim3 ga((unsigned)((M + 127) / 128), (unsigned)S);
-    if (L.rp32 == 32)
-      hipLaunchKernelGGL((k_prep_u<XT, 1>), ga, dim3(256), 0, stream, x, (int)M, (int)K, (int)r, vth, vtl, u_part, kslice);
-    else
-      hipLaunchKernelGGL((k_prep_u<XT, 2>), ga, dim3(256), 0, stream, x, (int)M, (int)K, (int)r, vth, vtl, u_part, kslice);
-    ASP_TRY(launch_status("prep_u"));
-  }
-  const int64_t nblk = K / 128;
-  const dim3 gb((unsigned)((M + 15) / 16), (unsigned)((nblk + 3) / 4));
-#define ASP_PREP_QUANT(KS_)                                                                     \
-  hipLaunchKernelGGL((k_prep_quant<XT, KS_>), gb, dim3(256), 0, stream, x, (int)M, (int)K, (int)r, \
-                     cvec, vh, vl, u_part, S, x_codes, x_scales, u, prequant)
+  const PrepShape s = prep_shape(M, K, r);
+  const int Mi = (int)M, Ki = (int)K;
   switch (L.rp32 / 32) {
-    case 0: ASP_PREP_QUANT(0); break;
-    case 1: ASP_PREP_QUANT(1); break;
-    default: ASP_PREP_QUANT(2); break;
+    case 0:
+      launch_ks<XT, 0>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
+                       prequant);
+      break;
+    case 1:
+      launch_ks<XT, 1>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
+                       prequant);
+      break;
+    default:
+      launch_ks<XT, 2>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
+                       prequant);
+      break;
   }
-#undef ASP_PREP_QUANT
-  return launch_status("prep_quant");
+  return launch_status("prep");
 }
 
 }  // namespace
 
-size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r) {
-  if (r == 0 || M == 0) return 0;
-  int S, kslice;
-  u_slicing(M, K, &S, &kslice);
-  return (size_t)S * (size_t)M * (size_t)r * sizeof(float);
-}
-
 int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                       const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream) {
+                      float* prequant, hipStream_t stream) {
   ASP_TRY(check_mk(M, K));
   ASP_TRY(check_rank(r));
   if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
@@ -428,18 +486,11 @@ int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int3
   ASP_TRY(check_ptr(x_scales, "x_scales", true));
   ASP_TRY(check_ptr(u, "u", r > 0));
   ASP_TRY(check_ptr(prequant, "prequant", false));
-  const size_t need = act_prep_scratch_bytes(M, K, r);
-  if (need) {
-    ASP_TRY(check_ptr(scratch, "workspace", true));
-    if (scratch_bytes < need)
-      return fail(ASP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", scratch_bytes, need);
-  }
-  float* u_part = static_cast<float*>(scratch);
   if (x_dtype == ASP_F32)
     return launch_prep(static_cast<const float*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                       prequant, u_part, stream);
+                       prequant, stream);
   return launch_prep(static_cast<const uint16_t*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                     prequant, u_part, stream);
+                     prequant, stream);
 }
 
 }  // namespace asp
@@ -448,21 +499,12 @@ using namespace asp;
 
 extern "C" {
 
-int32_t asp_act_prep_workspace_bytes(int64_t M, int64_t K, int32_t r, size_t* bytes) {
-  clear_error();
-  ASP_TRY(check_mk(M, K));
-  ASP_TRY(check_rank(r));
-  if (!bytes) return fail(ASP_ERR_ARG, "null output pointer");
-  *bytes = act_prep_scratch_bytes(M, K, r);
-  return ASP_OK;
-}
-
 int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                     float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
+                     float* prequant, void* stream) {
   clear_error();
-  return act_prep_impl(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+  return act_prep_impl(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant,
+                       (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -6,25 +6,22 @@
 namespace asp {
 namespace {
 
-// One lane per 8 consecutive elements; lane pairs form a 16-block.
-__global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ in, int64_t n_half,
-                                                  uint32_t* __restrict__ codes,
+// One lane per 16-element block.
+__global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ in, int64_t n_blk,
+                                                  uint2* __restrict__ codes,
                                                   uint8_t* __restrict__ scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool ok = i < n_half;
-  float v[8];
-  if (ok) {
-    load8(in + 8 * i, v);
-  } else {
+  if (i >= n_blk) return;
+  const float4* p = reinterpret_cast<const float4*>(in) + 4 * i;
+  float v[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  for (int k = 0; k < 4; ++k) {
+    const float4 a = p[k];
+    v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
   }
   uint32_t sc;
-  const uint32_t word = quantize8_pair(v, sc);
-  if (ok) {
-    codes[i] = word;
-    if ((i & 1) == 0) scales[i >> 1] = (uint8_t)sc;
-  }
+  codes[i] = quantize_block(v, sc);
+  scales[i] = (uint8_t)sc;
 }
 
 __global__ void __launch_bounds__(256) k_dequantize(const uint32_t* __restrict__ codes,
@@ -65,9 +62,9 @@ int32_t asp_quantize_nvfp4(const float* in, int64_t rows, int64_t cols, uint8_t*
   ASP_TRY(check_ptr(in, "in", true));
   ASP_TRY(check_ptr(codes, "codes", true));
   ASP_TRY(check_ptr(scales, "scales", true));
-  const int64_t n_half = rows * cols / 8;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n_half + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, in, n_half, reinterpret_cast<uint32_t*>(codes), scales);
+  const int64_t n_blk = rows * cols / 16;
+  hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n_blk + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, in, n_blk, reinterpret_cast<uint2*>(codes), scales);
   return launch_status("quantize");
 }
 
