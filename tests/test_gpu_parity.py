@@ -128,7 +128,10 @@ def prep_cases():
     r0 = synth.make_layer("r0", 77, 384, 64, 0, seed=3, dtype="bf16")
     r16 = synth.make_layer("r16", 5, 256, 32, 16, seed=4, dtype="f32")
     r64 = synth.make_layer("r64", 33, 1024, 32, 64, seed=6, dtype="bf16")
-    return [c0, c1, c2, r0, r16, r64]
+    # more blocks per wave than stay in registers: x is loaded again in phase 2
+    r64k = synth.make_layer("r64-reload", 20, 2048, 32, 64, seed=10, dtype="bf16")
+    f32k = synth.make_layer("f32-reload", 9, 3072, 32, 32, seed=11, dtype="f32")
+    return [c0, c1, c2, r0, r16, r64, r64k, f32k]
 
 
 @pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
@@ -188,7 +191,8 @@ def test_gemm_on_oracle_codes(lay):
     assert rel_fro(got16, want) <= 2e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (1024, 6144, 512)], ids=["small-tiles", "large-tiles"])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (1024, 1024, 256), (1024, 6144, 512)],
+                         ids=["split-k", "64x64-tiles", "256x192-tiles"])
 def test_gemm_every_scale_code(M, N, K):
     """Random codes under every finite E4M3 scale code (subnormal to 448) on
     both operands: the device's scale decoding and contraction against the

@@ -324,6 +324,205 @@ int32_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const float* u, int64_
   return launch_status("gemm");
 }
 
+// ---------------------------------------------------------------------------
+// k_gemm_sk: the path for few output tiles (small M).  A workgroup owns a
+// (32*FM) x (32*FN) tile of y; its W waves split K into W equal ranges, and
+// each wave computes the whole tile over its range, streaming its operand rows
+// straight from memory into registers (16-byte loads, two chunks in flight, no
+// LDS staging and no barrier in the K loop).  The W partial tiles then meet in
+// LDS and are added in a fixed order (deterministic), and each thread stores
+// a run of consecutive columns with one vector store.
+//
+// K-slot mapping.  Per group of 64 K elements (32 code bytes), lane half h
+// loads the 16 bytes holding elements 32h .. 32h+31 of the group (two NVFP4
+// blocks); K-step t = 0..3 of the group feeds its k-slots 8h .. 8h+7 with
+// elements 32h + 8t .. 32h + 8t + 7, which lie in block 2h + (t >> 1).  A and B
+// use the same mapping, so every product pairs equal K indices, and a lane's 8
+// values of a K-step share one block scale.
+template <int FM, int FN, int W>
+__global__ void __launch_bounds__(W * 64)
+    k_gemm_sk(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
+              const float* __restrict__ u, int M, int N, int K, int r,
+              const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+              const uint16_t* __restrict__ wv, const float* __restrict__ bias,
+              void* __restrict__ y, int y_bf16, int tiles_n) {
+  constexpr int BM = 32 * FM, BN = 32 * FN, NF = FM + FN;
+  constexpr int CH = 4;                      // groups of 64 K per register chunk
+  constexpr int EPT = BM * BN / (W * 64);    // output elements per thread
+  __shared__ float part[W][BM][BN + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t KB = K / 2, KS = K / 16;
+  const int ng = K / 64 / W;                 // groups of this wave
+  const int gbeg = wave * ng, gend = gbeg + ng;
+
+  const uint8_t* crow[NF];
+  const uint8_t* srow[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int64_t row = f < FM ? min(m0 + 32 * f + l32, M - 1) : min(n0 + 32 * (f - FM) + l32, N - 1);
+    crow[f] = (f < FM ? xc : wc) + row * KB + 16 * half;
+    srow[f] = (f < FM ? xs : ws) + row * KS;
+  }
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  uint4 cw[2][CH][NF];
+  uint32_t sw[2][CH][NF];
+  auto load = [&](int buf, int g0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (g0 + c < gend)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          cw[buf][c][f] = *reinterpret_cast<const uint4*>(crow[f] + 32 * (int64_t)(g0 + c));
+          sw[buf][c][f] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * (int64_t)(g0 + c));
+        }
+  };
+  auto compute = [&](int buf, int g0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (g0 + c >= gend) break;
+      half2_t sp[NF];  // this lane's two block scales of the group, as fp16
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        sp[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[buf][c][f] >> (16 * half), 1.0f, false);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        half8_t fr[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint4 q = cw[buf][c][f];
+          const uint32_t wd = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+          fr[f] = decode8(wd, sp[f][t >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[i], fr[FM + j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  load(0, gbeg);
+  for (int g0 = gbeg; g0 < gend; g0 += 2 * CH) {
+    if (g0 + CH < gend) load(1, g0 + CH);
+    compute(0, g0);
+    if (g0 + CH >= gend) break;
+    if (g0 + 2 * CH < gend) load(0, g0 + 2 * CH);
+    compute(1, g0 + CH);
+  }
+
+  // low-rank branch bf16(u) wv^T, in the first wave's partial
+  if (wave == 0) {
+    for (int c0 = 0; c0 < r; c0 += 16) {
+      const int cb = c0 + half * 8;
+      bf16x8_t la[FM], lb[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = min(m0 + 32 * i + l32, M - 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          la[i][e] = bf16_from_bits(f32_to_bf16_rne(cb + e < r ? u[m * r + cb + e] : 0.0f));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = min(n0 + 32 * j + l32, N - 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lb[j][e] = bf16_from_bits(cb + e < r ? wv[n * r + cb + e] : (uint16_t)0);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // partial tiles to LDS (accumulator element v of lane l: row 8*(v/4) +
+  // 4*(l/32) + v%4, column l%32), then the fixed-order sum, bias and store
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        part[wave][32 * i + 8 * (v >> 2) + 4 * half + (v & 3)][32 * j + l32] = acc[i][j][v];
+  __syncthreads();
+  const int e0 = tid * EPT, row = e0 / BN, col = e0 % BN;
+  const int gm = m0 + row, gn = n0 + col;
+  if (gm >= M) return;
+  float out[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) s += part[w][row][col + e];
+    out[e] = s + ((bias && gn + e < N) ? bias[gn + e] : 0.0f);
+  }
+  const int64_t base = (int64_t)gm * N + gn;
+  if (y_bf16) {
+    uint16_t* yo = reinterpret_cast<uint16_t*>(y) + base;
+    if (gn + EPT <= N && (base & 7) == 0 && EPT % 8 == 0) {
+#pragma unroll
+      for (int e = 0; e < EPT; e += 8) {
+        uint4 pk;
+        pk.x = f32_to_bf16_rne(out[e]) | ((uint32_t)f32_to_bf16_rne(out[e + 1]) << 16);
+        pk.y = f32_to_bf16_rne(out[e + 2]) | ((uint32_t)f32_to_bf16_rne(out[e + 3]) << 16);
+        pk.z = f32_to_bf16_rne(out[e + 4]) | ((uint32_t)f32_to_bf16_rne(out[e + 5]) << 16);
+        pk.w = f32_to_bf16_rne(out[e + 6]) | ((uint32_t)f32_to_bf16_rne(out[e + 7]) << 16);
+        *reinterpret_cast<uint4*>(yo + e) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (gn + e < N) yo[e] = f32_to_bf16_rne(out[e]);
+    }
+  } else {
+    float* yo = reinterpret_cast<float*>(y) + base;
+    if (gn + EPT <= N && (base & 3) == 0 && EPT % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4)
+        *reinterpret_cast<float4*>(yo + e) = make_float4(out[e], out[e + 1], out[e + 2], out[e + 3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+        if (gn + e < N) yo[e] = out[e];
+    }
+  }
+}
+
+// Waves per workgroup for k_gemm_sk: K split into W ranges of at least 256
+// elements (at most 8 ranges), each a whole number of 64-element groups.
+int sk_waves(int64_t K) {
+  const int64_t groups = K / 64;
+  for (int w : {8, 4, 2})
+    if (K / w >= 256 && groups % w == 0) return w;
+  return 1;
+}
+
+template <int FM, int FN, int W>
+int32_t launch_gemm_sk(const uint8_t* xc, const uint8_t* xs, const float* u, int64_t M, int64_t N,
+                       int64_t K, int32_t r, const uint8_t* wc, const uint8_t* wsc,
+                       const uint16_t* wv, const float* bias, void* y, int32_t y_dtype,
+                       hipStream_t stream) {
+  const int64_t tiles_m = (M + 32 * FM - 1) / (32 * FM), tiles_n = (N + 32 * FN - 1) / (32 * FN);
+  if (tiles_m * tiles_n > INT32_MAX)
+    return fail(ASP_ERR_SHAPE, "M=%lld N=%lld too large for one launch", (long long)M, (long long)N);
+  hipLaunchKernelGGL((k_gemm_sk<FM, FN, W>), dim3((unsigned)(tiles_m * tiles_n)), dim3(W * 64), 0,
+                     stream, xc, xs, u, (int)M, (int)N, (int)K, (int)r, wc, wsc, wv, bias, y,
+                     (int)(y_dtype == ASP_BF16), (int)tiles_n);
+  return launch_status("gemm_sk");
+}
+
 }  // namespace
 
 int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype) {
@@ -351,14 +550,33 @@ int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* 
   // Tile choice.  Large layers: 256 x 192 workgroup tiles (256 tiles, one per
   // CU, for a 4096 x 3072 output) of 8 waves with 64 x 96 per-wave tiles: five
   // fragment decodes feed six MFMAs per K-step, and two waves per SIMD overlap
-  // one wave's decode with the other's MFMAs.  Small layers: 64 x 64 tiles of
-  // 4 waves, for as many workgroups as the output allows.
+  // one wave's decode with the other's MFMAs.  Mid-size layers with at least
+  // 256 tiles of 64 x 64: those tiles, 4 waves each.  Fewer tiles (small M):
+  // 32 x 32 tiles with K split over the workgroup's waves (k_gemm_sk), so that
+  // more waves share the work and each one's chain of dependent K-steps is
+  // shorter.
   const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
   if (t192 >= 128)
     return launch_gemm<4, 2, 2, 3>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
                                    y, y_dtype, stream);
-  return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y,
-                                 y_dtype, stream);
+  const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+  if (t64 >= 256)
+    return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
+                                   y, y_dtype, stream);
+  switch (sk_waves(K)) {
+    case 8:
+      return launch_gemm_sk<1, 1, 8>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+    case 4:
+      return launch_gemm_sk<1, 1, 4>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+    case 2:
+      return launch_gemm_sk<1, 1, 2>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+    default:
+      return launch_gemm_sk<1, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+  }
 }
 
 }  // namespace asp

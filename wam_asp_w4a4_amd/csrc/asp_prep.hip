@@ -174,6 +174,40 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
     return KS > 0 ? wave + i * nw : ((int)blockIdx.y * NH + i) * nw + wave;
   };
 
+  // Operands of phase 2 for one block: the V rows of its 8 tiles (hi, lo) for
+  // the deflation and its 128 values of 1/(s sqrt 128), all issued together
+  struct P2 {
+    uint4 vh[KS > 0 ? KS : 1][8], vl[KS > 0 ? KS : 1][8];
+    float4 cv[2][4];
+  };
+  auto load_p2 = [&](P2& o, int b) {
+    const int col0 = b * 128;
+    if constexpr (KS > 0) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int64_t vrow = (int64_t)(col0 + 16 * t + l16) * RP + 32 * kk + 8 * q;
+          o.vh[kk][t] = *reinterpret_cast<const uint4*>(vh + vrow);
+          o.vl[kk][t] = *reinterpret_cast<const uint4*>(vl + vrow);
+        }
+    }
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o.cv[bb][k] = reinterpret_cast<const float4*>(cvec + col0 + 64 * bb + 16 * q)[k];
+  };
+
+  // With one block per wave (and bf16 x, for registers) its phase-2 operands
+  // are issued during phase 1, right after phase 1's own loads, so their
+  // memory latency overlaps phase 1 instead of following it.
+  constexpr bool kHoist = NB == 1 && !fp32_x;
+  P2 p2first;
+  if constexpr (kHoist && KS == 0) {
+    if (block_of(0) < nblk) load_p2(p2first, block_of(0));
+  }
+
   // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
   // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
   bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
@@ -185,10 +219,24 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) ah[c][i] = al[c][i] = 0.0f;
 
-    auto contract = [&](const XFrag<XT>& xf, int col0) {
+    // B fragments (rows of V''^T, hi and lo) of one block: all issued at once,
+    // so a block costs one memory round trip rather than one per MFMA
+    struct VFrag {
+      uint4 h[4][CT], l[4][CT];
+    };
+    auto load_v = [&](VFrag& vf, int col0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          const int64_t off = (int64_t)(c * 16 + l16) * K + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1);
+          vf.h[g][c] = *reinterpret_cast<const uint4*>(vth + off);
+          vf.l[g][c] = *reinterpret_cast<const uint4*>(vtl + off);
+        }
+    };
+    auto contract = [&](const XFrag<XT>& xf, const VFrag& vf) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int koff = col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1);
         bf16x8_t a_hi, a_lo;
         if constexpr (!fp32_x) {
           a_hi = as_bf16x8(xf.f[g]);
@@ -205,9 +253,8 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
         }
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-          const int64_t off = (int64_t)(c * 16 + l16) * K + koff;
-          const bf16x8_t b_hi = as_bf16x8(*reinterpret_cast<const uint4*>(vth + off));
-          const bf16x8_t b_lo = as_bf16x8(*reinterpret_cast<const uint4*>(vtl + off));
+          const bf16x8_t b_hi = as_bf16x8(vf.h[g][c]);
+          const bf16x8_t b_lo = as_bf16x8(vf.l[g][c]);
           ah[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, ah[c], 0, 0, 0);
           al[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, al[c], 0, 0, 0);
           if constexpr (fp32_x)
@@ -217,20 +264,30 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
     };
 
     if constexpr (NB > 0) {
+      // x of every block, then the V'' fragments double-buffered: block i+1's
+      // loads are in flight while block i's MFMAs run
+      VFrag vf[2];
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int b = block_of(i);
         if (b < nblk) xr[i].load(xrow, b * 128, q);
       }
+      if (block_of(0) < nblk) load_v(vf[0], block_of(0) * 128);
+      if constexpr (kHoist) {  // after phase 1's own loads, so they are served first
+        if (block_of(0) < nblk) load_p2(p2first, block_of(0));
+      }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int b = block_of(i);
-        if (b < nblk) contract(xr[i], b * 128);
+        if (i + 1 < NB && block_of(i + 1) < nblk) load_v(vf[(i + 1) & 1], block_of(i + 1) * 128);
+        if (b < nblk) contract(xr[i], vf[i & 1]);
       }
     } else {
+      VFrag vf;
       for (int b = wave; b < nblk; b += nw) {
         xr[0].load(xrow, b * 128, q);
-        contract(xr[0], b * 128);
+        load_v(vf, b * 128);
+        contract(xr[0], vf);
       }
     }
     // partial u (rows 4q + i, column 16c + l16) to LDS, then the fixed-order sum
@@ -258,18 +315,17 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
       }
   }
 
-  auto phase2 = [&](const XFrag<XT>& xf, int b) {
+  auto phase2 = [&](const XFrag<XT>& xf, const P2& p2, int b) {
     const int col0 = b * 128;
     // w[bb][j]: column col0 + 64*bb + 16*q + j times 1/(s sqrt 128); the
     // scaling is folded into the first butterfly stage (pairs j, j+1)
     float w[2][16];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const float4* cp = reinterpret_cast<const float4*>(cvec + col0 + 64 * bb + 16 * q);
       float cv[16], xv[16];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float4 t = cp[k];
+        const float4 t = p2.cv[bb][k];
         cv[4 * k] = t.x; cv[4 * k + 1] = t.y; cv[4 * k + 2] = t.z; cv[4 * k + 3] = t.w;
       }
       xf.get(2 * bb, xv);
@@ -323,9 +379,8 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
         bf16x8_t a_hi[8], a_lo[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int64_t vrow = (int64_t)(col0 + 16 * t + l16) * RP + 32 * kk + 8 * q;
-          a_hi[t] = as_bf16x8(*reinterpret_cast<const uint4*>(vh + vrow));
-          a_lo[t] = as_bf16x8(*reinterpret_cast<const uint4*>(vl + vrow));
+          a_hi[t] = as_bf16x8(p2.vh[kk][t]);
+          a_lo[t] = as_bf16x8(p2.vl[kk][t]);
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -383,27 +438,44 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
       const int b = block_of(i);
       if (b < nblk) {
         if constexpr (KS == 0) xr[i].load(xrow, b * 128, q);
-        phase2(xr[i], b);
+        if constexpr (kHoist) {
+          phase2(xr[i], p2first, b);
+        } else {
+          P2 p2;
+          load_p2(p2, b);
+          phase2(xr[i], p2, b);
+        }
       }
     }
   } else {
     for (int b = wave; b < nblk; b += nw) {
       xr[0].load(xrow, b * 128, q);
-      phase2(xr[0], b);
+      P2 p2;
+      load_p2(p2, b);
+      phase2(xr[0], p2, b);
     }
   }
 }
 
+// Most blocks per wave whose raw x stays in registers between the phases
+// without spilling (checked on the compiled kernels): more for bf16 x and
+// rank <= 32, fewer for fp32 x (twice the bytes) and rank 64 (twice the V
+// fragments).
+template <typename XT, int KS>
+constexpr int max_nb() {
+  return KS >= 2 ? 1 : (sizeof(XT) == 4 ? 2 : 4);
+}
+
 // Launch shape.  r > 0: one workgroup per 16 rows, nw <= 8 waves sharing the
-// row's blocks, nb per wave held in registers (nb = 0: reload in phase 2,
-// when more than 4 per wave would be needed).  r == 0: workgroups of up to 4
-// waves, one block per wave, the grid spanning the blocks too.
+// row's blocks, nb per wave held in registers (nb = 0: x reloaded in phase 2,
+// when more than max_nb per wave would be needed).  r == 0: workgroups of up
+// to 4 waves, one block per wave, the grid spanning the blocks too.
 struct PrepShape {
   int nw, nb;
   dim3 grid;
 };
 
-PrepShape prep_shape(int64_t M, int64_t K, int32_t r) {
+PrepShape prep_shape(int64_t M, int64_t K, int32_t r, int maxnb) {
   const int nblk = (int)(K / 128);
   const unsigned row_groups = (unsigned)((M + 15) / 16);
   PrepShape s;
@@ -414,16 +486,18 @@ PrepShape prep_shape(int64_t M, int64_t K, int32_t r) {
     return s;
   }
   const int nb = (nblk + 7) / 8;
-  s.nb = nb <= 4 ? nb : 0;
+  s.nb = nb <= maxnb ? nb : 0;
   s.nw = s.nb > 0 ? (nblk + nb - 1) / nb : 8;
   s.grid = dim3(row_groups, 1);
   return s;
 }
 
 template <typename XT, int KS>
-void launch_ks(const PrepShape& s, hipStream_t st, const XT* x, int M, int K, int r,
-               const float* cvec, const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh,
-               const uint16_t* vl, uint8_t* xc, uint8_t* xs, float* u, float* pre) {
+void launch_ks(hipStream_t st, const XT* x, int M, int K, int r, const float* cvec,
+               const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh, const uint16_t* vl,
+               uint8_t* xc, uint8_t* xs, float* u, float* pre) {
+  constexpr int MAXNB = max_nb<XT, KS>();
+  const PrepShape s = prep_shape(M, K, r, MAXNB);
   const dim3 blk(64 * s.nw);
 #define ASP_PREP(NB_)                                                                           \
   hipLaunchKernelGGL((k_prep<XT, KS, NB_>), s.grid, blk, 0, st, x, M, K, r, cvec, vth, vtl, vh, \
@@ -434,9 +508,9 @@ void launch_ks(const PrepShape& s, hipStream_t st, const XT* x, int M, int K, in
     switch (s.nb) {
       case 0: ASP_PREP(0); break;
       case 1: ASP_PREP(1); break;
-      case 2: ASP_PREP(2); break;
-      case 3: ASP_PREP(3); break;
-      default: ASP_PREP(4); break;
+      case 2: if constexpr (MAXNB >= 2) ASP_PREP(2); break;
+      case 3: if constexpr (MAXNB >= 3) ASP_PREP(3); break;
+      default: if constexpr (MAXNB >= 4) ASP_PREP(4); break;
     }
   }
 #undef ASP_PREP
@@ -452,20 +526,16 @@ int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t*
   const uint16_t* vtl = reinterpret_cast<const uint16_t*>(pack + L.vt_lo);
   const uint16_t* vh = reinterpret_cast<const uint16_t*>(pack + L.v_hi);
   const uint16_t* vl = reinterpret_cast<const uint16_t*>(pack + L.v_lo);
-  const PrepShape s = prep_shape(M, K, r);
   const int Mi = (int)M, Ki = (int)K;
   switch (L.rp32 / 32) {
     case 0:
-      launch_ks<XT, 0>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
-                       prequant);
+      launch_ks<XT, 0>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
       break;
     case 1:
-      launch_ks<XT, 1>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
-                       prequant);
+      launch_ks<XT, 1>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
       break;
     default:
-      launch_ks<XT, 2>(s, stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u,
-                       prequant);
+      launch_ks<XT, 2>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
       break;
   }
   return launch_status("prep");
