@@ -230,12 +230,14 @@ def main():
             xs = ws[off: off + M * K // 16]
             off2 = off + up(M * K // 16)
             u = ws[off2: off2 + 4 * M * r].view(torch.float32) if r else None
-            launches.append((lay, p, x, y, xc, xs, u))
+            scratch = ws[off2 + up(4 * M * r):]
+            launches.append((lay, p, x, y, xc, xs, u, scratch))
 
-    def prep_launch(lay, p, x, y, xc, xs, u):
-        B.asp_act_prep(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None)
+    def prep_launch(lay, p, x, y, xc, xs, u, scratch):
+        B.asp_act_prep(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None,
+                       scratch, scratch.numel())
 
-    def gemm_launch(lay, p, x, y, xc, xs, u):
+    def gemm_launch(lay, p, x, y, xc, xs, u, scratch):
         B.asp_gemm_lowrank(xc, xs, u, lay.M, lay.N, lay.K, lay.r, p.w_codes, p.w_scales, p.wv,
                            p.bias, y, B.DTYPES[y_dtype])
 

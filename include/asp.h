@@ -159,8 +159,12 @@ int32_t asp_dequantize_nvfp4(const uint8_t* codes, const uint8_t* scales,
                              int64_t rows, int64_t cols, float* out,
                              void* stream);
 
+/* Workspace bytes asp_act_prep needs (partial sums of u; 0 when r == 0). */
+int32_t asp_act_prep_workspace_bytes(int64_t M, int64_t K, int32_t r,
+                                     size_t* bytes);
+
 /*
- * Fused activation prep (every call): smooth-divide x/s, block Hadamard,
+ * Activation prep (every call): smooth-divide x/s, block Hadamard,
  * u = x_tilde V, deflation x_tilde - u V^T, NVFP4 quantise and pack
  * (model card, "What ASP is, and what the deflated form means").
  *   x          device, M x K, element type x_dtype (ASP_F32 or ASP_BF16)
@@ -169,13 +173,16 @@ int32_t asp_dequantize_nvfp4(const uint8_t* codes, const uint8_t* scales,
  *   u          device out, M x r float32 (NULL allowed iff r == 0)
  *   prequant   device out, M x K float32 deflated activation before
  *              quantisation, or NULL (a check hook; costs bandwidth)
- * Needs no scratch memory.  Deterministic: the same inputs give the same
- * bits on every call.
+ *   workspace  device scratch of asp_act_prep_workspace_bytes bytes for the
+ *              partial sums of u (NULL allowed when that is 0, i.e. r == 0);
+ *              16-byte aligned; contents undefined afterwards
+ * Deterministic: the same inputs give the same bits on every call, and a
+ * row's results do not depend on the other rows of the batch.
  */
 int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                      int32_t r, const uint8_t* prep_pack, uint8_t* x_codes,
                      uint8_t* x_scales, float* u, float* prequant,
-                     void* stream);
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * 4-bit GEMM with fused low-rank and bias epilogue:
@@ -199,7 +206,7 @@ int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales,
                          const float* bias, void* y, int32_t y_dtype,
                          void* stream);
 
-/* Workspace bytes asp_forward needs (activation codes, scales and u). */
+/* Workspace bytes asp_forward needs (activation codes, scales, u, prep scratch). */
 int32_t asp_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,
                             size_t* bytes);
 

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == B.ABI_VERSION == 3
+    assert B.asp_abi_version() == B.ABI_VERSION == 4
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
@@ -48,7 +48,8 @@ def test_sizes_are_four_and_a_half_bits_per_weight():
     c, s, w = B.asp_packed_sizes(4096, 3072, 32)
     assert c * 8 == 4 * 4096 * 3072 and s * 8 == 4096 * 3072 // 2 and w == 4096 * 32 * 2
     ws = B.asp_workspace_bytes(256, 1024, 1024, 32)
-    assert ws == 256 * 512 + 256 * 64 + 256 * 32 * 4  # codes, scales, u (256-byte aligned sections)
+    # codes, scales, u, then the prep's partial sums of u (256-byte aligned sections)
+    assert ws == 256 * 512 + 256 * 64 + 256 * 32 * 4 + B.asp_act_prep_workspace_bytes(256, 1024, 32)
 
 
 @pytest.mark.parametrize("K", [0, 100, 64, -128])
@@ -83,10 +84,11 @@ MIS = FAKE + 8
 
 def _act_prep(**over):
     a = dict(x=FAKE, x_dtype=1, M=4, K=128, r=16, pack=FAKE, x_codes=FAKE, x_scales=FAKE,
-             u=FAKE, prequant=None)
+             u=FAKE, prequant=None, ws=FAKE, ws_bytes=1 << 20)
     a.update(over)
     st = B.lib().asp_act_prep(a["x"], a["x_dtype"], a["M"], a["K"], a["r"], a["pack"],
-                              a["x_codes"], a["x_scales"], a["u"], a["prequant"], None)
+                              a["x_codes"], a["x_scales"], a["u"], a["prequant"], a["ws"],
+                              a["ws_bytes"], None)
     return st, B.asp_last_error()
 
 
@@ -99,6 +101,10 @@ def test_act_prep_pointer_validation():
     st, msg = _act_prep(x_codes=None)
     assert st == 1 and "x_codes is NULL" in msg
     assert _act_prep(M=0, x=None)[0] == 0     # empty batch: nothing to do, nothing checked
+    assert _act_prep(ws=None)[0] == 1          # r > 0 needs scratch for the partial sums of u
+    need = B.asp_act_prep_workspace_bytes(4, 128, 16)
+    assert need > 0 and B.asp_act_prep_workspace_bytes(4, 128, 0) == 0
+    assert _act_prep(ws_bytes=need - 1)[0] == 5
 
 
 def test_forward_workspace_and_alignment_checks():

@@ -117,7 +117,10 @@ def gpu_act_prep(lay):
     pre = torch.empty((M, K), dtype=torch.float32, device=DEV)
     pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
     B.asp_pack_prep(K, r, lay.s, lay.v, pack)
-    B.asp_act_prep(x_device(lay), B.DTYPES[lay.x_dtype], M, K, r, dev(pack), xc, xs, u, pre)
+    nws = B.asp_act_prep_workspace_bytes(M, K, r)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=DEV)
+    B.asp_act_prep(x_device(lay), B.DTYPES[lay.x_dtype], M, K, r, dev(pack), xc, xs, u, pre,
+                   ws, nws)
     return host(xc), host(xs), (host(u) if r else None), host(pre)
 
 

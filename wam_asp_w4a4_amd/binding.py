@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
 
 ASP_F32 = 0
@@ -38,7 +38,8 @@ SIGNATURES = {
     "asp_pack_prep": (_i32, [_i64, _i32, _p, _p, _p]),
     "asp_quantize_nvfp4": (_i32, [_p, _i64, _i64, _p, _p, _p]),
     "asp_dequantize_nvfp4": (_i32, [_p, _p, _i64, _i64, _p, _p]),
-    "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p]),
+    "asp_act_prep_workspace_bytes": (_i32, [_i64, _i64, _i32, _psz]),
+    "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "asp_gemm_lowrank": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
     "asp_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
     "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32,
@@ -159,10 +160,17 @@ def asp_dequantize_nvfp4(codes, scales, rows, cols, out, stream=None):
                                       _stream(stream, out)))
 
 
+def asp_act_prep_workspace_bytes(M: int, K: int, r: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().asp_act_prep_workspace_bytes(M, K, r, ctypes.byref(b)))
+    return b.value
+
+
 def asp_act_prep(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant=None,
-                 stream=None):
+                 workspace=None, workspace_bytes=0, stream=None):
     _check(lib().asp_act_prep(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(x_codes),
-                              _ptr(x_scales), _ptr(u), _ptr(prequant), _stream(stream, x)))
+                              _ptr(x_scales), _ptr(u), _ptr(prequant), _ptr(workspace),
+                              workspace_bytes, _stream(stream, x)))
 
 
 def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,

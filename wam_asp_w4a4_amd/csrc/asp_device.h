@@ -18,6 +18,9 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector: unlike HIP's uint4 (a struct of unions), it
+// stays in registers when carried around a loop
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1/sqrt(128), rounded to float32
 
@@ -115,9 +118,10 @@ inline int32_t check_mk(int64_t M, int64_t K) {
 }
 
 // Internal launchers (validate, then enqueue on `stream`).
+size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r);
 int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                       const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, hipStream_t stream);
+                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream);
 int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype);
 int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
                   int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,

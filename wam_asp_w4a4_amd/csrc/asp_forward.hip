@@ -1,13 +1,14 @@
 // The whole deflated-ASP NVFP4 layer: activation prep then the 4-bit GEMM
 // with its low-rank/bias epilogue, enqueued on one stream, with the
-// activation codes, scales and u in the caller's workspace.
+// activation codes, scales, u and the prep's partial sums of u in the caller's
+// workspace.
 #include "asp_device.h"
 
 namespace asp {
 namespace {
 
 struct WsLayout {
-  size_t codes, scales, u, total;
+  size_t codes, scales, u, scratch, total;
 };
 
 WsLayout ws_layout(int64_t M, int64_t K, int32_t r) {
@@ -16,7 +17,8 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t r) {
   L.codes = 0;
   L.scales = up((size_t)M * K / 2);
   L.u = L.scales + up((size_t)M * K / 16);
-  L.total = L.u + up((size_t)M * r * 4);
+  L.scratch = L.u + up((size_t)M * r * 4);
+  L.total = L.scratch + up(act_prep_scratch_bytes(M, K, r));
   return L;
 }
 
@@ -61,8 +63,8 @@ int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N, int64_
   uint8_t* xc = base + L.codes;
   uint8_t* xs = base + L.scales;
   float* u = r > 0 ? reinterpret_cast<float*>(base + L.u) : nullptr;
-  ASP_TRY(act_prep_impl(x, x_dtype, M, K, r, prep_pack, xc, xs, u, nullptr,
-                        (hipStream_t)stream));
+  ASP_TRY(act_prep_impl(x, x_dtype, M, K, r, prep_pack, xc, xs, u, nullptr, base + L.scratch,
+                        L.total - L.scratch, (hipStream_t)stream));
   return gemm_impl(xc, xs, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
                    (hipStream_t)stream);
 }

@@ -1,27 +1,31 @@
-// Fused activation prep on gfx950: x/s, block Hadamard, u = x_tilde V,
-// deflation x_tilde - u V^T, NVFP4 quantise + pack (model card "FastWAM UR3
-// 3-task -- 4-bit quantisations", section "What ASP is, and what the deflated
-// form means").  One kernel, k_prep; a workgroup owns 16 rows of x.
+// Activation prep on gfx950: x/s, block Hadamard, u = x_tilde V, deflation
+// x_tilde - u V^T, NVFP4 quantise + pack (model card "FastWAM UR3 3-task --
+// 4-bit quantisations", section "What ASP is, and what the deflated form
+// means").
 //
-// Every element of a row's deflated value needs the row's full reduction
-// u = x_tilde V first, so for r > 0 the workgroup covers the whole of K for
-// its rows and works in two phases:
+// Every deflated element needs its row's full reduction u = x_tilde V, and
+// both reductions of the layer -- u over K, the deflation over the rank -- read
+// a K x r basis (V'' = diag(1/s) H V for u, V for the deflation, each as bf16
+// high + low parts).  Each basis is far larger per row tile than the rows of x
+// themselves, so it is staged once per workgroup in LDS and shared by 64 rows:
 //
-//  phase 1  u.  u = x_tilde V = x (diag(1/s) H V) = x V'', with V'' a per-layer
-//           constant, so each wave contracts the raw rows of its Hadamard
-//           blocks against V'' on MFMA 16x16x32 bf16 (x is exact in bf16; an
-//           fp32 x is split into bf16 high + low; V'' is split into bf16 high +
-//           low, about 16 significant bits, the dropped low*low term lying
-//           below float32 rounding of the sum).  The waves' partial sums meet
-//           in LDS and are added in a fixed order: results are deterministic.
-//  phase 2  per (16 rows, 128-column block): scale by 1/(s sqrt 128), the
-//           Sylvester butterflies in registers and across lane rows, the
-//           deflation on MFMA, the NVFP4 quantiser and the packed stores.
-//           The raw x fragments of phase 1 stay in registers when they fit.
+//  k_prep_u  u = x_tilde V = x V'' (V'' a per-layer constant), a thin GEMM on
+//            the raw input: workgroup = 64 rows x one of S slices of K, the
+//            slice's V'' staged in LDS by direct global-to-LDS copies issued
+//            all at once, MFMA 16x16x32 bf16 with x exact in bf16 (an fp32 x
+//            split into bf16 high + low) and V'' high + low (about 16
+//            significant bits; the dropped low*low term lies below float32
+//            rounding).  Writes S partial sums of u.
+//  k_prep_q  workgroup = 64 rows x one 128-column Hadamard block, V's rows for
+//            the block and 1/(s sqrt 128) staged in LDS; each wave adds the S
+//            partial sums of u for its 16 rows in a fixed order (so results
+//            are deterministic), then transforms, deflates on MFMA, quantises
+//            and stores.  For r == 0 it runs alone, without u and V.
 //
-// With r == 0 there is no phase 1; a workgroup then takes a strip of blocks
-// and the grid also spans K.
+// S depends on K only, so a row's results do not depend on the batch it is in.
 #include "asp_device.h"
+
+#include <algorithm>
 
 namespace asp {
 namespace {
@@ -63,6 +67,7 @@ __device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8_t, q); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t q) { return __builtin_bit_cast(bf16x8_t, q); }
 
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16_rne(v);
@@ -77,14 +82,14 @@ struct XFrag;
 
 template <>
 struct XFrag<uint16_t> {
-  uint4 f[4];  // 8 bf16 per fragment
+  u32x4_t f[4];  // 8 bf16 per fragment
   __device__ __forceinline__ void load(const uint16_t* row, int col0, int q) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      f[g] = *reinterpret_cast<const uint4*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
+      f[g] = *reinterpret_cast<const u32x4_t*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
   }
   __device__ __forceinline__ void get(int g, float* v) const {
-    const uint32_t w[4] = {f[g].x, f[g].y, f[g].z, f[g].w};
+    const uint32_t w[4] = {f[g][0], f[g][1], f[g][2], f[g][3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] = bits_f32(w[e] << 16);
@@ -95,34 +100,151 @@ struct XFrag<uint16_t> {
 
 template <>
 struct XFrag<float> {
-  float4 f[8];  // 8 floats per fragment
+  f32x4_t f[8];  // 8 floats per fragment
   __device__ __forceinline__ void load(const float* row, int col0, int q) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float4* p =
-          reinterpret_cast<const float4*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
+      const f32x4_t* p =
+          reinterpret_cast<const f32x4_t*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
       f[2 * g] = p[0];
       f[2 * g + 1] = p[1];
     }
   }
   __device__ __forceinline__ void get(int g, float* v) const {
-    const float4 a = f[2 * g], b = f[2 * g + 1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const f32x4_t a = f[2 * g], b = f[2 * g + 1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
   }
 };
 
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base is wave-uniform); no registers are involved, so a
+// workgroup can have all of its staging loads in flight at once.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
-// k_prep.  Lane l of a wave: row l16 = l % 16 of the workgroup's 16 rows, lane
-// quarter q = l / 16.
+// k_prep_u.  Workgroup = 4 waves x 16 rows, one slice of K (blocks b0..b1).
+// Lane l of wave w: row m0 + 16w + l%16, lane quarter q = l/16.  Per block,
+// 4 k-steps of v_mfma_f32_16x16x32_bf16 per 16 columns of u: A = raw x
+// (fragment g supplies k-slots 8q..8q+7 -- any fixed pairing of k-slots with
+// columns works as long as B uses the same), B = rows of V''^T from LDS (u
+// column l%16, the same 8 columns).  Output lane layout: u row 4q + i, column
+// l%16.
 //
-// Phase 1 (KS > 0): per block, 4 k-steps of v_mfma_f32_16x16x32_bf16 per 16
-// columns of u: A = raw x (row l16; fragment g supplies k-slots 8q..8q+7 --
-// any fixed pairing of k-slots with columns works as long as B uses the same),
-// B = rows of V''^T (u column l16, the same 8 columns).  Output: u row 4q + i,
-// column l16.
-//
-// Phase 2, per block:
+// LDS: up to kUChunks chunks of V''^T (hi and lo; RP rows of 128 bf16 = 16
+// pieces of 16 bytes), staged in one round with lds_copy16.  Piece p of row
+// `row` sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read
+// the same piece of 16 different rows, hit 16 different bank groups.
+constexpr int kPrepRows = 64;  // rows of x per k_prep_q workgroup (4 waves x 16)
+
+template <int KS>
+struct UStage {
+  static constexpr int RP = 32 * KS;
+  static constexpr int CHUNK_PIECES = 2 * RP * 16;            // hi + lo, 16 pieces per row
+  static constexpr int CHUNKS = KS == 1 ? 8 : 4;               // 128 KB of LDS per round
+};
+
+template <typename XT, int KS>
+__global__ void __launch_bounds__(256) k_prep_u(const XT* __restrict__ x, int M, int K, int r,
+                                                    const uint16_t* __restrict__ vth,
+                                                    const uint16_t* __restrict__ vtl,
+                                                    float* __restrict__ u_part, int bps) {
+  using St = UStage<KS>;
+  constexpr int RP = St::RP, CT = KS * 2, NC = St::CHUNKS;
+  constexpr bool fp32_x = sizeof(XT) == 4;
+  extern __shared__ u32x4_t sv[];  // min(NC, bps) chunks, sized at launch
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, l16 = lane & 15;
+  const int m0 = blockIdx.x * kPrepRows + 16 * wave;
+  const int64_t mc = min(m0 + l16, M - 1);
+  const int nblk = K >> 7;
+  const int b0 = blockIdx.y * bps, b1 = min(nblk, b0 + bps);
+  const XT* xrow = x + mc * K;
+
+  f32x4_t ah[CT], al[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ah[c][i] = al[c][i] = 0.0f;
+
+  const int ncmax = min(NC, bps);
+  for (int rb = b0; rb < b1; rb += ncmax) {
+    const int nc = min(ncmax, b1 - rb);
+    // stage chunks rb .. rb+nc-1: slot P = (chunk*2 + hl)*RP*16 + row*16 + slot
+    const int pieces = nc * St::CHUNK_PIECES;
+    for (int base = 64 * wave; base < pieces; base += 256) {
+      const int P = base + lane;
+      const int c = P / St::CHUNK_PIECES, rem = P % St::CHUNK_PIECES;
+      const int hl = rem / (RP * 16), row = (rem / 16) % RP, slot = rem % 16;
+      const uint16_t* src = (hl ? vtl : vth) + (int64_t)row * K + (rb + c) * 128 + 8 * (slot ^ (row & 15));
+      lds_copy16(src, &sv[base]);
+    }
+    XFrag<XT> xr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c < nc) xr[c].load(xrow, (rb + c) * 128, q);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+    __syncthreads();                // and everyone else's
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c >= nc) break;
+      const u32x4_t* ch = sv + c * St::CHUNK_PIECES;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int piece = 8 * (g >> 1) + 2 * q + (g & 1);
+        bf16x8_t a_hi, a_lo;
+        if constexpr (!fp32_x) {
+          a_hi = as_bf16x8(xr[c].f[g]);
+        } else {
+          float f[8];
+          xr[c].get(g, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint16_t hi, lo;
+            split_bf16(f[e], hi, lo);
+            a_hi[e] = bf16_from_bits(hi);
+            a_lo[e] = bf16_from_bits(lo);
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int row = 16 * ct + l16;
+          const int slot = row * 16 + (piece ^ (row & 15));
+          const bf16x8_t b_hi = as_bf16x8(ch[slot]);
+          const bf16x8_t b_lo = as_bf16x8(ch[RP * 16 + slot]);
+          ah[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, ah[ct], 0, 0, 0);
+          al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, al[ct], 0, 0, 0);
+          if constexpr (fp32_x)
+            al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b_hi, al[ct], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // LDS is refilled by the next round
+  }
+  // partial u: rows 4q + i of the wave's 16, column 16c + l16
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 4 * q + i;
+      if (row < M) u_part[((int64_t)blockIdx.y * M + row) * RP + 16 * c + l16] = ah[c][i] + al[c][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_prep_q.  Workgroup = 4 waves x 16 rows and one 128-column block.  Lane l
+// of wave w: row m0 + 16w + l%16, lane quarter q = l/16.
+//  staging:    the block's V rows (hi, lo; 128 rows of RP bf16 = PPR pieces
+//              of 16 bytes) with lds_copy16, piece p of row `row` in slot
+//              p ^ ((row / (16/PPR)) % PPR) -- the 16 lanes of a quarter read
+//              one piece of 16 consecutive rows and hit 16 different bank
+//              groups; 1/(s sqrt 128) of the block by ordinary loads.
+//  u:          the S partial sums for the wave's rows added in slice order.
 //  transform:  the lane's 32 values are columns 64*bb + 16*q + j (bb = 0..1,
 //              j = 0..15).  Column bits 0..3 (j) and 6 (bb) are butterflied in
 //              registers; bit 4 (lane bit q0) against register bit j2 with
@@ -139,185 +261,98 @@ struct XFrag<float> {
 //              acc[b + 2*(c >> 2)][c & 3].
 //  quantise:   per block in one lane: amax, E4M3 scale, codes; one 16-byte
 //              code store and one 2-byte scale store per lane.
-//
-// Blocks of a wave: KS > 0, NB > 0: wave + i*nw for i < NB, raw x held in
-// registers between the phases; KS > 0, NB == 0: wave, wave + nw, ... with x
-// loaded again in phase 2; KS == 0: (blockIdx.y*NB + i)*nw + wave.
-template <typename XT, int KS, int NB>
-__global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, int K, int r,
-                                              const float* __restrict__ cvec,
-                                              const uint16_t* __restrict__ vth,
-                                              const uint16_t* __restrict__ vtl,
-                                              const uint16_t* __restrict__ vh,
-                                              const uint16_t* __restrict__ vl,
-                                              uint8_t* __restrict__ codes,
-                                              uint8_t* __restrict__ scales,
-                                              float* __restrict__ u_out,
-                                              float* __restrict__ pre) {
-  constexpr int RP = KS * 32;  // padded rank: row stride of V, rows of V''^T
-  constexpr int CT = KS * 2;   // 16-column tiles of u
-  constexpr int NH = NB > 0 ? NB : 1;
-  constexpr bool fp32_x = sizeof(XT) == 4;
-  __shared__ float up[KS > 0 ? 8 : 1][16][RP + 1];  // each wave's partial u
-  __shared__ float us[16][RP + 1];                  // u of the 16 rows
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+template <typename XT, int KS>
+__global__ void __launch_bounds__(256) k_prep_q(const XT* __restrict__ x, int M, int K, int r,
+                                                const float* __restrict__ cvec,
+                                                const uint16_t* __restrict__ vh,
+                                                const uint16_t* __restrict__ vl,
+                                                const float* __restrict__ u_part, int S,
+                                                uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales,
+                                                float* __restrict__ u_out,
+                                                float* __restrict__ pre) {
+  constexpr int RP = KS * 32;
+  constexpr int PPR = KS > 0 ? RP / 8 : 1;           // 16-byte pieces per V row
+  constexpr int BLK_PIECES = KS > 0 ? 2 * 128 * PPR : 1;
+  constexpr int RDIV = 16 / PPR;                      // rows sharing a swizzle key
+  constexpr int NBQ = 1;                              // blocks per workgroup
+  __shared__ u32x4_t sv[NBQ * BLK_PIECES];
+  __shared__ __attribute__((aligned(16))) float scv[NBQ][128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const int m0 = blockIdx.x * 16;
+  const int m0 = blockIdx.x * kPrepRows + 16 * wave;
   const int m = m0 + l16;
   const int64_t mc = min(m, M - 1);
   const bool mok = m < M;
   const int nblk = K >> 7;
-  const XT* xrow = x + mc * K;
+  const int bq0 = blockIdx.y * NBQ;
+  const int nb = min(NBQ, nblk - bq0);
 
-  XFrag<XT> xr[NH];
-  auto block_of = [&](int i) {
-    return KS > 0 ? wave + i * nw : ((int)blockIdx.y * NH + i) * nw + wave;
-  };
-
-  // Operands of phase 2 for one block: the V rows of its 8 tiles (hi, lo) for
-  // the deflation and its 128 values of 1/(s sqrt 128), all issued together
-  struct P2 {
-    uint4 vh[KS > 0 ? KS : 1][8], vl[KS > 0 ? KS : 1][8];
-    float4 cv[2][4];
-  };
-  auto load_p2 = [&](P2& o, int b) {
-    const int col0 = b * 128;
-    if constexpr (KS > 0) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int64_t vrow = (int64_t)(col0 + 16 * t + l16) * RP + 32 * kk + 8 * q;
-          o.vh[kk][t] = *reinterpret_cast<const uint4*>(vh + vrow);
-          o.vl[kk][t] = *reinterpret_cast<const uint4*>(vl + vrow);
-        }
+  if constexpr (KS > 0) {
+    const int pieces = nb * BLK_PIECES;
+    for (int base = 64 * wave; base < pieces; base += 256) {
+      const int P = base + lane;
+      const int i = P / BLK_PIECES, rem = P % BLK_PIECES;
+      const int hl = rem / (128 * PPR), row = (rem / PPR) % 128, slot = rem % PPR;
+      const int piece = slot ^ ((row / RDIV) % PPR);
+      const uint16_t* src = (hl ? vl : vh) + (int64_t)((bq0 + i) * 128 + row) * RP + 8 * piece;
+      lds_copy16(src, &sv[base]);
     }
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o.cv[bb][k] = reinterpret_cast<const float4*>(cvec + col0 + 64 * bb + 16 * q)[k];
-  };
-
-  // With one block per wave (and bf16 x, for registers) its phase-2 operands
-  // are issued during phase 1, right after phase 1's own loads, so their
-  // memory latency overlaps phase 1 instead of following it.
-  constexpr bool kHoist = NB == 1 && !fp32_x;
-  P2 p2first;
-  if constexpr (kHoist && KS == 0) {
-    if (block_of(0) < nblk) load_p2(p2first, block_of(0));
   }
+  f32x4_t cr;
+  if (tid < 32 * nb) cr = reinterpret_cast<const f32x4_t*>(cvec + bq0 * 128)[tid];
+  XFrag<XT> xr[NBQ];
+#pragma unroll
+  for (int i = 0; i < NBQ; ++i)
+    if (i < nb) xr[i].load(x + mc * K, (bq0 + i) * 128, q);
 
   // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
   // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
   bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
-
   if constexpr (KS > 0) {
-    f32x4_t ah[CT], al[CT];
+    float us[KS][8];
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ah[c][i] = al[c][i] = 0.0f;
-
-    // B fragments (rows of V''^T, hi and lo) of one block: all issued at once,
-    // so a block costs one memory round trip rather than one per MFMA
-    struct VFrag {
-      uint4 h[4][CT], l[4][CT];
-    };
-    auto load_v = [&](VFrag& vf, int col0) {
+      for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
+    for (int s = 0; s < S; ++s) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int kk = 0; kk < KS; ++kk) {
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(u_part + ((int64_t)s * M + mc) * RP + 32 * kk + 8 * q);
+        const f32x4_t a = p[0], c = p[1];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          const int64_t off = (int64_t)(c * 16 + l16) * K + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1);
-          vf.h[g][c] = *reinterpret_cast<const uint4*>(vth + off);
-          vf.l[g][c] = *reinterpret_cast<const uint4*>(vtl + off);
+        for (int e = 0; e < 4; ++e) {
+          us[kk][e] += a[e];
+          us[kk][4 + e] += c[e];
         }
-    };
-    auto contract = [&](const XFrag<XT>& xf, const VFrag& vf) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x8_t a_hi, a_lo;
-        if constexpr (!fp32_x) {
-          a_hi = as_bf16x8(xf.f[g]);
-        } else {
-          float f[8];
-          xf.get(g, f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            uint16_t hi, lo;
-            split_bf16(f[e], hi, lo);
-            a_hi[e] = bf16_from_bits(hi);
-            a_lo[e] = bf16_from_bits(lo);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-          const bf16x8_t b_hi = as_bf16x8(vf.h[g][c]);
-          const bf16x8_t b_lo = as_bf16x8(vf.l[g][c]);
-          ah[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, ah[c], 0, 0, 0);
-          al[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, al[c], 0, 0, 0);
-          if constexpr (fp32_x)
-            al[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b_hi, al[c], 0, 0, 0);
-        }
-      }
-    };
-
-    if constexpr (NB > 0) {
-      // x of every block, then the V'' fragments double-buffered: block i+1's
-      // loads are in flight while block i's MFMAs run
-      VFrag vf[2];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int b = block_of(i);
-        if (b < nblk) xr[i].load(xrow, b * 128, q);
-      }
-      if (block_of(0) < nblk) load_v(vf[0], block_of(0) * 128);
-      if constexpr (kHoist) {  // after phase 1's own loads, so they are served first
-        if (block_of(0) < nblk) load_p2(p2first, block_of(0));
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int b = block_of(i);
-        if (i + 1 < NB && block_of(i + 1) < nblk) load_v(vf[(i + 1) & 1], block_of(i + 1) * 128);
-        if (b < nblk) contract(xr[i], vf[i & 1]);
-      }
-    } else {
-      VFrag vf;
-      for (int b = wave; b < nblk; b += nw) {
-        xr[0].load(xrow, b * 128, q);
-        load_v(vf, b * 128);
-        contract(xr[0], vf);
       }
     }
-    // partial u (rows 4q + i, column 16c + l16) to LDS, then the fixed-order sum
+    if (bq0 == 0 && mok) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+      for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) up[wave][4 * q + i][16 * c + l16] = ah[c][i] + al[c][i];
-    __syncthreads();
-    for (int i = tid; i < 16 * RP; i += blockDim.x) {
-      const int rr = i / RP, c = i % RP;
-      float s = 0.0f;
-      for (int w = 0; w < nw; ++w) s += up[w][rr][c];
-      us[rr][c] = s;
-      if (c < r && m0 + rr < M) u_out[(int64_t)(m0 + rr) * r + c] = s;
+        for (int e = 0; e < 8; ++e)
+          if (32 * kk + 8 * q + e < r) u_out[(int64_t)m * r + 32 * kk + 8 * q + e] = us[kk][e];
     }
-    __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         uint16_t hi, lo;
-        split_bf16(-us[l16][32 * kk + 8 * q + e], hi, lo);
+        split_bf16(-us[kk][e], hi, lo);
         nuh[kk][e] = bf16_from_bits(hi);
         nul[kk][e] = bf16_from_bits(lo);
       }
   }
+  if (tid < 32 * nb) reinterpret_cast<f32x4_t*>(&scv[0][0])[tid] = cr;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies have landed
+  __syncthreads();
 
-  auto phase2 = [&](const XFrag<XT>& xf, const P2& p2, int b) {
-    const int col0 = b * 128;
-    // w[bb][j]: column col0 + 64*bb + 16*q + j times 1/(s sqrt 128); the
+#pragma unroll
+  for (int i = 0; i < NBQ; ++i) {
+    if (i >= nb) break;
+    const int col0 = (bq0 + i) * 128;
+    // w[bb][j]: column 64*bb + 16*q + j of the block times 1/(s sqrt 128); the
     // scaling is folded into the first butterfly stage (pairs j, j+1)
     float w[2][16];
 #pragma unroll
@@ -325,11 +360,12 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
       float cv[16], xv[16];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float4 t = p2.cv[bb][k];
-        cv[4 * k] = t.x; cv[4 * k + 1] = t.y; cv[4 * k + 2] = t.z; cv[4 * k + 3] = t.w;
+        const f32x4_t t = reinterpret_cast<const f32x4_t*>(&scv[i][64 * bb + 16 * q])[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cv[4 * k + e] = t[e];
       }
-      xf.get(2 * bb, xv);
-      xf.get(2 * bb + 1, xv + 8);
+      xr[i].get(2 * bb, xv);
+      xr[i].get(2 * bb + 1, xv + 8);
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
         const float t = xv[j + 1] * cv[j + 1];
@@ -372,15 +408,18 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][i] = w[t >> 2][4 * (t & 3) + i];
+      for (int e = 0; e < 4; ++e) acc[t][e] = w[t >> 2][4 * (t & 3) + e];
     if constexpr (KS > 0) {
+      const u32x4_t* vb = sv + i * BLK_PIECES;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         bf16x8_t a_hi[8], a_lo[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          a_hi[t] = as_bf16x8(p2.vh[kk][t]);
-          a_lo[t] = as_bf16x8(p2.vl[kk][t]);
+          const int row = 16 * t + l16, piece = 4 * kk + q;
+          const int slot = row * PPR + (piece ^ ((row / RDIV) % PPR));
+          a_hi[t] = as_bf16x8(vb[slot]);
+          a_lo[t] = as_bf16x8(vb[128 * PPR + slot]);
         }
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -399,16 +438,16 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[t][i] = acc[t][i];
+      for (int e = 0; e < 4; ++e) a[t][e] = acc[t][e];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) swap32(a[t][i], a[t + 4][i]);
+      for (int e = 0; e < 4; ++e) swap32(a[t][e], a[t + 4][e]);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if ((j & 2) == 0)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) swap16(a[j][i], a[j + 2][i]);
+        for (int e = 0; e < 4; ++e) swap16(a[j][e], a[j + 2][e]);
     uint32_t sc[2];
     uint2 cw[2];
 #pragma unroll
@@ -430,95 +469,43 @@ __global__ void __launch_bounds__(512) k_prep(const XT* __restrict__ x, int M, i
       *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) =
           (uint16_t)(sc[0] | (sc[1] << 8));
     }
-  };
-
-  if constexpr (NB > 0) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int b = block_of(i);
-      if (b < nblk) {
-        if constexpr (KS == 0) xr[i].load(xrow, b * 128, q);
-        if constexpr (kHoist) {
-          phase2(xr[i], p2first, b);
-        } else {
-          P2 p2;
-          load_p2(p2, b);
-          phase2(xr[i], p2, b);
-        }
-      }
-    }
-  } else {
-    for (int b = wave; b < nblk; b += nw) {
-      xr[0].load(xrow, b * 128, q);
-      P2 p2;
-      load_p2(p2, b);
-      phase2(xr[0], p2, b);
-    }
   }
 }
 
-// Most blocks per wave whose raw x stays in registers between the phases
-// without spilling (checked on the compiled kernels): more for bf16 x and
-// rank <= 32, fewer for fp32 x (twice the bytes) and rank 64 (twice the V
-// fragments).
-template <typename XT, int KS>
-constexpr int max_nb() {
-  return KS >= 2 ? 1 : (sizeof(XT) == 4 ? 2 : 4);
-}
-
-// Launch shape.  r > 0: one workgroup per 16 rows, nw <= 8 waves sharing the
-// row's blocks, nb per wave held in registers (nb = 0: x reloaded in phase 2,
-// when more than max_nb per wave would be needed).  r == 0: workgroups of up
-// to 4 waves, one block per wave, the grid spanning the blocks too.
-struct PrepShape {
-  int nw, nb;
-  dim3 grid;
-};
-
-PrepShape prep_shape(int64_t M, int64_t K, int32_t r, int maxnb) {
+// Slices of K for the partial sums of u (a function of K only, so a row's u
+// does not depend on the batch): up to 4, each a whole number of blocks.
+void u_slicing(int64_t K, int* S, int* bps) {
   const int nblk = (int)(K / 128);
-  const unsigned row_groups = (unsigned)((M + 15) / 16);
-  PrepShape s;
-  if (r == 0) {
-    s.nw = nblk < 4 ? nblk : 4;
-    s.nb = 1;
-    s.grid = dim3(row_groups, (unsigned)((nblk + s.nw - 1) / s.nw));
-    return s;
-  }
-  const int nb = (nblk + 7) / 8;
-  s.nb = nb <= maxnb ? nb : 0;
-  s.nw = s.nb > 0 ? (nblk + nb - 1) / nb : 8;
-  s.grid = dim3(row_groups, 1);
-  return s;
+  const int s = nblk < 4 ? nblk : 4;
+  *bps = (nblk + s - 1) / s;
+  *S = (nblk + *bps - 1) / *bps;
 }
 
 template <typename XT, int KS>
 void launch_ks(hipStream_t st, const XT* x, int M, int K, int r, const float* cvec,
                const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh, const uint16_t* vl,
-               uint8_t* xc, uint8_t* xs, float* u, float* pre) {
-  constexpr int MAXNB = max_nb<XT, KS>();
-  const PrepShape s = prep_shape(M, K, r, MAXNB);
-  const dim3 blk(64 * s.nw);
-#define ASP_PREP(NB_)                                                                           \
-  hipLaunchKernelGGL((k_prep<XT, KS, NB_>), s.grid, blk, 0, st, x, M, K, r, cvec, vth, vtl, vh, \
-                     vl, xc, xs, u, pre)
-  if constexpr (KS == 0) {
-    ASP_PREP(1);
-  } else {
-    switch (s.nb) {
-      case 0: ASP_PREP(0); break;
-      case 1: ASP_PREP(1); break;
-      case 2: if constexpr (MAXNB >= 2) ASP_PREP(2); break;
-      case 3: if constexpr (MAXNB >= 3) ASP_PREP(3); break;
-      default: if constexpr (MAXNB >= 4) ASP_PREP(4); break;
-    }
+               float* u_part, uint8_t* xc, uint8_t* xs, float* u, float* pre) {
+  const int nblk = K / 128;
+  const int tiles64 = (M + kPrepRows - 1) / kPrepRows;
+  int S = 0, bps = 0;
+  if constexpr (KS > 0) {
+    u_slicing(K, &S, &bps);
+    // the chunks of a slice (up to a round's worth) in dynamic LDS; above the
+    // default 64 KB this must be allowed per kernel (a host attribute of the
+    // current device, not a stream operation)
+    const size_t lds = (size_t)std::min(UStage<KS>::CHUNKS, bps) * UStage<KS>::CHUNK_PIECES * 16;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prep_u<XT, KS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S), dim3(256), lds, st,
+                       x, M, K, r, vth, vtl, u_part, bps);
   }
-#undef ASP_PREP
+  hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk), dim3(256), 0, st,
+                     x, M, K, r, cvec, vh, vl, u_part, S, xc, xs, u, pre);
 }
 
 template <typename XT>
 int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t* pack,
-                    uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant,
+                    uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant, float* u_part,
                     hipStream_t stream) {
   const PrepPackLayout L = prep_pack_layout(K, r);
   const float* cvec = reinterpret_cast<const float*>(pack + L.cvec);
@@ -529,13 +516,16 @@ int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t*
   const int Mi = (int)M, Ki = (int)K;
   switch (L.rp32 / 32) {
     case 0:
-      launch_ks<XT, 0>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
+      launch_ks<XT, 0>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+                       prequant);
       break;
     case 1:
-      launch_ks<XT, 1>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
+      launch_ks<XT, 1>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+                       prequant);
       break;
     default:
-      launch_ks<XT, 2>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, x_codes, x_scales, u, prequant);
+      launch_ks<XT, 2>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+                       prequant);
       break;
   }
   return launch_status("prep");
@@ -543,9 +533,16 @@ int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t*
 
 }  // namespace
 
+size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r) {
+  if (r == 0 || M == 0) return 0;
+  int S, bps;
+  u_slicing(K, &S, &bps);
+  return (size_t)S * (size_t)M * (size_t)prep_pack_layout(K, r).rp32 * sizeof(float);
+}
+
 int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                       const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, hipStream_t stream) {
+                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream) {
   ASP_TRY(check_mk(M, K));
   ASP_TRY(check_rank(r));
   if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
@@ -556,11 +553,18 @@ int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int3
   ASP_TRY(check_ptr(x_scales, "x_scales", true));
   ASP_TRY(check_ptr(u, "u", r > 0));
   ASP_TRY(check_ptr(prequant, "prequant", false));
+  const size_t need = act_prep_scratch_bytes(M, K, r);
+  if (need) {
+    ASP_TRY(check_ptr(scratch, "workspace", true));
+    if (scratch_bytes < need)
+      return fail(ASP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", scratch_bytes, need);
+  }
+  float* u_part = static_cast<float*>(scratch);
   if (x_dtype == ASP_F32)
     return launch_prep(static_cast<const float*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                       prequant, stream);
+                       prequant, u_part, stream);
   return launch_prep(static_cast<const uint16_t*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                     prequant, stream);
+                     prequant, u_part, stream);
 }
 
 }  // namespace asp
@@ -569,12 +573,21 @@ using namespace asp;
 
 extern "C" {
 
+int32_t asp_act_prep_workspace_bytes(int64_t M, int64_t K, int32_t r, size_t* bytes) {
+  clear_error();
+  ASP_TRY(check_mk(M, K));
+  ASP_TRY(check_rank(r));
+  if (!bytes) return fail(ASP_ERR_ARG, "null output pointer");
+  *bytes = act_prep_scratch_bytes(M, K, r);
+  return ASP_OK;
+}
+
 int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                     float* prequant, void* stream) {
+                     float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return act_prep_impl(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant,
-                       (hipStream_t)stream);
+  return act_prep_impl(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant, workspace,
+                       workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"
