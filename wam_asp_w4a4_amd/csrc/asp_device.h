@@ -69,6 +69,14 @@ __device__ __forceinline__ uint2 quantize_block(const float (&v)[16], uint32_t& 
   return make_uint2(w0, w1);
 }
 
+// Direct global-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_base + 16*l; lds_base must be wave-uniform.  No
+// registers are involved, so many copies can be in flight at once; they count
+// as vector-memory operations for s_waitcnt.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 // 8 packed E2M1 codes (one K-step's worth for one MFMA lane) times their
 // block scale, as exact fp16.  The hardware conversion applies only the
 // power-of-two part of a scale, so it runs with scale 1 and the E4M3 scale

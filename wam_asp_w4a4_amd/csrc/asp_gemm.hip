@@ -290,23 +290,58 @@ __global__ void __launch_bounds__(WM * WN * 64)
 
   // bias and store; accumulator element v of lane l is row 8*(v/4) + 4*(l/32)
   // + v%4 and column l%32 of its 32 x 32 tile
+  float bj[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int col = n0 + (wn * TN + j) * 32 + l32;
-    const bool cok2 = col < N;
-    const float bcol = (bias && cok2) ? bias[col] : 0.0f;
+    bj[j] = (bias && col < N) ? bias[col] : 0.0f;
+  }
+  if (y_bf16) {
+    // through LDS (the staging buffers are free once every wave is past the
+    // K loop), so that each thread writes 16 consecutive bytes of a row
+    static_assert(C::BM * C::BN * 2 <= C::LDS, "output tile must fit the staging LDS");
+    __syncthreads();
+    uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (!cok2 || row >= M) continue;
-        const float val = acc[i][j][v] + bcol;
-        if (y_bf16)
-          reinterpret_cast<uint16_t*>(y)[(int64_t)row * N + col] = f32_to_bf16_rne(val);
-        else
-          reinterpret_cast<float*>(y)[(int64_t)row * N + col] = val;
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const int col = (wn * TN + j) * 32 + l32;
+          ot[row * C::BN + col] = f32_to_bf16_rne(acc[i][j][v] + bj[j]);
+        }
+    __syncthreads();
+    uint16_t* yo = reinterpret_cast<uint16_t*>(y);
+    constexpr int CHUNKS = C::BM * C::BN / 8;
+    for (int c = tid; c < CHUNKS; c += C::NT) {
+      const int row = c / (C::BN / 8), col = (c % (C::BN / 8)) * 8;
+      const int gm = m0 + row, gn = n0 + col;
+      if (gm >= M) continue;
+      const int64_t off = (int64_t)gm * N + gn;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + row * C::BN + col);
+      if (gn + 8 <= N && (off & 7) == 0) {
+        *reinterpret_cast<u32x4_t*>(yo + off) = val;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gn + e < N) yo[off + e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
       }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + (wn * TN + j) * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (row < M) reinterpret_cast<float*>(y)[(int64_t)row * N + col] = acc[i][j][v] + bj[j];
+        }
+    }
   }
 }
 

@@ -120,13 +120,6 @@ struct XFrag<float> {
   }
 };
 
-// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base is wave-uniform); no registers are involved, so a
-// workgroup can have all of its staging loads in flight at once.
-__device__ __forceinline__ void lds_copy16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // k_prep_u.  Workgroup = 4 waves x 16 rows, one slice of K (blocks b0..b1).
 // Lane l of wave w: row m0 + 16w + l%16, lane quarter q = l/16.  Per block,
