@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the deflated-ASP NVFP4 W4A4 linear on one MI355X.
 
-One step = the whole per-call path (fused activation prep + 4-bit GEMM with
-the low-rank/bias epilogue) for every layer of the workload, on inputs and
+One step = the whole per-call path (the two activation-prep kernels, then the
+4-bit GEMM with the low-rank/bias epilogue) for every layer of the workload, on inputs and
 packed weights already resident in HBM.  The weight packing is offline (once
 per layer) and outside the timed region.  Steps rotate through replicas of
 every buffer (>= 1 GiB in total) so that each step reads from HBM rather than
@@ -41,7 +41,8 @@ CSRC = os.path.join(ROOT, "wam_asp_w4a4_amd", "csrc")
 # the sources each kernel is built from: a traffic figure measured with
 # hardware counters stays valid only while these files are unchanged
 KERNEL_SOURCES = {
-    "k_prep": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+    "k_prep_u": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+    "k_prep_q": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
     "k_gemm": ["asp_gemm.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
 }
 WORKLOAD_SLUGS = {0: "single_M64_K512_N512", 1: "action_attn_M256_K1024_N1024",
@@ -59,9 +60,15 @@ def layer_bytes(M, N, K, r, xb, yb):
     return M * K * xb + M * N * yb + N * K // 2 + N * K // 16 + 2 * N * r + 4 * K * r + 4 * K + 4 * N
 
 
-def prep_bytes(M, K, r, xb):
-    """Algorithmic bytes of one activation-prep launch: x, s, V in; codes, scales, u out."""
-    return M * K * xb + 4 * K + 4 * K * r + M * K // 2 + M * K // 16 + 4 * M * r
+def prep_u_bytes(M, K, r, xb):
+    """Algorithmic bytes of the u stage: x and diag(1/s) H V (two bf16 planes) in, u out."""
+    return M * K * xb + 4 * K * r + 4 * M * r
+
+
+def prep_q_bytes(M, K, r, xb):
+    """Algorithmic bytes of the quantise stage: x, 1/s, V (two bf16 planes) and u in;
+    codes, scales and u out."""
+    return M * K * xb + 4 * K + 4 * K * r + 4 * M * r + M * K // 2 + M * K // 16 + 4 * M * r
 
 
 def gemm_bytes(M, N, K, r, yb):
@@ -74,8 +81,23 @@ def gemm_flops(M, N, K, r):
     return 2 * M * N * K + 2 * M * N * r
 
 
-def prep_flops(M, K, r):
-    return 4 * M * K * r
+def prep_u_flops(M, K, r):
+    return 2 * M * K * r
+
+
+def prep_q_flops(M, K, r):
+    return 2 * M * K * r
+
+
+def roofline_of(nbytes, nflops, ms):
+    """The bound a kernel's arithmetic intensity puts it under, and its fraction of that peak."""
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = nflops / (ms * 1e-3) / 1e12
+    if nflops / nbytes >= RIDGE:
+        return {"bound": "mfma", "achieved": round(tfs, 2), "peak": F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfs / F16_PEAK_TFLOPS, 4)}, gbs, tfs
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}, gbs, tfs
 
 
 def parse():
@@ -233,21 +255,26 @@ def main():
             scratch = ws[off2 + up(4 * M * r):]
             launches.append((lay, p, x, y, xc, xs, u, scratch))
 
-    def prep_launch(lay, p, x, y, xc, xs, u, scratch):
-        B.asp_act_prep(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None,
-                       scratch, scratch.numel())
+    def prep_u_launch(lay, p, x, y, xc, xs, u, scratch):
+        B.asp_act_prep_u(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, scratch,
+                         scratch.numel())
+
+    def prep_q_launch(lay, p, x, y, xc, xs, u, scratch):
+        B.asp_act_prep_q(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None,
+                         scratch, scratch.numel())
 
     def gemm_launch(lay, p, x, y, xc, xs, u, scratch):
         B.asp_gemm_lowrank(xc, xs, u, lay.M, lay.N, lay.K, lay.r, p.w_codes, p.w_scales, p.wv,
                            p.bias, y, B.DTYPES[y_dtype])
 
-    def graph_ms(fn):
-        for a in launches[: len(layers)]:  # warm the code path outside the capture
+    def graph_ms(fn, sel):
+        todo = [a for a in launches if sel(a[0])]
+        for a in todo[: len(layers)]:  # warm the code path outside the capture
             fn(*a)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for a in launches:
+            for a in todo:
                 fn(*a)
         torch.cuda.synchronize()
         ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -255,44 +282,44 @@ def main():
         g.replay()
         eb.record(stream)
         torch.cuda.synchronize()
-        return ea.elapsed_time(eb)
+        return ea.elapsed_time(eb), len(todo)
 
-    prep_ms = graph_ms(prep_launch)   # also leaves valid codes in every workspace used
-    gemm_ms = graph_ms(gemm_launch)
-    prep_b = gemm_b = prep_f = gemm_f = 0
-    for lay, *_ in launches:
-        xb = 2 if lay.x_dtype == "bf16" else 4
-        prep_b += prep_bytes(lay.M, lay.K, lay.r, xb)
-        gemm_b += gemm_bytes(lay.M, lay.N, lay.K, lay.r, yb)
-        prep_f += prep_flops(lay.M, lay.K, lay.r)
-        gemm_f += gemm_flops(lay.M, lay.N, lay.K, lay.r)
-    evs = launches
-    n_launch = len(evs)
-    if gemm_ms >= prep_ms:
-        name, ms, nbytes, nflops = "k_gemm", gemm_ms, gemm_b, gemm_f
-    else:
-        name, ms, nbytes, nflops = "k_prep", prep_ms, prep_b, prep_f
-    avg_us = ms / n_launch * 1e3
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    tfs = nflops / (ms * 1e-3) / 1e12
-    ai = nflops / nbytes
-    if ai >= RIDGE:
-        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tfs / F16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # the three kernels of the path, each over the launches that run it (the u
+    # stage launches nothing for a rank-0 layer); the u stage goes first so the
+    # quantise stage and then the GEMM read valid partial sums and codes
+    xbytes = lambda l: 2 if l.x_dtype == "bf16" else 4
+    gemm_names = sorted({B.asp_gemm_kernel_name(l.M, l.N, l.K) for l, _, _ in host})
+    kernels = [
+        ("k_prep_u", "k_prep_u", prep_u_launch, lambda l: l.r > 0,
+         lambda l: prep_u_bytes(l.M, l.K, l.r, xbytes(l)), lambda l: prep_u_flops(l.M, l.K, l.r)),
+        ("k_prep_q", "k_prep_q", prep_q_launch, lambda l: True,
+         lambda l: prep_q_bytes(l.M, l.K, l.r, xbytes(l)), lambda l: prep_q_flops(l.M, l.K, l.r)),
+        (" + ".join(gemm_names), "k_gemm", gemm_launch, lambda l: True,
+         lambda l: gemm_bytes(l.M, l.N, l.K, l.r, yb), lambda l: gemm_flops(l.M, l.N, l.K, l.r)),
+    ]
+    timed = []
+    for name, family, fn, sel, fb, ff in kernels:
+        if not any(sel(a[0]) for a in launches):
+            continue
+        ms, n = graph_ms(fn, sel)
+        nbytes = sum(fb(a[0]) for a in launches if sel(a[0]))
+        nflops = sum(ff(a[0]) for a in launches if sel(a[0]))
+        timed.append((name, family, ms, n, nbytes, nflops))
+    name, family, ms, n_launch, nbytes, nflops = max(timed, key=lambda k: k[2])
+    roof, gbs, tfs = roofline_of(nbytes, nflops, ms)
     roof.update({
-        "traffic": measured_traffic(name, args.workload),
+        "traffic": measured_traffic(family, args.workload),
         "kernel": name,
-        "source_digest": kernel_source_digest(name),
-        "avg_launch_us": round(avg_us, 3),
+        "source_digest": kernel_source_digest(family),
+        "avg_launch_us": round(ms / n_launch * 1e3, 3),
         "launches": n_launch,
         "algorithmic_bytes_per_launch": nbytes // n_launch,
         "algorithmic_flops_per_launch": nflops // n_launch,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_f16_frac": round(tfs / F16_PEAK_TFLOPS, 4),
-        "other_kernel_avg_us": round((prep_ms if name == "k_gemm" else gemm_ms) / n_launch * 1e3, 3),
+        "kernels": {k[0]: {"avg_launch_us": round(k[2] / k[3] * 1e3, 3),
+                           "frac": roofline_of(k[4], k[5], k[2])[0]["frac"],
+                           "bound": roofline_of(k[4], k[5], k[2])[0]["bound"]} for k in timed},
     })
 
     # ---- CPU baseline: the oracle, on the host cores, on a bounded sample

@@ -185,6 +185,22 @@ int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two launches of asp_act_prep as separate entry points (for profiling
+ * each kernel on its own).  asp_act_prep_u writes the partial sums of u into
+ * the workspace (nothing when r == 0); asp_act_prep_q, called afterwards on
+ * the same stream with the same x, M, K, r, prep_pack and workspace, adds
+ * them and produces x_codes, x_scales, u (and prequant).  Together they equal
+ * asp_act_prep bit for bit.  Arguments as for asp_act_prep.
+ */
+int32_t asp_act_prep_u(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                       int32_t r, const uint8_t* prep_pack, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int32_t asp_act_prep_q(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                       int32_t r, const uint8_t* prep_pack, uint8_t* x_codes,
+                       uint8_t* x_scales, float* u, float* prequant,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * 4-bit GEMM with fused low-rank and bias epilogue:
  *   y = DQ(x_codes, x_scales) DQ(w_codes, w_scales)^T + bf16(u) wv^T + bias
  * The NVFP4 operands are decoded in registers to exact fp16 values (an E2M1
@@ -205,6 +221,13 @@ int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales,
                          const uint8_t* w_scales, const uint16_t* wv,
                          const float* bias, void* y, int32_t y_dtype,
                          void* stream);
+
+/*
+ * Name of the GPU kernel asp_gemm_lowrank launches for an M x N x K call, as
+ * a profiler lists it (for example "k_gemm<4, 2, 2, 3>"); "" for a shape the
+ * GEMM rejects.  Host only; the string is static and owned by the library.
+ */
+const char* asp_gemm_kernel_name(int64_t M, int64_t N, int64_t K);
 
 /* Workspace bytes asp_forward needs (activation codes, scales, u, prep scratch). */
 int32_t asp_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r,

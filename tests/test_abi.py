@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_entry_points():
     names = _declared_functions()
-    for must in ("asp_pack_weight", "asp_act_prep", "asp_gemm_lowrank", "asp_forward",
+    for must in ("asp_pack_weight", "asp_act_prep", "asp_act_prep_u", "asp_act_prep_q",
+                 "asp_gemm_lowrank", "asp_forward",
                  "asp_quantize_nvfp4", "asp_dequantize_nvfp4"):
         assert must in names
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == B.ABI_VERSION == 4
+    assert B.asp_abi_version() == B.ABI_VERSION == 5
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
@@ -105,6 +106,34 @@ def test_act_prep_pointer_validation():
     need = B.asp_act_prep_workspace_bytes(4, 128, 16)
     assert need > 0 and B.asp_act_prep_workspace_bytes(4, 128, 0) == 0
     assert _act_prep(ws_bytes=need - 1)[0] == 5
+
+
+def test_gemm_kernel_name_follows_tile_choice():
+    assert B.asp_gemm_kernel_name(4096, 3072, 3072) == "k_gemm<4, 2, 2, 3>"
+    assert B.asp_gemm_kernel_name(1024, 1024, 256) == "k_gemm<2, 2, 1, 1>"
+    assert B.asp_gemm_kernel_name(256, 1024, 1024) == "k_gemm_sk<1, 1, 4>"
+    assert B.asp_gemm_kernel_name(64, 64, 2048) == "k_gemm_sk<1, 1, 8>"
+    assert B.asp_gemm_kernel_name(1, 16, 128) == "k_gemm_sk<1, 1, 1>"
+    assert B.asp_gemm_kernel_name(4, 16, 100) == ""
+
+
+def test_act_prep_stage_entry_points_validate():
+    lib = B.lib()
+    need = B.asp_act_prep_workspace_bytes(4, 128, 16)
+    pu = lambda **o: lib.asp_act_prep_u(o.get("x", FAKE), 1, 4, 128, o.get("r", 16), FAKE,
+                                        o.get("ws", FAKE), o.get("nb", need), None)
+    assert pu(x=None) == 1
+    assert pu(x=MIS) == 3
+    assert pu(ws=None) == 1
+    assert pu(nb=need - 1) == 5
+    pq = lambda **o: lib.asp_act_prep_q(FAKE, 1, 4, 128, 16, FAKE, o.get("xc", FAKE), FAKE,
+                                        o.get("u", FAKE), None, FAKE, need, None)
+    assert pq(xc=None) == 1
+    assert pq(u=None) == 1
+    assert pq(u=MIS) == 3
+    with pytest.raises(B.ASPError) as ei:
+        B.asp_act_prep_u(None, 0, 4, 100, 0, None)
+    assert ei.value.status == 2
 
 
 def test_forward_workspace_and_alignment_checks():

@@ -158,6 +158,35 @@ def test_act_prep_against_oracle(lay):
     assert np.mean(xs != act["x_scales"]) <= 1e-3
 
 
+@pytest.mark.parametrize("lay", prep_cases()[:3] + prep_cases()[3:4] + prep_cases()[7:],
+                         ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
+def test_act_prep_stages_equal_combined(lay):
+    """asp_act_prep_u then asp_act_prep_q reproduce asp_act_prep bit for bit."""
+    M, K, r = lay.M, lay.K, lay.r
+    pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
+    B.asp_pack_prep(K, r, lay.s, lay.v, pack)
+    pack_d, x_d = dev(pack), x_device(lay)
+    nws = B.asp_act_prep_workspace_bytes(M, K, r)
+    outs = []
+    for staged in (False, True):
+        xc = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
+        xs = torch.empty((M, K // 16), dtype=torch.uint8, device=DEV)
+        u = torch.empty((M, max(r, 1)), dtype=torch.float32, device=DEV)
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=DEV)
+        if staged:
+            B.asp_act_prep_u(x_d, B.DTYPES[lay.x_dtype], M, K, r, pack_d, ws, nws)
+            B.asp_act_prep_q(x_d, B.DTYPES[lay.x_dtype], M, K, r, pack_d, xc, xs,
+                             u if r else None, None, ws, nws)
+        else:
+            B.asp_act_prep(x_d, B.DTYPES[lay.x_dtype], M, K, r, pack_d, xc, xs,
+                           u if r else None, None, ws, nws)
+        outs.append((host(xc), host(xs), host(u) if r else None))
+    (c0, s0, u0), (c1, s1, u1) = outs
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    if r:
+        assert np.array_equal(u0.view(np.uint32), u1.view(np.uint32))
+
+
 # ----------------------------------------------------------------------- GEMM
 
 

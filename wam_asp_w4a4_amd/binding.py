@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
 
 ASP_F32 = 0
@@ -31,6 +31,7 @@ SIGNATURES = {
     "asp_abi_version": (_i32, []),
     "asp_status_string": (ctypes.c_char_p, [_i32]),
     "asp_last_error": (ctypes.c_char_p, []),
+    "asp_gemm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "asp_packed_sizes": (_i32, [_i64, _i64, _i32, _psz, _psz, _psz]),
     "asp_pack_weight": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32]),
     "asp_quantize_nvfp4_host": (_i32, [_p, _i64, _i64, _p, _p]),
@@ -40,6 +41,8 @@ SIGNATURES = {
     "asp_dequantize_nvfp4": (_i32, [_p, _p, _i64, _i64, _p, _p]),
     "asp_act_prep_workspace_bytes": (_i32, [_i64, _i64, _i32, _psz]),
     "asp_act_prep": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "asp_act_prep_u": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _sz, _p]),
+    "asp_act_prep_q": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "asp_gemm_lowrank": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
     "asp_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
     "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32,
@@ -171,6 +174,23 @@ def asp_act_prep(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant=
     _check(lib().asp_act_prep(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(x_codes),
                               _ptr(x_scales), _ptr(u), _ptr(prequant), _ptr(workspace),
                               workspace_bytes, _stream(stream, x)))
+
+
+def asp_gemm_kernel_name(M, N, K):
+    return lib().asp_gemm_kernel_name(M, N, K).decode()
+
+
+def asp_act_prep_u(x, x_dtype, M, K, r, prep_pack, workspace=None, workspace_bytes=0,
+                   stream=None):
+    _check(lib().asp_act_prep_u(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(workspace),
+                                workspace_bytes, _stream(stream, x)))
+
+
+def asp_act_prep_q(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant=None,
+                   workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().asp_act_prep_q(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(x_codes),
+                                _ptr(x_scales), _ptr(u), _ptr(prequant), _ptr(workspace),
+                                workspace_bytes, _stream(stream, x)))
 
 
 def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,

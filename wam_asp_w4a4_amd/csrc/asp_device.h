@@ -127,9 +127,11 @@ inline int32_t check_mk(int64_t M, int64_t K) {
 
 // Internal launchers (validate, then enqueue on `stream`).
 size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r);
-int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
-                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream);
+// stages: 1 = partial sums of u (k_prep_u), 2 = the rest (k_prep_q), 3 = both
+int32_t act_prep_impl(int stages, const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                      int32_t r, const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales,
+                      float* u, float* prequant, void* scratch, size_t scratch_bytes,
+                      hipStream_t stream);
 int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype);
 int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
                   int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,

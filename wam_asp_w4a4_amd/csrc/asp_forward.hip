@@ -63,7 +63,7 @@ int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N, int64_
   uint8_t* xc = base + L.codes;
   uint8_t* xs = base + L.scales;
   float* u = r > 0 ? reinterpret_cast<float*>(base + L.u) : nullptr;
-  ASP_TRY(act_prep_impl(x, x_dtype, M, K, r, prep_pack, xc, xs, u, nullptr, base + L.scratch,
+  ASP_TRY(act_prep_impl(3, x, x_dtype, M, K, r, prep_pack, xc, xs, u, nullptr, base + L.scratch,
                         L.total - L.scratch, (hipStream_t)stream));
   return gemm_impl(xc, xs, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
                    (hipStream_t)stream);

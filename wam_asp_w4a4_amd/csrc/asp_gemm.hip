@@ -568,6 +568,39 @@ int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype) 
   return ASP_OK;
 }
 
+enum GemmVariant { kGemm256x192, kGemm64x64, kGemmSplitK8, kGemmSplitK4, kGemmSplitK2,
+                   kGemmSplitK1 };
+
+// Tile choice.  Large layers: 256 x 192 workgroup tiles (256 tiles, one per
+// CU, for a 4096 x 3072 output) of 8 waves with 64 x 96 per-wave tiles: five
+// fragment decodes feed six MFMAs per K-step, and two waves per SIMD overlap
+// one wave's decode with the other's MFMAs.  Mid-size layers with at least
+// 256 tiles of 64 x 64: those tiles, 4 waves each.  Fewer tiles (small M):
+// 32 x 32 tiles with K split over the workgroup's waves (k_gemm_sk), so that
+// more waves share the work and each one's chain of dependent K-steps is
+// shorter.
+GemmVariant gemm_variant(int64_t M, int64_t N, int64_t K) {
+  if (((M + 255) / 256) * ((N + 191) / 192) >= 128) return kGemm256x192;
+  if (((M + 63) / 64) * ((N + 63) / 64) >= 256) return kGemm64x64;
+  switch (sk_waves(K)) {
+    case 8: return kGemmSplitK8;
+    case 4: return kGemmSplitK4;
+    case 2: return kGemmSplitK2;
+    default: return kGemmSplitK1;
+  }
+}
+
+const char* gemm_variant_name(GemmVariant v) {
+  switch (v) {
+    case kGemm256x192: return "k_gemm<4, 2, 2, 3>";
+    case kGemm64x64: return "k_gemm<2, 2, 1, 1>";
+    case kGemmSplitK8: return "k_gemm_sk<1, 1, 8>";
+    case kGemmSplitK4: return "k_gemm_sk<1, 1, 4>";
+    case kGemmSplitK2: return "k_gemm_sk<1, 1, 2>";
+    default: return "k_gemm_sk<1, 1, 1>";
+  }
+}
+
 int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
                   int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
                   const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
@@ -582,30 +615,20 @@ int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* 
   ASP_TRY(check_ptr(wv, "wv", r > 0));
   ASP_TRY(check_ptr(bias, "bias", false));
   ASP_TRY(check_ptr(y, "y", true));
-  // Tile choice.  Large layers: 256 x 192 workgroup tiles (256 tiles, one per
-  // CU, for a 4096 x 3072 output) of 8 waves with 64 x 96 per-wave tiles: five
-  // fragment decodes feed six MFMAs per K-step, and two waves per SIMD overlap
-  // one wave's decode with the other's MFMAs.  Mid-size layers with at least
-  // 256 tiles of 64 x 64: those tiles, 4 waves each.  Fewer tiles (small M):
-  // 32 x 32 tiles with K split over the workgroup's waves (k_gemm_sk), so that
-  // more waves share the work and each one's chain of dependent K-steps is
-  // shorter.
-  const int64_t t192 = ((M + 255) / 256) * ((N + 191) / 192);
-  if (t192 >= 128)
-    return launch_gemm<4, 2, 2, 3>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
-                                   y, y_dtype, stream);
-  const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-  if (t64 >= 256)
-    return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias,
-                                   y, y_dtype, stream);
-  switch (sk_waves(K)) {
-    case 8:
+  switch (gemm_variant(M, N, K)) {
+    case kGemm256x192:
+      return launch_gemm<4, 2, 2, 3>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+    case kGemm64x64:
+      return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
+                                     bias, y, y_dtype, stream);
+    case kGemmSplitK8:
       return launch_gemm_sk<1, 1, 8>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
                                      bias, y, y_dtype, stream);
-    case 4:
+    case kGemmSplitK4:
       return launch_gemm_sk<1, 1, 4>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
                                      bias, y, y_dtype, stream);
-    case 2:
+    case kGemmSplitK2:
       return launch_gemm_sk<1, 1, 2>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
                                      bias, y, y_dtype, stream);
     default:
@@ -627,6 +650,11 @@ int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales, const 
   clear_error();
   return gemm_impl(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
                    (hipStream_t)stream);
+}
+
+const char* asp_gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 128 != 0) return "";
+  return gemm_variant_name(gemm_variant(M, N, K));
 }
 
 }  // extern "C"

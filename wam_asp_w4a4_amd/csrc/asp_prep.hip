@@ -465,6 +465,8 @@ __global__ void __launch_bounds__(256) k_prep_q(const XT* __restrict__ x, int M,
   }
 }
 
+constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
+
 // Slices of K for the partial sums of u (a function of K only, so a row's u
 // does not depend on the batch): up to 4, each a whole number of blocks.
 void u_slicing(int64_t K, int* S, int* bps) {
@@ -475,7 +477,7 @@ void u_slicing(int64_t K, int* S, int* bps) {
 }
 
 template <typename XT, int KS>
-void launch_ks(hipStream_t st, const XT* x, int M, int K, int r, const float* cvec,
+void launch_ks(hipStream_t st, int stages, const XT* x, int M, int K, int r, const float* cvec,
                const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh, const uint16_t* vl,
                float* u_part, uint8_t* xc, uint8_t* xs, float* u, float* pre) {
   const int nblk = K / 128;
@@ -483,21 +485,24 @@ void launch_ks(hipStream_t st, const XT* x, int M, int K, int r, const float* cv
   int S = 0, bps = 0;
   if constexpr (KS > 0) {
     u_slicing(K, &S, &bps);
-    // the chunks of a slice (up to a round's worth) in dynamic LDS; above the
-    // default 64 KB this must be allowed per kernel (a host attribute of the
-    // current device, not a stream operation)
-    const size_t lds = (size_t)std::min(UStage<KS>::CHUNKS, bps) * UStage<KS>::CHUNK_PIECES * 16;
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prep_u<XT, KS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S), dim3(256), lds, st,
-                       x, M, K, r, vth, vtl, u_part, bps);
+    if (stages & kStageU) {
+      // the chunks of a slice (up to a round's worth) in dynamic LDS; above the
+      // default 64 KB this must be allowed per kernel (a host attribute of the
+      // current device, not a stream operation)
+      const size_t lds = (size_t)std::min(UStage<KS>::CHUNKS, bps) * UStage<KS>::CHUNK_PIECES * 16;
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prep_u<XT, KS>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S), dim3(256), lds, st,
+                         x, M, K, r, vth, vtl, u_part, bps);
+    }
   }
-  hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk), dim3(256), 0, st,
-                     x, M, K, r, cvec, vh, vl, u_part, S, xc, xs, u, pre);
+  if (stages & kStageQ)
+    hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk), dim3(256), 0,
+                       st, x, M, K, r, cvec, vh, vl, u_part, S, xc, xs, u, pre);
 }
 
 template <typename XT>
-int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t* pack,
+int32_t launch_prep(int stages, const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t* pack,
                     uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant, float* u_part,
                     hipStream_t stream) {
   const PrepPackLayout L = prep_pack_layout(K, r);
@@ -509,15 +514,15 @@ int32_t launch_prep(const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t*
   const int Mi = (int)M, Ki = (int)K;
   switch (L.rp32 / 32) {
     case 0:
-      launch_ks<XT, 0>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+      launch_ks<XT, 0>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
                        prequant);
       break;
     case 1:
-      launch_ks<XT, 1>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+      launch_ks<XT, 1>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
                        prequant);
       break;
     default:
-      launch_ks<XT, 2>(stream, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
+      launch_ks<XT, 2>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
                        prequant);
       break;
   }
@@ -533,19 +538,22 @@ size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r) {
   return (size_t)S * (size_t)M * (size_t)prep_pack_layout(K, r).rp32 * sizeof(float);
 }
 
-int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
-                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
-                      float* prequant, void* scratch, size_t scratch_bytes, hipStream_t stream) {
+int32_t act_prep_impl(int stages, const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                      int32_t r, const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales,
+                      float* u, float* prequant, void* scratch, size_t scratch_bytes,
+                      hipStream_t stream) {
   ASP_TRY(check_mk(M, K));
   ASP_TRY(check_rank(r));
   if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
   if (M == 0) return ASP_OK;
   ASP_TRY(check_ptr(x, "x", true));
   ASP_TRY(check_ptr(prep_pack, "prep_pack", true));
-  ASP_TRY(check_ptr(x_codes, "x_codes", true));
-  ASP_TRY(check_ptr(x_scales, "x_scales", true));
-  ASP_TRY(check_ptr(u, "u", r > 0));
-  ASP_TRY(check_ptr(prequant, "prequant", false));
+  if (stages & kStageQ) {
+    ASP_TRY(check_ptr(x_codes, "x_codes", true));
+    ASP_TRY(check_ptr(x_scales, "x_scales", true));
+    ASP_TRY(check_ptr(u, "u", r > 0));
+    ASP_TRY(check_ptr(prequant, "prequant", false));
+  }
   const size_t need = act_prep_scratch_bytes(M, K, r);
   if (need) {
     ASP_TRY(check_ptr(scratch, "workspace", true));
@@ -554,10 +562,10 @@ int32_t act_prep_impl(const void* x, int32_t x_dtype, int64_t M, int64_t K, int3
   }
   float* u_part = static_cast<float*>(scratch);
   if (x_dtype == ASP_F32)
-    return launch_prep(static_cast<const float*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                       prequant, u_part, stream);
-  return launch_prep(static_cast<const uint16_t*>(x), M, K, r, prep_pack, x_codes, x_scales, u,
-                     prequant, u_part, stream);
+    return launch_prep(stages, static_cast<const float*>(x), M, K, r, prep_pack, x_codes,
+                       x_scales, u, prequant, u_part, stream);
+  return launch_prep(stages, static_cast<const uint16_t*>(x), M, K, r, prep_pack, x_codes,
+                     x_scales, u, prequant, u_part, stream);
 }
 
 }  // namespace asp
@@ -579,8 +587,24 @@ int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32
                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
                      float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return act_prep_impl(x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant, workspace,
-                       workspace_bytes, (hipStream_t)stream);
+  return act_prep_impl(kStageU | kStageQ, x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u,
+                       prequant, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int32_t asp_act_prep_u(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
+                       const uint8_t* prep_pack, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  clear_error();
+  return act_prep_impl(kStageU, x, x_dtype, M, K, r, prep_pack, nullptr, nullptr, nullptr,
+                       nullptr, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int32_t asp_act_prep_q(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
+                       const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
+                       float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return act_prep_impl(kStageQ, x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant,
+                       workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"
