@@ -2,7 +2,9 @@
 """Throughput of the deflated-ASP NVFP4 W4A4 linear on one MI355X.
 
 One step = the whole per-call path (the two activation-prep kernels, then the
-4-bit GEMM with the low-rank/bias epilogue) for every layer of the workload, on inputs and
+4-bit GEMM with the low-rank/bias epilogue) for every layer of the workload;
+layers that read the same input (the attention projection pair) run as one
+group, each kernel launched once for the group, on inputs and
 packed weights already resident in HBM.  The weight packing is offline (once
 per layer) and outside the timed region.  Steps rotate through replicas of
 every buffer (>= 1 GiB in total) so that each step reads from HBM rather than
@@ -186,25 +188,43 @@ def main():
         x = torch.from_numpy(np.ascontiguousarray(a))
         return (x.view(dtype) if dtype is not None else x).to(dev)
 
+    # layers that read one x (and share K and rank) run as one group: one
+    # launch per kernel for the whole group
+    group_keys = []
+    for lay, _, _ in host:
+        key = (id(lay.x), lay.K, lay.r, lay.x_dtype)
+        if key not in group_keys:
+            group_keys.append(key)
+    group_of = [group_keys.index((id(l.x), l.K, l.r, l.x_dtype)) for l, _, _ in host]
+
     replicas = []
     for _ in range(R):
-        rep = []
-        shared_x = {}
-        for lay, pk, xh in host:
-            key = id(lay.x)
-            if key not in shared_x:  # layers that share x share it within a replica
-                shared_x[key] = t(xh, torch.bfloat16 if lay.x_dtype == "bf16" else None)
+        groups = [{"layers": [], "packed": [], "ys": [], "wss": [], "x": None}
+                  for _ in group_keys]
+        for (lay, pk, xh), gi in zip(host, group_of):
+            g = groups[gi]
+            if g["x"] is None:
+                g["x"] = t(xh, torch.bfloat16 if lay.x_dtype == "bf16" else None)
             p = PackedLayer(lay.N, lay.K, lay.r, t(pk["w_codes"]), t(pk["w_scales"]),
                             None if pk["wv"] is None else t(pk["wv"], torch.int16),
                             t(pk["prep"]), t(lay.b))
-            y = torch.empty((lay.M, lay.N), dtype=torch.bfloat16, device=dev)
-            ws = p.workspace(lay.M)
-            rep.append((lay, p, shared_x[key], y, ws))
-        replicas.append(rep)
+            g["layers"].append(lay)
+            g["packed"].append(p)
+            g["ys"].append(torch.empty((lay.M, lay.N), dtype=torch.bfloat16, device=dev))
+            g["wss"].append(p.workspace(lay.M))
+        replicas.append(groups)
+
+    def run_group(g, stages):
+        lay0, ps = g["layers"][0], g["packed"]
+        B.asp_forward_group_stages(
+            stages, [g["x"]] * len(ps), B.DTYPES[lay0.x_dtype], lay0.M, lay0.K, lay0.r,
+            [p.prep for p in ps], [p.w_codes for p in ps], [p.w_scales for p in ps],
+            [p.wv for p in ps] if lay0.r else None, [p.bias for p in ps], [p.N for p in ps],
+            g["ys"], B.DTYPES[y_dtype], g["wss"], [w.numel() for w in g["wss"]])
 
     def step(i):
-        for lay, p, x, y, ws in replicas[i % R]:
-            p.forward(x, y_dtype, workspace=ws, y=y)
+        for g in replicas[i % R]:
+            run_group(g, 7)
 
     # ---- warm-up, then K steps from one graph
     for i in range(args.warmup):
@@ -238,73 +258,50 @@ def main():
                      for l, _, _ in host)
     tflops = flops_step / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-kernel durations: each kernel alone, nk launches cycling through
-    # the replicas, replayed from a graph of its own between two events on the
-    # launch stream (graph replay keeps host launch cost out of the figure)
+    # ---- per-kernel durations: each kernel alone (asp_forward_group_stages),
+    # nk steps' worth of its launches cycling through the replicas, replayed
+    # from a graph of its own between two events on the launch stream (graph
+    # replay keeps host launch cost out of the figure).  The u stage goes
+    # first, so the quantise stage and then the GEMM read valid partial sums
+    # and codes.
     nk = max(1, min(args.kernel_timing_steps, args.steps))
-    up = lambda b: (b + 255) // 256 * 256
-    launches = []
-    for i in range(nk):
-        for lay, p, x, y, ws in replicas[i % R]:
-            M, N, K, r = lay.M, lay.N, lay.K, lay.r
-            xc = ws[: M * K // 2]
-            off = up(M * K // 2)
-            xs = ws[off: off + M * K // 16]
-            off2 = off + up(M * K // 16)
-            u = ws[off2: off2 + 4 * M * r].view(torch.float32) if r else None
-            scratch = ws[off2 + up(4 * M * r):]
-            launches.append((lay, p, x, y, xc, xs, u, scratch))
 
-    def prep_u_launch(lay, p, x, y, xc, xs, u, scratch):
-        B.asp_act_prep_u(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, scratch,
-                         scratch.numel())
-
-    def prep_q_launch(lay, p, x, y, xc, xs, u, scratch):
-        B.asp_act_prep_q(x, B.DTYPES[lay.x_dtype], lay.M, lay.K, lay.r, p.prep, xc, xs, u, None,
-                         scratch, scratch.numel())
-
-    def gemm_launch(lay, p, x, y, xc, xs, u, scratch):
-        B.asp_gemm_lowrank(xc, xs, u, lay.M, lay.N, lay.K, lay.r, p.w_codes, p.w_scales, p.wv,
-                           p.bias, y, B.DTYPES[y_dtype])
-
-    def graph_ms(fn, sel):
-        todo = [a for a in launches if sel(a[0])]
-        for a in todo[: len(layers)]:  # warm the code path outside the capture
-            fn(*a)
+    def graph_ms(stages, sel):
+        todo = [g for i in range(nk) for g in replicas[i % R] if sel(g)]
+        for g in todo[: len(group_keys)]:  # warm the code path outside the capture
+            run_group(g, stages)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for a in todo:
-                fn(*a)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for g in todo:
+                run_group(g, stages)
         torch.cuda.synchronize()
         ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ea.record(stream)
-        g.replay()
+        gr.replay()
         eb.record(stream)
         torch.cuda.synchronize()
-        return ea.elapsed_time(eb), len(todo)
+        return ea.elapsed_time(eb), todo
 
-    # the three kernels of the path, each over the launches that run it (the u
-    # stage launches nothing for a rank-0 layer); the u stage goes first so the
-    # quantise stage and then the GEMM read valid partial sums and codes
     xbytes = lambda l: 2 if l.x_dtype == "bf16" else 4
-    gemm_names = sorted({B.asp_gemm_kernel_name(l.M, l.N, l.K) for l, _, _ in host})
+    gemm_names = sorted({B.asp_gemm_kernel_name(g["layers"][0].M, sum(l.N for l in g["layers"]),
+                                                g["layers"][0].K) for g in replicas[0]})
     kernels = [
-        ("k_prep_u", "k_prep_u", prep_u_launch, lambda l: l.r > 0,
+        ("k_prep_u", "k_prep_u", 1, lambda g: g["layers"][0].r > 0,
          lambda l: prep_u_bytes(l.M, l.K, l.r, xbytes(l)), lambda l: prep_u_flops(l.M, l.K, l.r)),
-        ("k_prep_q", "k_prep_q", prep_q_launch, lambda l: True,
+        ("k_prep_q", "k_prep_q", 2, lambda g: True,
          lambda l: prep_q_bytes(l.M, l.K, l.r, xbytes(l)), lambda l: prep_q_flops(l.M, l.K, l.r)),
-        (" + ".join(gemm_names), "k_gemm", gemm_launch, lambda l: True,
+        (" + ".join(gemm_names), "k_gemm", 4, lambda g: True,
          lambda l: gemm_bytes(l.M, l.N, l.K, l.r, yb), lambda l: gemm_flops(l.M, l.N, l.K, l.r)),
     ]
     timed = []
-    for name, family, fn, sel, fb, ff in kernels:
-        if not any(sel(a[0]) for a in launches):
+    for name, family, stages, sel, fb, ff in kernels:
+        if not any(sel(g) for g in replicas[0]):
             continue
-        ms, n = graph_ms(fn, sel)
-        nbytes = sum(fb(a[0]) for a in launches if sel(a[0]))
-        nflops = sum(ff(a[0]) for a in launches if sel(a[0]))
-        timed.append((name, family, ms, n, nbytes, nflops))
+        ms, todo = graph_ms(stages, sel)
+        nbytes = sum(fb(l) for g in todo for l in g["layers"])
+        nflops = sum(ff(l) for g in todo for l in g["layers"])
+        timed.append((name, family, ms, len(todo), nbytes, nflops))
     name, family, ms, n_launch, nbytes, nflops = max(timed, key=lambda k: k[2])
     roof, gbs, tfs = roofline_of(nbytes, nflops, ms)
     roof.update({
@@ -348,6 +345,7 @@ def main():
             "flops_per_step": flops_step,
             "algorithmic_bytes_per_step": bytes_step,
             "effective_GBps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+            "groups": [[l.name for l in g["layers"]] for g in replicas[0]],
             "replicas": R,
             "replica_bytes": per,
             "timing": "one HIP graph of K steps, events on the capture stream",

@@ -247,6 +247,55 @@ int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N,
                     int32_t y_dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Several layers that share M, K and r (for example projections that read
+ * the same input) in one call: each of the three kernels is launched once
+ * for the whole group, so small layers fill more of the GPU and share the
+ * launch cost.  Layer i computes exactly what asp_forward computes with
+ * x[i], prep_pack[i], w_codes[i], w_scales[i], wv[i], bias[i], N[i], y[i]
+ * and workspace[i]; the GEMM kernel is chosen for the group's total width
+ * sum(N), so the float32 accumulation order of a layer can differ from a
+ * lone asp_forward call when that choice differs (asp_gemm_kernel_name(M,
+ * sum(N), K) names it).
+ *   n_layers          1..8
+ *   x .. workspace    host arrays of n_layers device pointers (x[i] may
+ *                     repeat); bias may be NULL (no bias anywhere) and so
+ *                     may its entries; wv may be NULL when r == 0
+ *   N                 host array of n_layers output widths
+ *   workspace_bytes   host array; each at least asp_workspace_bytes(M,
+ *                     N[i], K, r), each workspace 256-byte aligned; the
+ *                     workspaces must not overlap
+ * Errors as asp_forward; nothing is enqueued unless every layer validates.
+ */
+int32_t asp_forward_group(int32_t n_layers, const void* const* x,
+                          int32_t x_dtype, int64_t M, int64_t K, int32_t r,
+                          const uint8_t* const* prep_pack,
+                          const uint8_t* const* w_codes,
+                          const uint8_t* const* w_scales,
+                          const uint16_t* const* wv, const float* const* bias,
+                          const int64_t* N, void* const* y, int32_t y_dtype,
+                          void* const* workspace,
+                          const size_t* workspace_bytes, void* stream);
+
+/*
+ * asp_forward_group one kernel at a time (for profiling each launch on its
+ * own): stages is a bit mask of 1 = k_prep_u (the partial sums of u), 2 =
+ * k_prep_q (codes, scales, u), 4 = the GEMM; 7 is asp_forward_group.  Each
+ * stage reads what the earlier ones left in the workspaces, so they must run
+ * in that order on one stream with the same arguments.
+ */
+int32_t asp_forward_group_stages(int32_t stages, int32_t n_layers,
+                                 const void* const* x, int32_t x_dtype,
+                                 int64_t M, int64_t K, int32_t r,
+                                 const uint8_t* const* prep_pack,
+                                 const uint8_t* const* w_codes,
+                                 const uint8_t* const* w_scales,
+                                 const uint16_t* const* wv,
+                                 const float* const* bias, const int64_t* N,
+                                 void* const* y, int32_t y_dtype,
+                                 void* const* workspace,
+                                 const size_t* workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,6 +152,41 @@ def test_forward_workspace_and_alignment_checks():
     assert "wv" in B.asp_last_error()
 
 
+def test_forward_group_validation():
+    lib = B.lib()
+    need = B.asp_workspace_bytes(8, 64, 256, 32)
+    P = ctypes.c_void_p
+
+    def grp(n, N=(64, 48), ws=(FAKE, FAKE + 4096), nb=None, wv=True, K=256, x_dtype=1, arrays=True):
+        m = len(N)
+        arr = lambda vals: (P * m)(*vals)
+        nb = nb or (need, need)
+        return lib.asp_forward_group(
+            n, arr([FAKE] * m) if arrays else None, x_dtype, 8, K, 32, arr([FAKE] * m),
+            arr([FAKE] * m), arr([FAKE] * m), arr([FAKE] * m) if wv else None, None,
+            (ctypes.c_int64 * m)(*N), arr([FAKE] * m), 0, arr(list(ws)),
+            (ctypes.c_size_t * m)(*nb), None)
+
+    assert grp(0) == 1 and "n_layers" in B.asp_last_error()
+    assert grp(9, N=(64,) * 9, ws=(FAKE,) * 9, nb=(need,) * 9) == 1
+    assert grp(2, arrays=False) == 1
+    assert grp(2, wv=False) == 1           # r > 0 needs the wv array
+    assert grp(2, K=100) == 2
+    assert grp(2, x_dtype=7) == 1
+    assert grp(2, N=(64, 0)) == 2
+    assert grp(2, ws=(FAKE, FAKE + 16)) == 3
+    assert "layer 1" in B.asp_last_error()
+    assert grp(2, nb=(need, need - 1)) == 5
+    st = lib.asp_forward_group_stages(8, 1, None, 1, 8, 256, 32, None, None, None, None, None,
+                                      None, None, 0, None, None, None)
+    assert st == 1 and "stages" in B.asp_last_error()
+    # an empty batch validates shapes only and enqueues nothing
+    assert lib.asp_forward_group(1, (P * 1)(None), 1, 0, 256, 32, (P * 1)(None), (P * 1)(None),
+                                 (P * 1)(None), (P * 1)(None), None, (ctypes.c_int64 * 1)(64),
+                                 (P * 1)(None), 0, (P * 1)(None), (ctypes.c_size_t * 1)(0),
+                                 None) == 0
+
+
 def test_host_quantizer_validation():
     a = np.zeros((2, 24), np.float32)
     with pytest.raises(B.ASPError):

@@ -16,6 +16,8 @@ Gates (derived in the design notes):
   but those rare boundary decisions is checked at accumulation precision.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,7 @@ from oracle import asp as OA
 from oracle import formats as OF
 from wam_asp_w4a4_amd import binding as B
 from wam_asp_w4a4_amd import synth
-from wam_asp_w4a4_amd.layer import PackedLayer
+from wam_asp_w4a4_amd.layer import PackedLayer, forward_group
 
 from test_host_packer import e4m3_tie_blocks, element_tie_blocks
 from test_oracle_formats import _load_golden
@@ -334,3 +336,49 @@ def test_row_independence_bitwise():
     rows = [3, 100, 255, 17, 128]
     part = host(p.forward(x[rows].contiguous(), "f32"))
     assert np.array_equal(full[rows], part)
+
+
+# ------------------------------------------------------------- grouped layers
+
+
+def _rne_bf16(a):
+    """bf16 bit patterns of finite float32 values, rounded to nearest even."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _group_layers(M, K, r, Ns, dtype, seed):
+    """Layers of one K and rank that read the same input (the first one's x)."""
+    lays = [synth.make_layer(f"g{i}", M, K, N, r, seed=seed + i, dtype=dtype)
+            for i, N in enumerate(Ns)]
+    return [dataclasses.replace(l, x=lays[0].x) for l in lays]
+
+
+@pytest.mark.parametrize("M,K,r,Ns,dtype", [
+    (256, 1024, 32, (1024, 1024), "bf16"),        # the action-expert attention pair
+    (37, 384, 33, (200, 48, 16), "f32"),          # ragged widths, odd rank
+    (1024, 512, 32, (128,) * 8, "bf16"),          # the group's width picks a larger tile
+    (64, 256, 0, (64, 96), "bf16"),               # rank 0
+])
+def test_forward_group(M, K, r, Ns, dtype):
+    """Each layer of a grouped call against the float64 oracle (fp32 output,
+    the 2e-3 gate) and against a lone asp_forward call; the bf16 output is the
+    round-to-nearest-even cast of the fp32 one, bit for bit (the same
+    accumulators, only the store differs)."""
+    lays = _group_layers(M, K, r, Ns, dtype, seed=M + K + r)
+    packed = [PackedLayer.pack(l.w, l.s, l.v, l.b, DEV) for l in lays]
+    x = x_device(lays[0])
+    y32 = [host(y) for y in forward_group(packed, x, "f32")]
+    y16 = [host(y.float()) for y in forward_group(packed, x, "bf16")]
+    same_kernel = (B.asp_gemm_kernel_name(M, sum(Ns), K) == B.asp_gemm_kernel_name(M, Ns[0], K))
+    for lay, p, a, b in zip(lays, packed, y32, y16):
+        want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
+        e = rel_fro(a, want)
+        print(f"group {Ns} {lay.name}: rel err fp32 {e:.3e}, bf16 {rel_fro(b, want):.3e}")
+        assert e <= 2e-3
+        assert np.array_equal(_rne_bf16(a), (b.view(np.uint32) >> 16).astype(np.uint16))
+        alone = host(p.forward(x, "f32"))
+        if same_kernel:
+            assert np.array_equal(a, alone)        # one launch or several: the same bits
+        else:
+            assert rel_fro(a, alone) <= 1e-5       # only the float32 summation order differs

@@ -47,6 +47,10 @@ SIGNATURES = {
     "asp_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
     "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32,
                            _p, _sz, _p]),
+    "asp_forward_group": (_i32, [_i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p,
+                                 _i32, _p, _p, _p]),
+    "asp_forward_group_stages": (_i32, [_i32, _i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p,
+                                        _p, _p, _p, _i32, _p, _p, _p]),
 }
 
 _lib = None
@@ -198,6 +202,40 @@ def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bi
     _check(lib().asp_gemm_lowrank(_ptr(x_codes), _ptr(x_scales), _ptr(u), M, N, K, r,
                                   _ptr(w_codes), _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y),
                                   y_dtype, _stream(stream, y)))
+
+
+def _ptr_array(items):
+    """A host array of device pointers (NULL entries for None); None for a None list."""
+    if items is None:
+        return None, None
+    arr = (ctypes.c_void_p * len(items))(*[_ptr(a) for a in items])
+    return arr, ctypes.cast(arr, ctypes.c_void_p).value
+
+
+def asp_forward_group(x, x_dtype, M, K, r, prep_pack, w_codes, w_scales, wv, bias, N, y, y_dtype,
+                      workspace, workspace_bytes, stream=None):
+    """Per-layer arguments are equal-length lists (bias and wv may be None)."""
+    asp_forward_group_stages(7, x, x_dtype, M, K, r, prep_pack, w_codes, w_scales, wv, bias, N, y,
+                             y_dtype, workspace, workspace_bytes, stream)
+
+
+def asp_forward_group_stages(stages, x, x_dtype, M, K, r, prep_pack, w_codes, w_scales, wv, bias,
+                             N, y, y_dtype, workspace, workspace_bytes, stream=None):
+    n = len(y)
+    keep = []  # the ctypes arrays must outlive the call
+
+    def arr(items):
+        a, p = _ptr_array(items)
+        keep.append(a)
+        return p
+
+    nn = (ctypes.c_int64 * n)(*N)
+    nb = (ctypes.c_size_t * n)(*workspace_bytes)
+    keep += [nn, nb]
+    _check(lib().asp_forward_group_stages(
+        stages, n, arr(x), x_dtype, M, K, r, arr(prep_pack), arr(w_codes), arr(w_scales), arr(wv),
+        arr(bias), ctypes.cast(nn, ctypes.c_void_p).value, arr(y), y_dtype, arr(workspace),
+        ctypes.cast(nb, ctypes.c_void_p).value, _stream(stream, *y)))
 
 
 def asp_forward(x, x_dtype, M, N, K, r, prep_pack, w_codes, w_scales, wv, bias, y, y_dtype,

@@ -125,17 +125,41 @@ inline int32_t check_mk(int64_t M, int64_t K) {
   return ASP_OK;
 }
 
-// Internal launchers (validate, then enqueue on `stream`).
+// Internal launchers (validate, then enqueue on `stream`).  A call covers one
+// layer or a group of up to kMaxGroup layers with the same M, K, r and dtypes:
+// each launch then spans every layer of the group (one more grid dimension),
+// so small layers fill more of the chip and pay one launch between them.
+constexpr int kMaxGroup = 8;
+
+struct PrepCall {
+  const void* x;
+  const uint8_t* prep_pack;
+  uint8_t* x_codes;
+  uint8_t* x_scales;
+  float* u;
+  float* prequant;
+  void* scratch;  // the partial sums of u
+  size_t scratch_bytes;
+};
+
+struct GemmCall {
+  const uint8_t* x_codes;
+  const uint8_t* x_scales;
+  const float* u;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const uint16_t* wv;
+  const float* bias;
+  void* y;
+  int64_t N;
+};
+
 size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r);
 // stages: 1 = partial sums of u (k_prep_u), 2 = the rest (k_prep_q), 3 = both
-int32_t act_prep_impl(int stages, const void* x, int32_t x_dtype, int64_t M, int64_t K,
-                      int32_t r, const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales,
-                      float* u, float* prequant, void* scratch, size_t scratch_bytes,
-                      hipStream_t stream);
+int32_t act_prep_impl(int stages, int n, const PrepCall* calls, int32_t x_dtype, int64_t M,
+                      int64_t K, int32_t r, hipStream_t stream);
 int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype);
-int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
-                  int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
-                  const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
-                  int32_t y_dtype, hipStream_t stream);
+int32_t gemm_impl(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r, int32_t y_dtype,
+                  hipStream_t stream);
 
 }  // namespace asp

@@ -1,7 +1,8 @@
 // The whole deflated-ASP NVFP4 layer: activation prep then the 4-bit GEMM
 // with its low-rank/bias epilogue, enqueued on one stream, with the
 // activation codes, scales, u and the prep's partial sums of u in the caller's
-// workspace.
+// workspace.  A group of layers with the same M, K and r (for example the
+// projections that read one input) runs as one launch per kernel.
 #include "asp_device.h"
 
 namespace asp {
@@ -39,34 +40,67 @@ int32_t asp_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, size_t* 
   return ASP_OK;
 }
 
+int32_t asp_forward_group_stages(int32_t stages, int32_t n_layers, const void* const* x,
+                                 int32_t x_dtype, int64_t M, int64_t K, int32_t r,
+                                 const uint8_t* const* prep_pack, const uint8_t* const* w_codes,
+                                 const uint8_t* const* w_scales, const uint16_t* const* wv,
+                                 const float* const* bias, const int64_t* N, void* const* y,
+                                 int32_t y_dtype, void* const* workspace,
+                                 const size_t* workspace_bytes, void* stream) {
+  clear_error();
+  if (stages < 1 || stages > 7) return fail(ASP_ERR_ARG, "stages=%d outside [1, 7]", stages);
+  if (n_layers < 1 || n_layers > kMaxGroup)
+    return fail(ASP_ERR_ARG, "n_layers=%d outside [1, %d]", n_layers, kMaxGroup);
+  if (!x || !prep_pack || !w_codes || !w_scales || !N || !y || !workspace || !workspace_bytes ||
+      (r > 0 && !wv))
+    return fail(ASP_ERR_ARG, "a per-layer array is NULL");
+  if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
+  for (int i = 0; i < n_layers; ++i) ASP_TRY(gemm_check(M, N[i], K, r, y_dtype));
+  if (M == 0) return ASP_OK;
+  const WsLayout L = ws_layout(M, K, r);
+  PrepCall pc[kMaxGroup];
+  GemmCall gc[kMaxGroup];
+  for (int i = 0; i < n_layers; ++i) {
+    if (!workspace[i]) return fail(ASP_ERR_ARG, "workspace of layer %d is NULL", i);
+    if (((uintptr_t)workspace[i] & 255u) != 0)
+      return fail(ASP_ERR_ALIGN, "workspace of layer %d must be 256-byte aligned", i);
+    if (workspace_bytes[i] < L.total)
+      return fail(ASP_ERR_WORKSPACE, "workspace of layer %d: %zu bytes, need %zu", i,
+                  workspace_bytes[i], L.total);
+    uint8_t* base = static_cast<uint8_t*>(workspace[i]);
+    float* u = r > 0 ? reinterpret_cast<float*>(base + L.u) : nullptr;
+    pc[i] = {x[i], prep_pack[i], base + L.codes, base + L.scales, u, nullptr, base + L.scratch,
+             L.total - L.scratch};
+    gc[i] = {base + L.codes, base + L.scales, u, w_codes[i], w_scales[i], r > 0 ? wv[i] : nullptr,
+             bias ? bias[i] : nullptr, y[i], N[i]};
+    // validate the GEMM's own pointers before enqueuing anything
+    ASP_TRY(check_ptr(gc[i].w_codes, "w_codes", true));
+    ASP_TRY(check_ptr(gc[i].w_scales, "w_scales", true));
+    ASP_TRY(check_ptr(gc[i].wv, "wv", r > 0));
+    ASP_TRY(check_ptr(gc[i].bias, "bias", false));
+    ASP_TRY(check_ptr(gc[i].y, "y", true));
+  }
+  if (stages & 3) ASP_TRY(act_prep_impl(stages & 3, n_layers, pc, x_dtype, M, K, r, (hipStream_t)stream));
+  if (stages & 4) return gemm_impl(n_layers, gc, M, K, r, y_dtype, (hipStream_t)stream);
+  return ASP_OK;
+}
+
+int32_t asp_forward_group(int32_t n_layers, const void* const* x, int32_t x_dtype, int64_t M,
+                          int64_t K, int32_t r, const uint8_t* const* prep_pack,
+                          const uint8_t* const* w_codes, const uint8_t* const* w_scales,
+                          const uint16_t* const* wv, const float* const* bias, const int64_t* N,
+                          void* const* y, int32_t y_dtype, void* const* workspace,
+                          const size_t* workspace_bytes, void* stream) {
+  return asp_forward_group_stages(7, n_layers, x, x_dtype, M, K, r, prep_pack, w_codes, w_scales,
+                                  wv, bias, N, y, y_dtype, workspace, workspace_bytes, stream);
+}
+
 int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N, int64_t K, int32_t r,
                     const uint8_t* prep_pack, const uint8_t* w_codes, const uint8_t* w_scales,
                     const uint16_t* wv, const float* bias, void* y, int32_t y_dtype,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
-  ASP_TRY(gemm_check(M, N, K, r, y_dtype));
-  if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
-  if (M == 0) return ASP_OK;
-  const WsLayout L = ws_layout(M, K, r);
-  if (!workspace) return fail(ASP_ERR_ARG, "workspace is NULL");
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(ASP_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(ASP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
-  // validate the GEMM's own pointers before enqueuing anything
-  ASP_TRY(check_ptr(w_codes, "w_codes", true));
-  ASP_TRY(check_ptr(w_scales, "w_scales", true));
-  ASP_TRY(check_ptr(wv, "wv", r > 0));
-  ASP_TRY(check_ptr(bias, "bias", false));
-  ASP_TRY(check_ptr(y, "y", true));
-  uint8_t* base = static_cast<uint8_t*>(workspace);
-  uint8_t* xc = base + L.codes;
-  uint8_t* xs = base + L.scales;
-  float* u = r > 0 ? reinterpret_cast<float*>(base + L.u) : nullptr;
-  ASP_TRY(act_prep_impl(3, x, x_dtype, M, K, r, prep_pack, xc, xs, u, nullptr, base + L.scratch,
-                        L.total - L.scratch, (hipStream_t)stream));
-  return gemm_impl(xc, xs, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
-                   (hipStream_t)stream);
+  return asp_forward_group(1, &x, x_dtype, M, K, r, &prep_pack, &w_codes, &w_scales, &wv, &bias,
+                           &N, &y, y_dtype, &workspace, &workspace_bytes, stream);
 }
 
 }  // extern "C"

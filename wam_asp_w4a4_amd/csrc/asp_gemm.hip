@@ -26,6 +26,8 @@
 // bytes are converted to fp16 once, when a stage is written to LDS.
 #include "asp_device.h"
 
+#include <algorithm>
+
 namespace asp {
 namespace {
 
@@ -80,12 +82,14 @@ __device__ __forceinline__ uint32_t scale_pair_f16(uint32_t w) {
 }
 
 template <int WM, int WN, int TM, int TN>
-__global__ void __launch_bounds__(WM * WN * 64)
-    k_gemm(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-           const float* __restrict__ u, int M, int N, int K, int r,
-           const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-           const uint16_t* __restrict__ wv, const float* __restrict__ bias, void* __restrict__ y,
-           int y_bf16, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
+                                          const uint8_t* __restrict__ xs,
+                                          const float* __restrict__ u, int M, int N, int K, int r,
+                                          const uint8_t* __restrict__ wc,
+                                          const uint8_t* __restrict__ ws,
+                                          const uint16_t* __restrict__ wv,
+                                          const float* __restrict__ bias, void* __restrict__ y,
+                                          int y_bf16, int tiles_m, int tiles_n) {
   using C = Cfg<WM, WN, TM, TN>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -345,17 +349,63 @@ __global__ void __launch_bounds__(WM * WN * 64)
   }
 }
 
+// Per-layer pointers of a (grouped) launch; layer = blockIdx.y.  A layer
+// with fewer tiles than the grid's x extent leaves the rest idle.
+struct GemmLayerArgs {
+  const uint8_t* xc;
+  const uint8_t* xs;
+  const float* u;
+  const uint8_t* wc;
+  const uint8_t* ws;
+  const uint16_t* wv;
+  const float* bias;
+  void* y;
+  int N;
+  int tiles_n;
+};
+
+struct GemmArgs {
+  GemmLayerArgs l[kMaxGroup];
+};
+
 template <int WM, int WN, int TM, int TN>
-int32_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const float* u, int64_t M, int64_t N,
-                    int64_t K, int32_t r, const uint8_t* wc, const uint8_t* wsc, const uint16_t* wv,
-                    const float* bias, void* y, int32_t y_dtype, hipStream_t stream) {
+__global__ void __launch_bounds__(WM * WN * 64)
+    k_gemm(const GemmArgs a, int M, int K, int r, int y_bf16, int tiles_m) {
+  const GemmLayerArgs& L = a.l[blockIdx.y];
+  if ((int)blockIdx.x >= tiles_m * L.tiles_n) return;
+  gemm_body<WM, WN, TM, TN>(L.xc, L.xs, L.u, M, L.N, K, r, L.wc, L.ws, L.wv, L.bias, L.y, y_bf16,
+                            tiles_m, L.tiles_n);
+}
+
+// The grid's x extent: the largest layer's tile count; every layer's count
+// must fit an int.
+inline int32_t group_args(int n, const GemmCall* calls, int64_t M, int BM, int BN, GemmArgs& a,
+                          int64_t& tiles_m, int64_t& max_tiles) {
+  tiles_m = (M + BM - 1) / BM;
+  max_tiles = 0;
+  a = GemmArgs{};
+  for (int i = 0; i < n; ++i) {
+    const int64_t tn = (calls[i].N + BN - 1) / BN;
+    if (tiles_m * tn > INT32_MAX)
+      return fail(ASP_ERR_SHAPE, "M=%lld N=%lld too large for one launch", (long long)M,
+                  (long long)calls[i].N);
+    max_tiles = std::max(max_tiles, tiles_m * tn);
+    a.l[i] = {calls[i].x_codes, calls[i].x_scales, calls[i].u, calls[i].w_codes,
+              calls[i].w_scales, calls[i].wv, calls[i].bias, calls[i].y, (int)calls[i].N, (int)tn};
+  }
+  return ASP_OK;
+}
+
+template <int WM, int WN, int TM, int TN>
+int32_t launch_gemm(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r, int32_t y_dtype,
+                    hipStream_t stream) {
   using C = Cfg<WM, WN, TM, TN>;
-  const int64_t tiles_m = (M + C::BM - 1) / C::BM, tiles_n = (N + C::BN - 1) / C::BN;
-  if (tiles_m * tiles_n > INT32_MAX)
-    return fail(ASP_ERR_SHAPE, "M=%lld N=%lld too large for one launch", (long long)M, (long long)N);
-  hipLaunchKernelGGL((k_gemm<WM, WN, TM, TN>), dim3((unsigned)(tiles_m * tiles_n)), dim3(C::NT), 0,
-                     stream, xc, xs, u, (int)M, (int)N, (int)K, (int)r, wc, wsc, wv, bias, y,
-                     (int)(y_dtype == ASP_BF16), (int)tiles_m, (int)tiles_n);
+  GemmArgs a;
+  int64_t tiles_m, max_tiles;
+  ASP_TRY(group_args(n, calls, M, C::BM, C::BN, a, tiles_m, max_tiles));
+  hipLaunchKernelGGL((k_gemm<WM, WN, TM, TN>), dim3((unsigned)max_tiles, (unsigned)n), dim3(C::NT),
+                     0, stream, a, (int)M, (int)K, (int)r, (int)(y_dtype == ASP_BF16),
+                     (int)tiles_m);
   return launch_status("gemm");
 }
 
@@ -375,12 +425,14 @@ int32_t launch_gemm(const uint8_t* xc, const uint8_t* xs, const float* u, int64_
 // use the same mapping, so every product pairs equal K indices, and a lane's 8
 // values of a K-step share one block scale.
 template <int FM, int FN, int W>
-__global__ void __launch_bounds__(W * 64)
-    k_gemm_sk(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs,
-              const float* __restrict__ u, int M, int N, int K, int r,
-              const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-              const uint16_t* __restrict__ wv, const float* __restrict__ bias,
-              void* __restrict__ y, int y_bf16, int tiles_n) {
+__device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
+                                             const uint8_t* __restrict__ xs,
+                                             const float* __restrict__ u, int M, int N, int K,
+                                             int r, const uint8_t* __restrict__ wc,
+                                             const uint8_t* __restrict__ ws,
+                                             const uint16_t* __restrict__ wv,
+                                             const float* __restrict__ bias,
+                                             void* __restrict__ y, int y_bf16, int tiles_n) {
   constexpr int BM = 32 * FM, BN = 32 * FN, NF = FM + FN;
   constexpr int CH = 4;                      // groups of 64 K per register chunk
   constexpr int EPT = BM * BN / (W * 64);    // output elements per thread
@@ -545,16 +597,23 @@ int sk_waves(int64_t K) {
 }
 
 template <int FM, int FN, int W>
-int32_t launch_gemm_sk(const uint8_t* xc, const uint8_t* xs, const float* u, int64_t M, int64_t N,
-                       int64_t K, int32_t r, const uint8_t* wc, const uint8_t* wsc,
-                       const uint16_t* wv, const float* bias, void* y, int32_t y_dtype,
-                       hipStream_t stream) {
-  const int64_t tiles_m = (M + 32 * FM - 1) / (32 * FM), tiles_n = (N + 32 * FN - 1) / (32 * FN);
-  if (tiles_m * tiles_n > INT32_MAX)
-    return fail(ASP_ERR_SHAPE, "M=%lld N=%lld too large for one launch", (long long)M, (long long)N);
-  hipLaunchKernelGGL((k_gemm_sk<FM, FN, W>), dim3((unsigned)(tiles_m * tiles_n)), dim3(W * 64), 0,
-                     stream, xc, xs, u, (int)M, (int)N, (int)K, (int)r, wc, wsc, wv, bias, y,
-                     (int)(y_dtype == ASP_BF16), (int)tiles_n);
+__global__ void __launch_bounds__(W * 64)
+    k_gemm_sk(const GemmArgs a, int M, int K, int r, int y_bf16, int tiles_m) {
+  const GemmLayerArgs& L = a.l[blockIdx.y];
+  if ((int)blockIdx.x >= tiles_m * L.tiles_n) return;
+  gemm_sk_body<FM, FN, W>(L.xc, L.xs, L.u, M, L.N, K, r, L.wc, L.ws, L.wv, L.bias, L.y, y_bf16,
+                          L.tiles_n);
+}
+
+template <int FM, int FN, int W>
+int32_t launch_gemm_sk(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r,
+                       int32_t y_dtype, hipStream_t stream) {
+  GemmArgs a;
+  int64_t tiles_m, max_tiles;
+  ASP_TRY(group_args(n, calls, M, 32 * FM, 32 * FN, a, tiles_m, max_tiles));
+  hipLaunchKernelGGL((k_gemm_sk<FM, FN, W>), dim3((unsigned)max_tiles, (unsigned)n), dim3(W * 64),
+                     0, stream, a, (int)M, (int)K, (int)r, (int)(y_dtype == ASP_BF16),
+                     (int)tiles_m);
   return launch_status("gemm_sk");
 }
 
@@ -601,39 +660,34 @@ const char* gemm_variant_name(GemmVariant v) {
   }
 }
 
-int32_t gemm_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* u, int64_t M,
-                  int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
-                  const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
-                  int32_t y_dtype, hipStream_t stream) {
-  ASP_TRY(gemm_check(M, N, K, r, y_dtype));
+int32_t gemm_impl(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r, int32_t y_dtype,
+                  hipStream_t stream) {
+  if (n < 1 || n > kMaxGroup) return fail(ASP_ERR_ARG, "group of %d layers outside [1, %d]", n, kMaxGroup);
+  int64_t n_total = 0;
+  for (int i = 0; i < n; ++i) {
+    ASP_TRY(gemm_check(M, calls[i].N, K, r, y_dtype));
+    n_total += calls[i].N;
+  }
   if (M == 0) return ASP_OK;
-  ASP_TRY(check_ptr(x_codes, "x_codes", true));
-  ASP_TRY(check_ptr(x_scales, "x_scales", true));
-  ASP_TRY(check_ptr(u, "u", r > 0));
-  ASP_TRY(check_ptr(w_codes, "w_codes", true));
-  ASP_TRY(check_ptr(w_scales, "w_scales", true));
-  ASP_TRY(check_ptr(wv, "wv", r > 0));
-  ASP_TRY(check_ptr(bias, "bias", false));
-  ASP_TRY(check_ptr(y, "y", true));
-  switch (gemm_variant(M, N, K)) {
-    case kGemm256x192:
-      return launch_gemm<4, 2, 2, 3>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
-    case kGemm64x64:
-      return launch_gemm<2, 2, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
-    case kGemmSplitK8:
-      return launch_gemm_sk<1, 1, 8>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
-    case kGemmSplitK4:
-      return launch_gemm_sk<1, 1, 4>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
-    case kGemmSplitK2:
-      return launch_gemm_sk<1, 1, 2>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
-    default:
-      return launch_gemm_sk<1, 1, 1>(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv,
-                                     bias, y, y_dtype, stream);
+  for (int i = 0; i < n; ++i) {
+    const GemmCall& c = calls[i];
+    ASP_TRY(check_ptr(c.x_codes, "x_codes", true));
+    ASP_TRY(check_ptr(c.x_scales, "x_scales", true));
+    ASP_TRY(check_ptr(c.u, "u", r > 0));
+    ASP_TRY(check_ptr(c.w_codes, "w_codes", true));
+    ASP_TRY(check_ptr(c.w_scales, "w_scales", true));
+    ASP_TRY(check_ptr(c.wv, "wv", r > 0));
+    ASP_TRY(check_ptr(c.bias, "bias", false));
+    ASP_TRY(check_ptr(c.y, "y", true));
+  }
+  // one kernel for the whole group, chosen for its total output width
+  switch (gemm_variant(M, n_total, K)) {
+    case kGemm256x192: return launch_gemm<4, 2, 2, 3>(n, calls, M, K, r, y_dtype, stream);
+    case kGemm64x64: return launch_gemm<2, 2, 1, 1>(n, calls, M, K, r, y_dtype, stream);
+    case kGemmSplitK8: return launch_gemm_sk<1, 1, 8>(n, calls, M, K, r, y_dtype, stream);
+    case kGemmSplitK4: return launch_gemm_sk<1, 1, 4>(n, calls, M, K, r, y_dtype, stream);
+    case kGemmSplitK2: return launch_gemm_sk<1, 1, 2>(n, calls, M, K, r, y_dtype, stream);
+    default: return launch_gemm_sk<1, 1, 1>(n, calls, M, K, r, y_dtype, stream);
   }
 }
 
@@ -648,8 +702,8 @@ int32_t asp_gemm_lowrank(const uint8_t* x_codes, const uint8_t* x_scales, const 
                          const uint8_t* w_scales, const uint16_t* wv, const float* bias, void* y,
                          int32_t y_dtype, void* stream) {
   clear_error();
-  return gemm_impl(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bias, y, y_dtype,
-                   (hipStream_t)stream);
+  const GemmCall c = {x_codes, x_scales, u, w_codes, w_scales, wv, bias, y, N};
+  return gemm_impl(1, &c, M, K, r, y_dtype, (hipStream_t)stream);
 }
 
 const char* asp_gemm_kernel_name(int64_t M, int64_t N, int64_t K) {

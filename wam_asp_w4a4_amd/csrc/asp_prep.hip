@@ -143,10 +143,10 @@ struct UStage {
 };
 
 template <typename XT, int KS>
-__global__ void __launch_bounds__(256) k_prep_u(const XT* __restrict__ x, int M, int K, int r,
-                                                    const uint16_t* __restrict__ vth,
-                                                    const uint16_t* __restrict__ vtl,
-                                                    float* __restrict__ u_part, int bps) {
+__device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int K, int r,
+                                            const uint16_t* __restrict__ vth,
+                                            const uint16_t* __restrict__ vtl,
+                                            float* __restrict__ u_part, int bps) {
   using St = UStage<KS>;
   constexpr int RP = St::RP, CT = KS * 2, NC = St::CHUNKS;
   constexpr bool fp32_x = sizeof(XT) == 4;
@@ -255,15 +255,15 @@ __global__ void __launch_bounds__(256) k_prep_u(const XT* __restrict__ x, int M,
 //  quantise:   per block in one lane: amax, E4M3 scale, codes; one 16-byte
 //              code store and one 2-byte scale store per lane.
 template <typename XT, int KS>
-__global__ void __launch_bounds__(256) k_prep_q(const XT* __restrict__ x, int M, int K, int r,
-                                                const float* __restrict__ cvec,
-                                                const uint16_t* __restrict__ vh,
-                                                const uint16_t* __restrict__ vl,
-                                                const float* __restrict__ u_part, int S,
-                                                uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales,
-                                                float* __restrict__ u_out,
-                                                float* __restrict__ pre) {
+__device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int K, int r,
+                                            const float* __restrict__ cvec,
+                                            const uint16_t* __restrict__ vh,
+                                            const uint16_t* __restrict__ vl,
+                                            const float* __restrict__ u_part, int S,
+                                            uint8_t* __restrict__ codes,
+                                            uint8_t* __restrict__ scales,
+                                            float* __restrict__ u_out,
+                                            float* __restrict__ pre) {
   constexpr int RP = KS * 32;
   constexpr int PPR = KS > 0 ? RP / 8 : 1;           // 16-byte pieces per V row
   constexpr int BLK_PIECES = KS > 0 ? 2 * 128 * PPR : 1;
@@ -465,6 +465,41 @@ __global__ void __launch_bounds__(256) k_prep_q(const XT* __restrict__ x, int M,
   }
 }
 
+// Per-layer pointers of a (grouped) launch; layer = blockIdx.z.
+template <typename XT>
+struct PrepLayerArgs {
+  const XT* x;
+  const float* cvec;
+  const uint16_t* vth;
+  const uint16_t* vtl;
+  const uint16_t* vh;
+  const uint16_t* vl;
+  float* u_part;
+  uint8_t* xc;
+  uint8_t* xs;
+  float* u;
+  float* pre;
+};
+
+template <typename XT>
+struct PrepArgs {
+  PrepLayerArgs<XT> l[kMaxGroup];
+};
+
+template <typename XT, int KS>
+__global__ void __launch_bounds__(256) k_prep_u(const PrepArgs<XT> a, int M, int K, int r,
+                                                int bps) {
+  const PrepLayerArgs<XT>& L = a.l[blockIdx.z];
+  prep_u_body<XT, KS>(L.x, M, K, r, L.vth, L.vtl, L.u_part, bps);
+}
+
+template <typename XT, int KS>
+__global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int K, int r,
+                                                int S) {
+  const PrepLayerArgs<XT>& L = a.l[blockIdx.z];
+  prep_q_body<XT, KS>(L.x, M, K, r, L.cvec, L.vh, L.vl, L.u_part, S, L.xc, L.xs, L.u, L.pre);
+}
+
 constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
 
 // Slices of K for the partial sums of u (a function of K only, so a row's u
@@ -477,9 +512,7 @@ void u_slicing(int64_t K, int* S, int* bps) {
 }
 
 template <typename XT, int KS>
-void launch_ks(hipStream_t st, int stages, const XT* x, int M, int K, int r, const float* cvec,
-               const uint16_t* vth, const uint16_t* vtl, const uint16_t* vh, const uint16_t* vl,
-               float* u_part, uint8_t* xc, uint8_t* xs, float* u, float* pre) {
+void launch_ks(hipStream_t st, int stages, int n, const PrepArgs<XT>& a, int M, int K, int r) {
   const int nblk = K / 128;
   const int tiles64 = (M + kPrepRows - 1) / kPrepRows;
   int S = 0, bps = 0;
@@ -492,39 +525,40 @@ void launch_ks(hipStream_t st, int stages, const XT* x, int M, int K, int r, con
       const size_t lds = (size_t)std::min(UStage<KS>::CHUNKS, bps) * UStage<KS>::CHUNK_PIECES * 16;
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prep_u<XT, KS>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S), dim3(256), lds, st,
-                         x, M, K, r, vth, vtl, u_part, bps);
+      hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S, (unsigned)n),
+                         dim3(256), lds, st, a, M, K, r, bps);
     }
   }
   if (stages & kStageQ)
-    hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk), dim3(256), 0,
-                       st, x, M, K, r, cvec, vh, vl, u_part, S, xc, xs, u, pre);
+    hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk, (unsigned)n),
+                       dim3(256), 0, st, a, M, K, r, S);
 }
 
 template <typename XT>
-int32_t launch_prep(int stages, const XT* x, int64_t M, int64_t K, int32_t r, const uint8_t* pack,
-                    uint8_t* x_codes, uint8_t* x_scales, float* u, float* prequant, float* u_part,
+int32_t launch_prep(int stages, int n, const PrepCall* calls, int64_t M, int64_t K, int32_t r,
                     hipStream_t stream) {
-  const PrepPackLayout L = prep_pack_layout(K, r);
-  const float* cvec = reinterpret_cast<const float*>(pack + L.cvec);
-  const uint16_t* vth = reinterpret_cast<const uint16_t*>(pack + L.vt_hi);
-  const uint16_t* vtl = reinterpret_cast<const uint16_t*>(pack + L.vt_lo);
-  const uint16_t* vh = reinterpret_cast<const uint16_t*>(pack + L.v_hi);
-  const uint16_t* vl = reinterpret_cast<const uint16_t*>(pack + L.v_lo);
+  const PrepPackLayout P = prep_pack_layout(K, r);
+  PrepArgs<XT> a = {};
+  for (int i = 0; i < n; ++i) {
+    const uint8_t* pack = calls[i].prep_pack;
+    PrepLayerArgs<XT>& L = a.l[i];
+    L.x = static_cast<const XT*>(calls[i].x);
+    L.cvec = reinterpret_cast<const float*>(pack + P.cvec);
+    L.vth = reinterpret_cast<const uint16_t*>(pack + P.vt_hi);
+    L.vtl = reinterpret_cast<const uint16_t*>(pack + P.vt_lo);
+    L.vh = reinterpret_cast<const uint16_t*>(pack + P.v_hi);
+    L.vl = reinterpret_cast<const uint16_t*>(pack + P.v_lo);
+    L.u_part = static_cast<float*>(calls[i].scratch);
+    L.xc = calls[i].x_codes;
+    L.xs = calls[i].x_scales;
+    L.u = calls[i].u;
+    L.pre = calls[i].prequant;
+  }
   const int Mi = (int)M, Ki = (int)K;
-  switch (L.rp32 / 32) {
-    case 0:
-      launch_ks<XT, 0>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
-                       prequant);
-      break;
-    case 1:
-      launch_ks<XT, 1>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
-                       prequant);
-      break;
-    default:
-      launch_ks<XT, 2>(stream, stages, x, Mi, Ki, r, cvec, vth, vtl, vh, vl, u_part, x_codes, x_scales, u,
-                       prequant);
-      break;
+  switch (P.rp32 / 32) {
+    case 0: launch_ks<XT, 0>(stream, stages, n, a, Mi, Ki, r); break;
+    case 1: launch_ks<XT, 1>(stream, stages, n, a, Mi, Ki, r); break;
+    default: launch_ks<XT, 2>(stream, stages, n, a, Mi, Ki, r); break;
   }
   return launch_status("prep");
 }
@@ -538,34 +572,32 @@ size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r) {
   return (size_t)S * (size_t)M * (size_t)prep_pack_layout(K, r).rp32 * sizeof(float);
 }
 
-int32_t act_prep_impl(int stages, const void* x, int32_t x_dtype, int64_t M, int64_t K,
-                      int32_t r, const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales,
-                      float* u, float* prequant, void* scratch, size_t scratch_bytes,
-                      hipStream_t stream) {
+int32_t act_prep_impl(int stages, int n, const PrepCall* calls, int32_t x_dtype, int64_t M,
+                      int64_t K, int32_t r, hipStream_t stream) {
   ASP_TRY(check_mk(M, K));
   ASP_TRY(check_rank(r));
   if (x_dtype != ASP_F32 && x_dtype != ASP_BF16) return fail(ASP_ERR_ARG, "x_dtype=%d", x_dtype);
+  if (n < 1 || n > kMaxGroup) return fail(ASP_ERR_ARG, "group of %d layers outside [1, %d]", n, kMaxGroup);
   if (M == 0) return ASP_OK;
-  ASP_TRY(check_ptr(x, "x", true));
-  ASP_TRY(check_ptr(prep_pack, "prep_pack", true));
-  if (stages & kStageQ) {
-    ASP_TRY(check_ptr(x_codes, "x_codes", true));
-    ASP_TRY(check_ptr(x_scales, "x_scales", true));
-    ASP_TRY(check_ptr(u, "u", r > 0));
-    ASP_TRY(check_ptr(prequant, "prequant", false));
-  }
   const size_t need = act_prep_scratch_bytes(M, K, r);
-  if (need) {
-    ASP_TRY(check_ptr(scratch, "workspace", true));
-    if (scratch_bytes < need)
-      return fail(ASP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", scratch_bytes, need);
+  for (int i = 0; i < n; ++i) {
+    const PrepCall& c = calls[i];
+    ASP_TRY(check_ptr(c.x, "x", true));
+    ASP_TRY(check_ptr(c.prep_pack, "prep_pack", true));
+    if (stages & kStageQ) {
+      ASP_TRY(check_ptr(c.x_codes, "x_codes", true));
+      ASP_TRY(check_ptr(c.x_scales, "x_scales", true));
+      ASP_TRY(check_ptr(c.u, "u", r > 0));
+      ASP_TRY(check_ptr(c.prequant, "prequant", false));
+    }
+    if (need) {
+      ASP_TRY(check_ptr(c.scratch, "workspace", true));
+      if (c.scratch_bytes < need)
+        return fail(ASP_ERR_WORKSPACE, "workspace %zu bytes, need %zu", c.scratch_bytes, need);
+    }
   }
-  float* u_part = static_cast<float*>(scratch);
-  if (x_dtype == ASP_F32)
-    return launch_prep(stages, static_cast<const float*>(x), M, K, r, prep_pack, x_codes,
-                       x_scales, u, prequant, u_part, stream);
-  return launch_prep(stages, static_cast<const uint16_t*>(x), M, K, r, prep_pack, x_codes,
-                     x_scales, u, prequant, u_part, stream);
+  if (x_dtype == ASP_F32) return launch_prep<float>(stages, n, calls, M, K, r, stream);
+  return launch_prep<uint16_t>(stages, n, calls, M, K, r, stream);
 }
 
 }  // namespace asp
@@ -587,24 +619,24 @@ int32_t asp_act_prep(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32
                      const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
                      float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return act_prep_impl(kStageU | kStageQ, x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u,
-                       prequant, workspace, workspace_bytes, (hipStream_t)stream);
+  const PrepCall c = {x, prep_pack, x_codes, x_scales, u, prequant, workspace, workspace_bytes};
+  return act_prep_impl(kStageU | kStageQ, 1, &c, x_dtype, M, K, r, (hipStream_t)stream);
 }
 
 int32_t asp_act_prep_u(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                        const uint8_t* prep_pack, void* workspace, size_t workspace_bytes,
                        void* stream) {
   clear_error();
-  return act_prep_impl(kStageU, x, x_dtype, M, K, r, prep_pack, nullptr, nullptr, nullptr,
-                       nullptr, workspace, workspace_bytes, (hipStream_t)stream);
+  const PrepCall c = {x, prep_pack, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes};
+  return act_prep_impl(kStageU, 1, &c, x_dtype, M, K, r, (hipStream_t)stream);
 }
 
 int32_t asp_act_prep_q(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
                        const uint8_t* prep_pack, uint8_t* x_codes, uint8_t* x_scales, float* u,
                        float* prequant, void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
-  return act_prep_impl(kStageQ, x, x_dtype, M, K, r, prep_pack, x_codes, x_scales, u, prequant,
-                       workspace, workspace_bytes, (hipStream_t)stream);
+  const PrepCall c = {x, prep_pack, x_codes, x_scales, u, prequant, workspace, workspace_bytes};
+  return act_prep_impl(kStageQ, 1, &c, x_dtype, M, K, r, (hipStream_t)stream);
 }
 
 }  // extern "C"

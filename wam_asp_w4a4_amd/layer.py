@@ -89,3 +89,27 @@ class PackedLayer:
                       self.w_scales, self.wv, self.bias, y, B.DTYPES[y_dtype], ws, ws.numel(),
                       stream)
         return y
+
+
+def forward_group(layers, x, y_dtype: str = "f32", workspaces=None, ys=None, stream=None):
+    """Run several layers with the same K and rank over one input x as one
+    grouped call (one launch per kernel for the whole group)."""
+    M = x.shape[0]
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be float32 or bfloat16")
+    x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
+    K, r = layers[0].K, layers[0].r
+    if any(l.K != K or l.r != r for l in layers):
+        raise ValueError("a group needs one K and one rank")
+    if ys is None:
+        ys = [torch.empty((M, l.N), device=x.device,
+                          dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16)
+              for l in layers]
+    if workspaces is None:
+        workspaces = [l.workspace(M) for l in layers]
+    B.asp_forward_group([x] * len(layers), x_dtype, M, K, r, [l.prep for l in layers],
+                        [l.w_codes for l in layers], [l.w_scales for l in layers],
+                        [l.wv for l in layers] if r else None,
+                        [l.bias for l in layers], [l.N for l in layers], ys, B.DTYPES[y_dtype],
+                        workspaces, [w.numel() for w in workspaces], stream)
+    return ys
