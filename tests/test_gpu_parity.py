@@ -302,7 +302,10 @@ def test_forward_sampled_rows_of_mot_layers():
 
 
 @pytest.mark.parametrize("M,N,K,r", [(1, 16, 128, 0), (37, 48, 256, 1), (200, 200, 384, 16),
-                                     (129, 130, 128, 33), (64, 64, 512, 64), (300, 16, 1280, 32)])
+                                     (129, 130, 128, 33), (64, 64, 512, 64), (300, 16, 1280, 32),
+                                     # 64 x 64 tiles with r % 16 == 8 (a half-empty last
+                                     # low-rank step), ragged M
+                                     (1024, 1024, 256, 24), (1030, 1000, 128, 8)])
 def test_ragged_shapes(M, N, K, r):
     lay = synth.make_layer("edge", M, K, N, r, seed=M + N + K + r, dtype="bf16")
     check_layer(lay, label="edge")

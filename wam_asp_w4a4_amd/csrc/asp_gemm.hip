@@ -262,14 +262,26 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
     for (int i = 0; i < TM; ++i) {
       const int64_t m = min(m0 + (wm * TM + i) * 32 + l32, M - 1);
       float f[8];
+      // clamped, always valid addresses, columns past r zeroed afterwards (no
+      // lane-dependent branch around a load); cb is a multiple of 8, so when
+      // r % 8 == 0 the 8 columns lie wholly inside or wholly past the row
+      // (past it: the upper lane half of the last step when r % 16 == 8)
       if ((r & 7) == 0) {
-        const float4 p = *reinterpret_cast<const float4*>(u + m * r + cb);
-        const float4 q = *reinterpret_cast<const float4*>(u + m * r + cb + 4);
-        f[0] = p.x; f[1] = p.y; f[2] = p.z; f[3] = p.w; f[4] = q.x; f[5] = q.y; f[6] = q.z; f[7] = q.w;
-        if (cb >= r) for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+        const bool in = cb < r;
+        const float* pu = u + m * r + (in ? cb : 0);
+        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(pu);
+        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(pu + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = in ? p[e] : 0.0f;
+          f[4 + e] = in ? q[e] : 0.0f;
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = cb + e < r ? u[m * r + cb + e] : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+          const float v = u[m * r + min(cb + e, r - 1)];
+          f[e] = cb + e < r ? v : 0.0f;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) la[i][e] = bf16_from_bits(f32_to_bf16_rne(f[e]));
@@ -278,11 +290,16 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
     for (int j = 0; j < TN; ++j) {
       const int64_t n = min(n0 + (wn * TN + j) * 32 + l32, N - 1);
       if ((r & 7) == 0) {
-        uint4 q = cb < r ? *reinterpret_cast<const uint4*>(wv + n * r + cb) : make_uint4(0, 0, 0, 0);
+        const bool in = cb < r;
+        u32x4_t q = *reinterpret_cast<const u32x4_t*>(wv + n * r + (in ? cb : 0));
+        if (!in) q = u32x4_t{0, 0, 0, 0};
         lb[j] = __builtin_bit_cast(bf16x8_t, q);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lb[j][e] = bf16_from_bits(cb + e < r ? wv[n * r + cb + e] : (uint16_t)0);
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = wv[n * r + min(cb + e, r - 1)];
+          lb[j][e] = bf16_from_bits(cb + e < r ? v : (uint16_t)0);
+        }
       }
     }
 #pragma unroll
@@ -434,9 +451,15 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
                                              const float* __restrict__ bias,
                                              void* __restrict__ y, int y_bf16, int tiles_n) {
   constexpr int BM = 32 * FM, BN = 32 * FN, NF = FM + FN;
-  constexpr int CH = 4;                      // groups of 64 K per register chunk
+  constexpr int CH = 4;                      // groups of 64 K per chunk
   constexpr int EPT = BM * BN / (W * 64);    // output elements per thread
-  __shared__ float part[W][BM][BN + 4];
+  // Each wave stages a chunk of its operand rows (32 rows x 128 bytes per
+  // fragment) in a private LDS slot; after the K loop the same memory holds
+  // the partial tiles.
+  constexpr int STAGE = NF * 4 * 64;         // 16-byte pieces per wave
+  static_assert(W * BM * (BN + 4) * 4 <= W * STAGE * 16, "partials must fit the staging LDS");
+  __shared__ u32x4_t stage[W][STAGE];
+  auto part = reinterpret_cast<float(*)[BM][BN + 4]>(&stage[0][0]);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -445,12 +468,10 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
   const int ng = K / 64 / W;                 // groups of this wave
   const int gbeg = wave * ng, gend = gbeg + ng;
 
-  const uint8_t* crow[NF];
   const uint8_t* srow[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int64_t row = f < FM ? min(m0 + 32 * f + l32, M - 1) : min(n0 + 32 * (f - FM) + l32, N - 1);
-    crow[f] = (f < FM ? xc : wc) + row * KB + 16 * half;
     srow[f] = (f < FM ? xs : ws) + row * KS;
   }
 
@@ -462,35 +483,129 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  uint4 cw[2][CH][NF];
-  uint32_t sw[2][CH][NF];
-  auto load = [&](int buf, int g0) {
+  // The low-rank operands and the bias are loaded before the main loop so
+  // their latency hides behind it.  Low-rank K-step c (16 of the r columns)
+  // belongs to wave c % W; lane half h supplies columns 16c + 8h .. 16c + 8h + 7.
+  // Loads read clamped, always valid addresses; columns past r (and bias
+  // entries past N) are zeroed only where the values are used, so nothing
+  // waits for these loads before the main loop.  When r % 8 == 0 the 8
+  // columns are 16-byte aligned (u and wv are) and lie wholly inside or
+  // wholly past the row.
+  constexpr int LRW = (4 + W - 1) / W;       // r <= 64: at most 4 steps, spread over W waves
+  f32x4_t lu[LRW][FM][2];
+  u32x4_t lw[LRW][FN];
+  const bool vec = (r & 7) == 0;
+#pragma unroll
+  for (int k = 0; k < LRW; ++k) {
+    const int cb = 16 * (wave + k * W) + 8 * half;
+    if (cb - 8 * half >= r) continue;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const float* pu = u + min(m0 + 32 * i + l32, M - 1) * (int64_t)r;
+      if (vec) {
+        const float* p = pu + (cb < r ? cb : 0);
+        lu[k][i][0] = *reinterpret_cast<const f32x4_t*>(p);
+        lu[k][i][1] = *reinterpret_cast<const f32x4_t*>(p + 4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lu[k][i][e >> 2][e & 3] = pu[min(cb + e, r - 1)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint16_t* pw = wv + min(n0 + 32 * j + l32, N - 1) * (int64_t)r;
+      if (vec) {
+        lw[k][j] = *reinterpret_cast<const u32x4_t*>(pw + (cb < r ? cb : 0));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lw[k][j][e] = pw[min(cb + 2 * e, r - 1)] | ((uint32_t)pw[min(cb + 2 * e + 1, r - 1)] << 16);
+      }
+    }
+  }
+  const int e0 = tid * EPT, orow = e0 / BN, ocol = e0 % BN;
+  const int gm = m0 + orow, gn = n0 + ocol;
+  float bv[EPT];
+  if (bias) {
+    if (gn + EPT <= N && ((gn | N) & 3) == 0 && EPT % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4) {
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(bias + gn + e);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bv[e + t] = b[t];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) bv[e] = bias[min(gn + e, N - 1)];
+    }
+  }
+
+  // Codes: global -> LDS by direct 16-byte copies.  Copy j of fragment f
+  // moves tile rows 8j .. 8j+7 x the chunk's 128 bytes (8 pieces of 16 bytes,
+  // 8 whole rows per instruction); slot s of the copy receives piece
+  // (s % 8) ^ (row % 8) of row 8j + s / 8, so that the MFMA-layout reads below
+  // (lane: row l32, piece 2c + half) fall in distinct banks.  Pieces past the
+  // wave's K range copy valid bytes of the range that nobody reads.
+  const uint8_t* srcrow[NF][4];
+  const int crr = lane >> 3;
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int trow = 8 * j + crr;
+      const int64_t row = f < FM ? min(m0 + 32 * f + trow, M - 1) : min(n0 + 32 * (f - FM) + trow, N - 1);
+      srcrow[f][j] = (f < FM ? xc : wc) + row * KB;
+    }
+  const int cp = (lane & 7) ^ (crr & 7);     // the piece this lane copies (rows 8j + crr)
+  auto issue = [&](int g0) {
+    const int g = g0 + (cp >> 1) < gend ? g0 + (cp >> 1) : g0;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        lds_copy16(srcrow[f][j] + 32 * (int64_t)g + 16 * (cp & 1), &stage[wave][(f * 4 + j) * 64]);
+  };
+  static_assert(CH == 4, "a chunk's scales are one 16-byte load");
+  auto load_scales = [&](uint32_t (&sw)[CH][NF], int g0) {
+    // the chunk's 4 groups' scales (16 consecutive bytes of the row) in one
+    // load when they are whole and 16-byte aligned
+    if ((KS & 15) == 0 && (g0 & 3) == 0 && g0 + CH <= gend) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(srow[f] + 4 * (int64_t)g0);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) sw[c][f] = q[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (g0 + c < gend)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            sw[c][f] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * (int64_t)(g0 + c));
+    }
+  };
+  auto fetch = [&](u32x4_t (&cw)[CH][NF]) {
+    const int key = l32 & 7;
 #pragma unroll
     for (int c = 0; c < CH; ++c)
-      if (g0 + c < gend)
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          cw[buf][c][f] = *reinterpret_cast<const uint4*>(crow[f] + 32 * (int64_t)(g0 + c));
-          sw[buf][c][f] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * (int64_t)(g0 + c));
-        }
+      for (int f = 0; f < NF; ++f)
+        cw[c][f] = stage[wave][(f * 4 + (l32 >> 3)) * 64 + key * 8 + ((2 * c + half) ^ key)];
   };
-  auto compute = [&](int buf, int g0) {
+  auto compute = [&](const u32x4_t (&cw)[CH][NF], const uint32_t (&sw)[CH][NF], int g0) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (g0 + c >= gend) break;
       half2_t sp[NF];  // this lane's two block scales of the group, as fp16
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        sp[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[buf][c][f] >> (16 * half), 1.0f, false);
+        sp[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[c][f] >> (16 * half), 1.0f, false);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         half8_t fr[NF];
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint4 q = cw[buf][c][f];
-          const uint32_t wd = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
-          fr[f] = decode8(wd, sp[f][t >> 1]);
-        }
+        for (int f = 0; f < NF; ++f) fr[f] = decode8(cw[c][f][t], sp[f][t >> 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -499,39 +614,53 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
       }
     }
   };
-  load(0, gbeg);
-  for (int g0 = gbeg; g0 < gend; g0 += 2 * CH) {
-    if (g0 + CH < gend) load(1, g0 + CH);
-    compute(0, g0);
-    if (g0 + CH >= gend) break;
-    if (g0 + 2 * CH < gend) load(0, g0 + 2 * CH);
-    compute(1, g0 + CH);
-  }
-
-  // low-rank branch bf16(u) wv^T, in the first wave's partial
-  if (wave == 0) {
-    for (int c0 = 0; c0 < r; c0 += 16) {
-      const int cb = c0 + half * 8;
-      bf16x8_t la[FM], lb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = min(m0 + 32 * i + l32, M - 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          la[i][e] = bf16_from_bits(f32_to_bf16_rne(cb + e < r ? u[m * r + cb + e] : 0.0f));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t n = min(n0 + 32 * j + l32, N - 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lb[j][e] = bf16_from_bits(cb + e < r ? wv[n * r + cb + e] : (uint16_t)0);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
+  uint32_t sw[CH][NF];
+  issue(gbeg);
+  load_scales(sw, gbeg);
+  for (int g0 = gbeg; g0 < gend; g0 += CH) {
+    // the copies into this wave's slot have landed (and nothing else of the
+    // wave is in flight); the memory clobber keeps the LDS reads below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    u32x4_t cw[CH][NF];
+    fetch(cw);
+    const bool more = g0 + CH < gend;
+    uint32_t swn[CH][NF];
+    if (more) {
+      // the reads of the slot are complete before it is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(g0 + CH);
+      load_scales(swn, g0 + CH);
     }
+    compute(cw, sw, g0);
+    if (more)
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) sw[c][f] = swn[c][f];
+  }
+  __syncthreads();  // every wave is done with the staging slots: they become the partials
+
+  // low-rank branch bf16(u) wv^T: this wave's steps, into its partial
+#pragma unroll
+  for (int k = 0; k < LRW; ++k) {
+    const int cb = 16 * (wave + k * W) + 8 * half;
+    if (cb - 8 * half >= r) continue;
+    bf16x8_t la[FM], lb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        la[i][e] = bf16_from_bits(cb + e < r ? f32_to_bf16_rne(lu[k][i][e >> 2][e & 3]) : (uint16_t)0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        lb[j][e] = bf16_from_bits(cb + e < r ? (uint16_t)(lw[k][j][e >> 1] >> (16 * (e & 1))) : (uint16_t)0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
   }
 
   // partial tiles to LDS (accumulator element v of lane l: row 8*(v/4) +
@@ -544,29 +673,25 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
       for (int v = 0; v < 16; ++v)
         part[wave][32 * i + 8 * (v >> 2) + 4 * half + (v & 3)][32 * j + l32] = acc[i][j][v];
   __syncthreads();
-  const int e0 = tid * EPT, row = e0 / BN, col = e0 % BN;
-  const int gm = m0 + row, gn = n0 + col;
   if (gm >= M) return;
   float out[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) s += part[w][row][col + e];
-    out[e] = s + ((bias && gn + e < N) ? bias[gn + e] : 0.0f);
+    for (int w = 0; w < W; ++w) s += part[w][orow][ocol + e];
+    out[e] = s + ((bias && gn + e < N) ? bv[e] : 0.0f);
   }
   const int64_t base = (int64_t)gm * N + gn;
   if (y_bf16) {
     uint16_t* yo = reinterpret_cast<uint16_t*>(y) + base;
-    if (gn + EPT <= N && (base & 7) == 0 && EPT % 8 == 0) {
+    if (gn + EPT <= N && (base & 3) == 0 && EPT % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < EPT; e += 8) {
-        uint4 pk;
+      for (int e = 0; e < EPT; e += 4) {
+        uint2 pk;
         pk.x = f32_to_bf16_rne(out[e]) | ((uint32_t)f32_to_bf16_rne(out[e + 1]) << 16);
         pk.y = f32_to_bf16_rne(out[e + 2]) | ((uint32_t)f32_to_bf16_rne(out[e + 3]) << 16);
-        pk.z = f32_to_bf16_rne(out[e + 4]) | ((uint32_t)f32_to_bf16_rne(out[e + 5]) << 16);
-        pk.w = f32_to_bf16_rne(out[e + 6]) | ((uint32_t)f32_to_bf16_rne(out[e + 7]) << 16);
-        *reinterpret_cast<uint4*>(yo + e) = pk;
+        *reinterpret_cast<uint2*>(yo + e) = pk;
       }
     } else {
 #pragma unroll

@@ -134,6 +134,7 @@ struct XFrag<float> {
 // `row` sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read
 // the same piece of 16 different rows, hit 16 different bank groups.
 constexpr int kPrepRows = 64;  // rows of x per k_prep_q workgroup (4 waves x 16)
+constexpr int kMaxSlices = 4;  // slices of K for the partial sums of u
 
 template <int KS>
 struct UStage {
@@ -308,18 +309,29 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
-    for (int s = 0; s < S; ++s) {
+    // all S (<= kMaxSlices) partials are loaded before the first is used, so
+    // their latencies overlap; slices past S re-read the last one and are
+    // not added (the sum keeps slice order)
+    f32x4_t pa[kMaxSlices][KS][2];
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(u_part + ((int64_t)s * M + mc) * RP + 32 * kk + 8 * q);
-        const f32x4_t a = p[0], c = p[1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          us[kk][e] += a[e];
-          us[kk][4 + e] += c[e];
-        }
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
+            u_part + ((int64_t)min(s, S - 1) * M + mc) * RP + 32 * kk + 8 * q);
+        pa[s][kk][0] = p[0];
+        pa[s][kk][1] = p[1];
       }
-    }
+#pragma unroll
+    for (int s = 0; s < kMaxSlices; ++s)
+      if (s < S)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            us[kk][e] += pa[s][kk][0][e];
+            us[kk][4 + e] += pa[s][kk][1][e];
+          }
     if (bq0 == 0 && mok) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
@@ -503,10 +515,11 @@ __global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int
 constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
 
 // Slices of K for the partial sums of u (a function of K only, so a row's u
-// does not depend on the batch): up to 4, each a whole number of blocks.
+// does not depend on the batch): up to kMaxSlices, each a whole number of
+// blocks.
 void u_slicing(int64_t K, int* S, int* bps) {
   const int nblk = (int)(K / 128);
-  const int s = nblk < 4 ? nblk : 4;
+  const int s = nblk < kMaxSlices ? nblk : kMaxSlices;
   *bps = (nblk + s - 1) / s;
   *S = (nblk + *bps - 1) / *bps;
 }
