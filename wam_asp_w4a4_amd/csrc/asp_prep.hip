@@ -88,6 +88,8 @@ struct XFrag<uint16_t> {
     for (int g = 0; g < 4; ++g)
       f[g] = *reinterpret_cast<const u32x4_t*>(row + col0 + 64 * (g >> 1) + 16 * q + 8 * (g & 1));
   }
+  // from a wave's staged tile (XStage layout): row l16, fragment pieces
+  __device__ __forceinline__ void load_lds(const u32x4_t* t, int q, int l16);
   __device__ __forceinline__ void get(int g, float* v) const {
     const uint32_t w[4] = {f[g][0], f[g][1], f[g][2], f[g][3]};
 #pragma unroll
@@ -110,6 +112,7 @@ struct XFrag<float> {
       f[2 * g + 1] = p[1];
     }
   }
+  __device__ __forceinline__ void load_lds(const u32x4_t* t, int q, int l16);
   __device__ __forceinline__ void get(int g, float* v) const {
     const f32x4_t a = f[2 * g], b = f[2 * g + 1];
 #pragma unroll
@@ -120,6 +123,48 @@ struct XFrag<float> {
   }
 };
 
+// A wave's 16 rows x 128 columns of x staged in LDS by direct 16-byte copies
+// (lds_copy16): copy j moves RPC whole rows (4 rows of 256 bytes for bf16, 2
+// of 512 for fp32), so one instruction reads few, fully used cache lines.
+// Slot l of copy j holds piece (l % PPR) ^ (R & 15) of tile row R = RPC*j +
+// l / PPR; a fragment read (16 lanes: one piece of 16 different rows) then
+// falls in 16 distinct bank groups.
+template <typename XT>
+struct XStage {
+  static constexpr int PPR = 128 * (int)sizeof(XT) / 16;  // 16-byte pieces per row
+  static constexpr int RPC = 64 / PPR;                     // rows per copy
+  static constexpr int COPIES = 16 / RPC;
+  static constexpr int PIECES = 16 * PPR;                  // per wave
+  __device__ static __forceinline__ int slot(int row, int piece) {
+    return (row / RPC) * 64 + (row % RPC) * PPR + (piece ^ (row & 15));
+  }
+  // rows m0 .. m0+15 (clamped to M - 1), columns col0 .. col0+127
+  __device__ static __forceinline__ void issue(const XT* x, int64_t m0, int M, int64_t K, int col0,
+                                               u32x4_t* t, int lane) {
+    const int R0 = lane / PPR, p = lane % PPR;
+#pragma unroll
+    for (int j = 0; j < COPIES; ++j) {
+      const int R = RPC * j + R0;
+      const int64_t row = min(m0 + R, (int64_t)M - 1);
+      lds_copy16(x + row * K + col0 + (p ^ (R & 15)) * (16 / (int)sizeof(XT)), t + 64 * j);
+    }
+  }
+};
+
+__device__ __forceinline__ void XFrag<uint16_t>::load_lds(const u32x4_t* t, int q, int l16) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) f[g] = t[XStage<uint16_t>::slot(l16, 8 * (g >> 1) + 2 * q + (g & 1))];
+}
+
+__device__ __forceinline__ void XFrag<float>::load_lds(const u32x4_t* t, int q, int l16) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int p = 16 * (g >> 1) + 4 * q + 2 * (g & 1);
+    f[2 * g] = __builtin_bit_cast(f32x4_t, t[XStage<float>::slot(l16, p)]);
+    f[2 * g + 1] = __builtin_bit_cast(f32x4_t, t[XStage<float>::slot(l16, p + 1)]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_prep_u.  Workgroup = 4 waves x 16 rows, one slice of K (blocks b0..b1).
 // Lane l of wave w: row m0 + 16w + l%16, lane quarter q = l/16.  Per block,
@@ -129,18 +174,21 @@ struct XFrag<float> {
 // column l%16, the same 8 columns).  Output lane layout: u row 4q + i, column
 // l%16.
 //
-// LDS: up to kUChunks chunks of V''^T (hi and lo; RP rows of 128 bf16 = 16
-// pieces of 16 bytes), staged in one round with lds_copy16.  Piece p of row
-// `row` sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read
-// the same piece of 16 different rows, hit 16 different bank groups.
+// LDS per round: up to CHUNKS chunks (128-column blocks) of V''^T (hi and lo;
+// RP rows of 128 bf16 = 16 pieces of 16 bytes) and of every wave's x rows
+// (XStage), all staged at once with lds_copy16.  Piece p of V''^T row `row`
+// sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read the
+// same piece of 16 different rows, hit 16 different bank groups.
 constexpr int kPrepRows = 64;  // rows of x per k_prep_q workgroup (4 waves x 16)
 constexpr int kMaxSlices = 4;  // slices of K for the partial sums of u
 
-template <int KS>
+template <typename XT, int KS>
 struct UStage {
   static constexpr int RP = 32 * KS;
   static constexpr int CHUNK_PIECES = 2 * RP * 16;            // hi + lo, 16 pieces per row
-  static constexpr int CHUNKS = KS == 1 ? 8 : 4;               // 128 KB of LDS per round
+  static constexpr int X_PIECES = 4 * XStage<XT>::PIECES;     // the 4 waves' x
+  static constexpr int CHUNKS = 8192 / (CHUNK_PIECES + X_PIECES);  // up to 128 KB per round
+  static_assert(CHUNKS >= 1, "one chunk must fit");
 };
 
 template <typename XT, int KS>
@@ -148,17 +196,16 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
                                             const uint16_t* __restrict__ vth,
                                             const uint16_t* __restrict__ vtl,
                                             float* __restrict__ u_part, int bps) {
-  using St = UStage<KS>;
+  using St = UStage<XT, KS>;
   constexpr int RP = St::RP, CT = KS * 2, NC = St::CHUNKS;
   constexpr bool fp32_x = sizeof(XT) == 4;
-  extern __shared__ u32x4_t sv[];  // min(NC, bps) chunks, sized at launch
+  extern __shared__ u32x4_t sv[];  // min(NC, bps) chunks of V''^T, then of x; sized at launch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int m0 = blockIdx.x * kPrepRows + 16 * wave;
   const int64_t mc = min(m0 + l16, M - 1);
   const int nblk = K >> 7;
   const int b0 = blockIdx.y * bps, b1 = min(nblk, b0 + bps);
-  const XT* xrow = x + mc * K;
 
   f32x4_t ah[CT], al[CT];
 #pragma unroll
@@ -178,25 +225,26 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
       const uint16_t* src = (hl ? vtl : vth) + (int64_t)row * K + (rb + c) * 128 + 8 * (slot ^ (row & 15));
       lds_copy16(src, &sv[base]);
     }
-    XFrag<XT> xr[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (c < nc) xr[c].load(xrow, (rb + c) * 128, q);
+    u32x4_t* sx = sv + ncmax * St::CHUNK_PIECES;  // chunk c, wave w: sx + (4c + w) * PIECES
+    for (int c = 0; c < nc; ++c)
+      XStage<XT>::issue(x, m0, M, K, (rb + c) * 128, sx + (4 * c + wave) * XStage<XT>::PIECES, lane);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
     __syncthreads();                // and everyone else's
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (c >= nc) break;
       const u32x4_t* ch = sv + c * St::CHUNK_PIECES;
+      XFrag<XT> xc;
+      xc.load_lds(sx + (4 * c + wave) * XStage<XT>::PIECES, q, l16);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int piece = 8 * (g >> 1) + 2 * q + (g & 1);
         bf16x8_t a_hi, a_lo;
         if constexpr (!fp32_x) {
-          a_hi = as_bf16x8(xr[c].f[g]);
+          a_hi = as_bf16x8(xc.f[g]);
         } else {
           float f[8];
-          xr[c].get(g, f);
+          xc.get(g, f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             uint16_t hi, lo;
@@ -295,10 +343,16 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   }
   f32x4_t cr;
   if (tid < 32 * nb) cr = reinterpret_cast<const f32x4_t*>(cvec + bq0 * 128)[tid];
+  // x through LDS (XStage) unless that would take static LDS past 64 KB
+  // (fp32 x with r > 32): then straight to registers
+  static_assert(NBQ == 1, "one block of x per wave is staged");
+  constexpr bool kStageX = sizeof(XT) == 2 || KS < 2;
+  __shared__ u32x4_t sx[kStageX ? 4 : 1][kStageX ? XStage<XT>::PIECES : 1];
   XFrag<XT> xr[NBQ];
-#pragma unroll
-  for (int i = 0; i < NBQ; ++i)
-    if (i < nb) xr[i].load(x + mc * K, (bq0 + i) * 128, q);
+  if constexpr (kStageX)
+    XStage<XT>::issue(x, m0, M, K, bq0 * 128, sx[wave], lane);
+  else
+    xr[0].load(x + mc * K, bq0 * 128, q);
 
   // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
   // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
@@ -352,6 +406,7 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   if (tid < 32 * nb) reinterpret_cast<f32x4_t*>(&scv[0][0])[tid] = cr;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies have landed
   __syncthreads();
+  if constexpr (kStageX) xr[0].load_lds(sx[wave], q, l16);
 
 #pragma unroll
   for (int i = 0; i < NBQ; ++i) {
@@ -535,7 +590,8 @@ void launch_ks(hipStream_t st, int stages, int n, const PrepArgs<XT>& a, int M, 
       // the chunks of a slice (up to a round's worth) in dynamic LDS; above the
       // default 64 KB this must be allowed per kernel (a host attribute of the
       // current device, not a stream operation)
-      const size_t lds = (size_t)std::min(UStage<KS>::CHUNKS, bps) * UStage<KS>::CHUNK_PIECES * 16;
+      using St = UStage<XT, KS>;
+      const size_t lds = (size_t)std::min(St::CHUNKS, bps) * (St::CHUNK_PIECES + St::X_PIECES) * 16;
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prep_u<XT, KS>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       hipLaunchKernelGGL((k_prep_u<XT, KS>), dim3((unsigned)tiles64, (unsigned)S, (unsigned)n),
