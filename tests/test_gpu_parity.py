@@ -136,7 +136,10 @@ def prep_cases():
     # more blocks per wave than stay in registers: x is loaded again in phase 2
     r64k = synth.make_layer("r64-reload", 20, 2048, 32, 64, seed=10, dtype="bf16")
     f32k = synth.make_layer("f32-reload", 9, 3072, 32, 32, seed=11, dtype="f32")
-    return [c0, c1, c2, r0, r16, r64, r64k, f32k]
+    # 32 or more blocks: 8 slices of K for rank <= 32, 4 for rank 64
+    s8 = synth.make_layer("f32-8slices", 7, 4096, 32, 16, seed=12, dtype="f32")
+    s4 = synth.make_layer("r64-4slices", 9, 4096, 32, 64, seed=13, dtype="bf16")
+    return [c0, c1, c2, r0, r16, r64, r64k, f32k, s8, s4]
 
 
 @pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")

@@ -180,7 +180,12 @@ __device__ __forceinline__ void XFrag<float>::load_lds(const u32x4_t* t, int q, 
 // sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read the
 // same piece of 16 different rows, hit 16 different bank groups.
 constexpr int kPrepRows = 64;  // rows of x per k_prep_q workgroup (4 waves x 16)
-constexpr int kMaxSlices = 4;  // slices of K for the partial sums of u
+// Slices of K for the partial sums of u: up to 8 when u has at most 32
+// columns, up to 4 when it has 64 (the quantise stage holds every slice's
+// partial sums in registers at once).  Every 128-column workgroup of the
+// quantise stage reads all of its rows' partial sums, so more slices cost
+// there what they save in the u stage; 8 pay off only for long rows.
+constexpr int max_slices(int ks) { return ks <= 1 ? 8 : 4; }
 
 template <typename XT, int KS>
 struct UStage {
@@ -363,12 +368,13 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
-    // all S (<= kMaxSlices) partials are loaded before the first is used, so
+    // all S (<= max_slices) partials are loaded before the first is used, so
     // their latencies overlap; slices past S re-read the last one and are
     // not added (the sum keeps slice order)
-    f32x4_t pa[kMaxSlices][KS][2];
+    constexpr int MS = max_slices(KS);
+    f32x4_t pa[MS][KS][2];
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s)
+    for (int s = 0; s < MS; ++s)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
@@ -377,7 +383,7 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
         pa[s][kk][1] = p[1];
       }
 #pragma unroll
-    for (int s = 0; s < kMaxSlices; ++s)
+    for (int s = 0; s < MS; ++s)
       if (s < S)
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -569,12 +575,12 @@ __global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int
 
 constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
 
-// Slices of K for the partial sums of u (a function of K only, so a row's u
-// does not depend on the batch): up to kMaxSlices, each a whole number of
-// blocks.
-void u_slicing(int64_t K, int* S, int* bps) {
+// Slices of K for the partial sums of u (a function of K and the padded rank
+// only, so a row's u does not depend on the batch): up to max_slices, each a
+// whole number of blocks.
+void u_slicing(int64_t K, int ks, int* S, int* bps) {
   const int nblk = (int)(K / 128);
-  const int s = nblk < kMaxSlices ? nblk : kMaxSlices;
+  const int s = std::min(nblk, nblk >= 32 ? max_slices(ks) : 4);
   *bps = (nblk + s - 1) / s;
   *S = (nblk + *bps - 1) / *bps;
 }
@@ -585,7 +591,7 @@ void launch_ks(hipStream_t st, int stages, int n, const PrepArgs<XT>& a, int M, 
   const int tiles64 = (M + kPrepRows - 1) / kPrepRows;
   int S = 0, bps = 0;
   if constexpr (KS > 0) {
-    u_slicing(K, &S, &bps);
+    u_slicing(K, KS, &S, &bps);
     if (stages & kStageU) {
       // the chunks of a slice (up to a round's worth) in dynamic LDS; above the
       // default 64 KB this must be allowed per kernel (a host attribute of the
@@ -637,8 +643,9 @@ int32_t launch_prep(int stages, int n, const PrepCall* calls, int64_t M, int64_t
 size_t act_prep_scratch_bytes(int64_t M, int64_t K, int32_t r) {
   if (r == 0 || M == 0) return 0;
   int S, bps;
-  u_slicing(K, &S, &bps);
-  return (size_t)S * (size_t)M * (size_t)prep_pack_layout(K, r).rp32 * sizeof(float);
+  const int rp32 = prep_pack_layout(K, r).rp32;
+  u_slicing(K, rp32 / 32, &S, &bps);
+  return (size_t)S * (size_t)M * (size_t)rp32 * sizeof(float);
 }
 
 int32_t act_prep_impl(int stages, int n, const PrepCall* calls, int32_t x_dtype, int64_t M,
