@@ -215,7 +215,11 @@ def gemm_on_oracle_codes(lay, y_dtype):
 def gemm_cases():
     return [synth.workload(0)[0], synth.workload(1)[0],
             synth.make_layer("ragged", 200, 384, 200, 33, seed=8, dtype="f32"),
-            synth.make_layer("tiny", 1, 128, 16, 0, seed=9, dtype="f32")]
+            synth.make_layer("tiny", 1, 128, 16, 0, seed=9, dtype="f32"),
+            # the tile kernels' low-rank rows through LDS (r <= 32, r % 8 == 0):
+            # 64 x 64 tiles with r = 16; 256 x 192 tiles, ragged N, r = 24
+            synth.make_layer("tile64-r16", 1024, 256, 1024, 16, seed=14, dtype="bf16"),
+            synth.make_layer("tile256-r24", 4096, 256, 2000, 24, seed=15, dtype="bf16")]
 
 
 @pytest.mark.parametrize("lay", gemm_cases(), ids=lambda l: f"{l.name}-M{l.M}-N{l.N}-K{l.K}-r{l.r}")

@@ -97,6 +97,20 @@ __device__ __forceinline__ _Float16 scale_f16(uint32_t code) {
 
 __device__ __forceinline__ __bf16 bf16_from_bits(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
 
+// float -> bf16 rounded to nearest even by the hardware conversion
+// (v_cvt_pk_bf16_f32, two values per instruction; finite inputs)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ bf16x8_t bf16x8_rne(const float (&f)[8]) {
+  const uint32_t w[4] = {bf16x2_rne(f[0], f[1]), bf16x2_rne(f[2], f[3]), bf16x2_rne(f[4], f[5]),
+                         bf16x2_rne(f[6], f[7])};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 // ------------------------------------------------------------- host helpers
 
 inline int32_t launch_status(const char* what) {

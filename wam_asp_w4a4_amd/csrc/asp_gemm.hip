@@ -189,6 +189,41 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
 #pragma unroll
   for (int j = 0; j < TN; ++j) boff[j] = (C::BM + (wn * TN + j) * 32 + l32);
 
+  // Low-rank operands through LDS when r <= 32 and r % 8 == 0: during the
+  // last stage the other staging buffer is free, and direct 16-byte copies
+  // (no registers) fill it with the tile's rows of u (BM x 32 fp32, 128 B a
+  // row) and W~V (BN x 32 bf16, 64 B a row).  Piece p of a u row sits in slot
+  // p ^ (row & 7), of a W~V row in slot p ^ (row & 3), so the fragment reads
+  // below spread over the banks; pieces past r copy piece 0 (never read).
+  static_assert(C::BM * 128 + C::BN * 64 <= C::STAGE, "low-rank rows must fit a staging buffer");
+  // (Measured: this pays off for the 64 x 64 tiles; in the 256 x 192 tiles it
+  // costs more in the K loop's registers than it hides.)
+  constexpr bool kLrStage = TM * TN == 1;
+  const bool lr_lds = kLrStage && r > 0 && r <= 32 && (r & 7) == 0;
+  auto lr_issue = [&](uint8_t* buf) {
+    // an opaque zero keeps the address arithmetic inside the last stage
+    // instead of live across the whole K loop
+    int zo = 0;
+    asm volatile("" : "+s"(zo));
+    const int w = (tid >> 6) + zo;
+#pragma unroll
+    for (int j = 0; j < (C::BM * 8 + C::NT - 1) / C::NT; ++j) {
+      const int P0 = (j * C::NW + w) * 64;
+      if (P0 >= C::BM * 8) break;
+      const int P = P0 + lane, row = P >> 3, slot = P & 7, pc = slot ^ (row & 7);
+      const int64_t m = min(m0 + row, M - 1);
+      lds_copy16(u + m * r + (4 * pc < r ? 4 * pc : 0), buf + 16 * P0);
+    }
+#pragma unroll
+    for (int j = 0; j < (C::BN * 4 + C::NT - 1) / C::NT; ++j) {
+      const int P0 = (j * C::NW + w) * 64;
+      if (P0 >= C::BN * 4) break;
+      const int P = P0 + lane, row = P >> 2, slot = P & 3, pc = slot ^ (row & 3);
+      const int64_t n = min(n0 + row, N - 1);
+      lds_copy16(wv + n * r + (8 * pc < r ? 8 * pc : 0), buf + C::BM * 128 + 16 * P0);
+    }
+  };
+
   const int nk = (K + BK - 1) / BK;
   gload(0);
   sstore(0);
@@ -196,6 +231,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
   __syncthreads();
   for (int kc = 0; kc < nk; ++kc) {
     const uint8_t* base = smem + (kc & 1) * C::STAGE;
+    if constexpr (kLrStage)
+      if (lr_lds && kc == nk - 1) lr_issue(smem + ((kc + 1) & 1) * C::STAGE);
     uint32_t aw[TM], bw[TN], asw[TM], bsw[TN];
     auto read_words = [&](int ks, uint32_t (&a)[TM], uint32_t (&b)[TN]) {
 #pragma unroll
@@ -254,51 +291,72 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
   }
 
   // low-rank branch: bf16(u) (M x r) times wv^T (r x N), K-steps of 16.  The
-  // operand rows are fetched with vector loads when r is a multiple of 8.
+  // operand rows come from the staging buffer filled during the last stage
+  // (lr_lds), else straight from memory (vector loads when r % 8 == 0).
+  const uint8_t* lrb = smem + (nk & 1) * C::STAGE;
+  if (lr_lds) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies have landed
+    __syncthreads();                                   // and every other wave's
+  }
   for (int c0 = 0; c0 < r; c0 += 16) {
     bf16x8_t la[TM], lb[TN];
-    const int cb = c0 + half * 8;
+    const int cb = c0 + half * 8;                      // this lane's 8 columns
+    const bool in = cb < r;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int64_t m = min(m0 + (wm * TM + i) * 32 + l32, M - 1);
       float f[8];
-      // clamped, always valid addresses, columns past r zeroed afterwards (no
-      // lane-dependent branch around a load); cb is a multiple of 8, so when
-      // r % 8 == 0 the 8 columns lie wholly inside or wholly past the row
-      // (past it: the upper lane half of the last step when r % 16 == 8)
-      if ((r & 7) == 0) {
-        const bool in = cb < r;
-        const float* pu = u + m * r + (in ? cb : 0);
-        const f32x4_t p = *reinterpret_cast<const f32x4_t*>(pu);
-        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(pu + 4);
+      if (lr_lds) {
+        const int row = (wm * TM + i) * 32 + l32, p0 = cb >> 2;
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(lrb + row * 128 + 16 * ((p0 ^ (row & 7)) & 7));
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(lrb + row * 128 + 16 * (((p0 + 1) ^ (row & 7)) & 7));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          f[e] = in ? p[e] : 0.0f;
-          f[4 + e] = in ? q[e] : 0.0f;
+          f[e] = in ? a[e] : 0.0f;
+          f[4 + e] = in ? b[e] : 0.0f;
         }
       } else {
+        // clamped, always valid addresses, columns past r zeroed afterwards
+        // (no lane-dependent branch around a load); when r % 8 == 0 the 8
+        // columns lie wholly inside or wholly past the row
+        const int64_t m = min(m0 + (wm * TM + i) * 32 + l32, M - 1);
+        if ((r & 7) == 0) {
+          const float* pu = u + m * r + (in ? cb : 0);
+          const f32x4_t a = *reinterpret_cast<const f32x4_t*>(pu);
+          const f32x4_t b = *reinterpret_cast<const f32x4_t*>(pu + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = u[m * r + min(cb + e, r - 1)];
-          f[e] = cb + e < r ? v : 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            f[e] = in ? a[e] : 0.0f;
+            f[4 + e] = in ? b[e] : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = u[m * r + min(cb + e, r - 1)];
+            f[e] = cb + e < r ? v : 0.0f;
+          }
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) la[i][e] = bf16_from_bits(f32_to_bf16_rne(f[e]));
+      la[i] = bf16x8_rne(f);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int64_t n = min(n0 + (wn * TN + j) * 32 + l32, N - 1);
-      if ((r & 7) == 0) {
-        const bool in = cb < r;
-        u32x4_t q = *reinterpret_cast<const u32x4_t*>(wv + n * r + (in ? cb : 0));
+      if (lr_lds) {
+        const int row = (wn * TN + j) * 32 + l32;
+        u32x4_t q = *reinterpret_cast<const u32x4_t*>(lrb + C::BM * 128 + row * 64 + 16 * (((cb >> 3) ^ (row & 3)) & 3));
         if (!in) q = u32x4_t{0, 0, 0, 0};
         lb[j] = __builtin_bit_cast(bf16x8_t, q);
       } else {
+        const int64_t n = min(n0 + (wn * TN + j) * 32 + l32, N - 1);
+        if ((r & 7) == 0) {
+          u32x4_t q = *reinterpret_cast<const u32x4_t*>(wv + n * r + (in ? cb : 0));
+          if (!in) q = u32x4_t{0, 0, 0, 0};
+          lb[j] = __builtin_bit_cast(bf16x8_t, q);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t v = wv[n * r + min(cb + e, r - 1)];
-          lb[j][e] = bf16_from_bits(cb + e < r ? v : (uint16_t)0);
+          for (int e = 0; e < 8; ++e) {
+            const uint16_t v = wv[n * r + min(cb + e, r - 1)];
+            lb[j][e] = bf16_from_bits(cb + e < r ? v : (uint16_t)0);
+          }
         }
       }
     }
@@ -331,7 +389,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
         for (int v = 0; v < 16; ++v) {
           const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
           const int col = (wn * TN + j) * 32 + l32;
-          ot[row * C::BN + col] = f32_to_bf16_rne(acc[i][j][v] + bj[j]);
+          ot[row * C::BN + col] = bf16_rne(acc[i][j][v] + bj[j]);
         }
     __syncthreads();
     uint16_t* yo = reinterpret_cast<uint16_t*>(y);
@@ -647,10 +705,12 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
     if (cb - 8 * half >= r) continue;
     bf16x8_t la[FM], lb[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      float f[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        la[i][e] = bf16_from_bits(cb + e < r ? f32_to_bf16_rne(lu[k][i][e >> 2][e & 3]) : (uint16_t)0);
+      for (int e = 0; e < 8; ++e) f[e] = cb + e < r ? lu[k][i][e >> 2][e & 3] : 0.0f;
+      la[i] = bf16x8_rne(f);
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -689,14 +749,14 @@ __device__ __forceinline__ void gemm_sk_body(const uint8_t* __restrict__ xc,
 #pragma unroll
       for (int e = 0; e < EPT; e += 4) {
         uint2 pk;
-        pk.x = f32_to_bf16_rne(out[e]) | ((uint32_t)f32_to_bf16_rne(out[e + 1]) << 16);
-        pk.y = f32_to_bf16_rne(out[e + 2]) | ((uint32_t)f32_to_bf16_rne(out[e + 3]) << 16);
+        pk.x = bf16x2_rne(out[e], out[e + 1]);
+        pk.y = bf16x2_rne(out[e + 2], out[e + 3]);
         *reinterpret_cast<uint2*>(yo + e) = pk;
       }
     } else {
 #pragma unroll
       for (int e = 0; e < EPT; ++e)
-        if (gn + e < N) yo[e] = f32_to_bf16_rne(out[e]);
+        if (gn + e < N) yo[e] = bf16_rne(out[e]);
     }
   } else {
     float* yo = reinterpret_cast<float*>(y) + base;

@@ -70,8 +70,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_ca
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t q) { return __builtin_bit_cast(bf16x8_t, q); }
 
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16_rne(v);
-  lo = f32_to_bf16_rne(v - bits_f32((uint32_t)hi << 16));
+  hi = bf16_rne(v);
+  lo = bf16_rne(v - bits_f32((uint32_t)hi << 16));
 }
 
 // Raw x of one (16 rows, 128 columns) unit as this lane loads it: columns
