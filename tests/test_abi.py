@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == B.ABI_VERSION == 5
+    assert B.asp_abi_version() == B.ABI_VERSION == 6
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"

@@ -139,7 +139,9 @@ def prep_cases():
     # 32 or more blocks: 8 slices of K for rank <= 32, 4 for rank 64
     s8 = synth.make_layer("f32-8slices", 7, 4096, 32, 16, seed=12, dtype="f32")
     s4 = synth.make_layer("r64-4slices", 9, 4096, 32, 64, seed=13, dtype="bf16")
-    return [c0, c1, c2, r0, r16, r64, r64k, f32k, s8, s4]
+    f64 = synth.make_layer("f32-r64", 70, 1024, 32, 64, seed=16, dtype="f32")
+    big = synth.make_layer("big-batch", 600, 1024, 32, 32, seed=17, dtype="bf16")
+    return [c0, c1, c2, r0, r16, r64, r64k, f32k, s8, s4, f64, big]
 
 
 @pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
@@ -163,8 +165,7 @@ def test_act_prep_against_oracle(lay):
     assert np.mean(xs != act["x_scales"]) <= 1e-3
 
 
-@pytest.mark.parametrize("lay", prep_cases()[:3] + prep_cases()[3:4] + prep_cases()[7:],
-                         ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
+@pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
 def test_act_prep_stages_equal_combined(lay):
     """asp_act_prep_u then asp_act_prep_q reproduce asp_act_prep bit for bit."""
     M, K, r = lay.M, lay.K, lay.r

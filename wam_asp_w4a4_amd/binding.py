@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
 
 ASP_F32 = 0

@@ -133,7 +133,7 @@ using namespace asp;
 
 extern "C" {
 
-int32_t asp_abi_version(void) { return 5; }
+int32_t asp_abi_version(void) { return 6; }
 
 const char* asp_status_string(int32_t status) {
   switch (status) {
