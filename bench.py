@@ -252,6 +252,28 @@ def main():
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
+    # spread: the same graph replayed a few more times (value keeps the first)
+    replays = [ms_per_step]
+    for _ in range(4):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        replays.append(e0.elapsed_time(e1) / args.steps)
+    replays.sort()
+
+    # secondary bandwidth denominator: a plain 256 MiB device-to-device copy
+    csrc = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 3 * COPY_CALIBRATION_BYTES / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del csrc, cdst
 
     flops_step = sum(layer_flops(l.M, l.N, l.K, l.r) for l, _, _ in host)
     bytes_step = sum(layer_bytes(l.M, l.N, l.K, l.r, 2 if l.x_dtype == "bf16" else 4, yb)
@@ -314,6 +336,14 @@ def main():
         "algorithmic_flops_per_launch": nflops // n_launch,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "mfma_f16_frac": round(tfs / F16_PEAK_TFLOPS, 4),
+        # the roofline the kernel's arithmetic intensity allows, min(P, AI * BW)
+        "attainable": round(min(F16_PEAK_TFLOPS, nflops / nbytes * HBM_PEAK_GBS / 1e3), 2)
+        if roof["bound"] == "mfma" else HBM_PEAK_GBS,
+        "frac_of_attainable": round((tfs if roof["bound"] == "mfma" else gbs)
+                                    / (min(F16_PEAK_TFLOPS, nflops / nbytes * HBM_PEAK_GBS / 1e3)
+                                       if roof["bound"] == "mfma" else HBM_PEAK_GBS), 4),
+        "copy_GBps": round(copy_gbs, 1),
+        "hbm_frac_of_copy": round(gbs / copy_gbs, 4),
         "kernels": {k[0]: {"avg_launch_us": round(k[2] / k[3] * 1e3, 3),
                            "frac": roofline_of(k[4], k[5], k[2])[0]["frac"],
                            "bound": roofline_of(k[4], k[5], k[2])[0]["bound"]} for k in timed},
@@ -349,6 +379,8 @@ def main():
             "replicas": R,
             "replica_bytes": per,
             "timing": "one HIP graph of K steps, events on the capture stream",
+            "ms_per_step_replays": {"min": round(replays[0], 6), "median": round(replays[2], 6),
+                                    "max": round(replays[-1], 6), "replays": len(replays)},
         },
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -376,6 +408,7 @@ def cpu_baseline(layers, budget_s):
         if el >= budget_s or n >= 1000:
             break
     return {"value": round(flops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "affinity_cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"{n} full steps of the same workload (float64 NumPy oracle, weights "
                       f"pre-packed), {el:.1f} s; cores = BLAS threads"}
