@@ -116,6 +116,22 @@ int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
                         int32_t n_threads);
 
 /*
+ * The shared-weight arm of the same page ("What ASP is, and what the
+ * deflated form means": the variant that quantises one weight and stores V
+ * alone).  Reading taken: the 4-bit weight is W_tilde itself (not deflated),
+ * and the low-rank factor is derived from that one quantised weight, L =
+ * DQ(Q(W_tilde)) V (decoded exactly, products in float64, rounded to bf16).
+ * Arguments, layouts and the device path (asp_forward with the same
+ * activation prep) as for asp_pack_weight; w_prequant receives float32(W_tilde).
+ * Without quantisation it also reduces to x W^T + b, since the projector is
+ * needed on one side only.
+ */
+int32_t asp_pack_weight_shared(int64_t N, int64_t K, int32_t r, const float* w,
+                               const float* s, const float* v, uint8_t* w_codes,
+                               uint8_t* w_scales, uint16_t* wv, float* w_prequant,
+                               int32_t n_threads);
+
+/*
  * NVFP4 quantiser on the host (the packer's last step, exposed for checks):
  * rows x cols float32 -> codes (rows x cols/2) and scales (rows x cols/16).
  * cols must be a positive multiple of 16.  All pointers host.

@@ -30,6 +30,14 @@ x: M x K, W: N x K, y = x W^T + b):
 
 ``quantize=False`` replaces NVFP4 quantise/dequantise and the bf16 roundings
 by the identity; then y equals x W^T + b up to float64 rounding.
+
+The same section names a cheaper shared-weight arm, which quantises one weight
+and stores V alone (``form="shared"``).  Reading taken: the 4-bit weight is
+W_tilde itself, not deflated, and the low-rank factor is derived from that one
+quantised weight, L = DQ(Q(W_tilde)) V.  The activation side is the same.
+Without quantisation it also gives x W^T + b: (x_tilde V)(W_tilde V)^T +
+(x_tilde - x_tilde V V^T) W_tilde^T = x_tilde W_tilde^T, the projector being
+needed on one side only.
 """
 
 import numpy as np
@@ -71,30 +79,43 @@ def _basis(v, k):
     return v
 
 
-def pack_weight(w, s, v=None, block: int = HADAMARD_BLOCK):
+def pack_weight(w, s, v=None, block: int = HADAMARD_BLOCK, form: str = "deflated"):
     """Weight side, done once per layer.
 
-    W_tilde = W diag(s) H;  L = W_tilde V;  W_d = W_tilde - L V^T;
+    Deflated arm: W_tilde = W diag(s) H;  L = W_tilde V;  W_d = W_tilde - L V^T;
     NVFP4(float32(W_d)) row-wise along K;  L kept as bf16.
+    Shared arm: NVFP4(float32(W_tilde));  L = DQ(that) V, kept as bf16.
     Returns a dict with the codes, scales, bf16 low-rank factor (float64 array
-    holding bf16 values, N x r) and the intermediates.
+    holding bf16 values, N x r) and the intermediates; "w_4bit" and "low_rank"
+    are the unquantised weight of the 4-bit path and low-rank factor.
     """
+    if form not in ("deflated", "shared"):
+        raise ValueError(f"unknown weight form {form!r}")
     w = np.asarray(w, dtype=np.float64)
     s = np.asarray(s, dtype=np.float64)
     n, k = w.shape
     vb = _basis(v, k)
     w_tilde = block_rotate(w * s[None, :], block)
-    low_rank = w_tilde @ vb
-    w_defl = w_tilde - low_rank @ vb.T
-    w_pre = round_fp32(w_defl)
-    codes, scales = formats.quantize_nvfp4(w_pre)
+    if form == "deflated":
+        low_rank = w_tilde @ vb
+        w_4bit = w_tilde - low_rank @ vb.T
+        w_pre = round_fp32(w_4bit)
+        codes, scales = formats.quantize_nvfp4(w_pre)
+        lr_stored = low_rank
+    else:
+        low_rank = w_tilde @ vb
+        w_4bit = w_tilde
+        w_pre = round_fp32(w_4bit)
+        codes, scales = formats.quantize_nvfp4(w_pre)
+        lr_stored = formats.dequantize_nvfp4(codes, scales) @ vb
     return {
         "w_codes": codes,
         "w_scales": scales,
-        "wv": round_bf16(low_rank),
+        "wv": round_bf16(lr_stored),
         "w_prequant": w_pre,
         "w_tilde": w_tilde,
-        "w_deflated": w_defl,
+        "w_4bit": w_4bit,
+        "w_deflated": w_tilde - low_rank @ vb.T,
         "low_rank": low_rank,
     }
 
@@ -142,16 +163,17 @@ def output_from_codes(x_codes, x_scales, u, w_codes, w_scales, wv, bias=None):
 
 
 def forward(x, w, bias, s, v=None, quantize: bool = True, packed=None,
-            block: int = HADAMARD_BLOCK):
-    """y (float64, M x N) of the deflated ASP linear for the inputs given.
+            block: int = HADAMARD_BLOCK, form: str = "deflated"):
+    """y (float64, M x N) of the ASP linear (deflated or shared-weight arm) for
+    the inputs given.
 
-    ``packed`` may hold an earlier ``pack_weight`` result for the same (w, s, v).
+    ``packed`` may hold an earlier ``pack_weight`` result for the same (w, s, v, form).
     """
     if packed is None:
-        packed = pack_weight(w, s, v, block)
+        packed = pack_weight(w, s, v, block, form)
     act = activation_side(x, s, v, block)
     if not quantize:
-        y = act["x_deflated"] @ packed["w_deflated"].T + act["u"] @ packed["low_rank"].T
+        y = act["x_deflated"] @ packed["w_4bit"].T + act["u"] @ packed["low_rank"].T
         if bias is not None:
             y = y + np.asarray(bias, dtype=np.float64)[None, :]
         return y

@@ -393,3 +393,33 @@ def test_forward_group(M, K, r, Ns, dtype):
             assert np.array_equal(a, alone)        # one launch or several: the same bits
         else:
             assert rel_fro(a, alone) <= 1e-5       # only the float32 summation order differs
+
+
+# ------------------------------------------------------- shared-weight arm
+
+
+@pytest.mark.parametrize("lay", [synth.workload(0)[0], synth.workload(1)[0],
+                                 synth.make_layer("ragged", 77, 384, 200, 24, seed=18, dtype="f32")],
+                         ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-N{l.N}-r{l.r}")
+def test_forward_shared_weight_arm(lay):
+    """The shared-weight packing through the same device path: the 2e-3 gate
+    against the float64 oracle of that arm, and 1e-5 against the oracle's
+    contraction of the device's own activation codes and u."""
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV, form="shared")
+    x = x_device(lay)
+    y32 = host(p.forward(x, "f32"))
+    y16 = host(p.forward(x, "bf16").float())
+    want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v, form="shared")
+    e32, e16 = rel_fro(y32, want), rel_fro(y16, want)
+    pk = OA.pack_weight(lay.w, lay.s, lay.v, form="shared")
+    xc, xs, u, _ = gpu_act_prep(lay)
+    mine = OA.output_from_codes(xc, xs, u.astype(np.float64), pk["w_codes"], pk["w_scales"],
+                                pk["wv"], lay.b)
+    tight = rel_fro(y32, mine)
+    dfl = rel_fro(host(PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV).forward(x, "f32")),
+                  OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v, quantize=False))
+    shr = rel_fro(y32, OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v, quantize=False))
+    print(f"shared arm {lay.name}: vs oracle fp32 {e32:.2e} bf16 {e16:.2e}, own codes {tight:.1e}; "
+          f"error vs the unquantised layer: shared {shr:.3e}, deflated {dfl:.3e}")
+    assert e32 <= 2e-3 and e16 <= 2e-3
+    assert tight <= 1e-5

@@ -110,6 +110,22 @@ def test_packer_matches_oracle(cfg):
         assert np.mean(p["wv"] != wv) <= 1e-4
 
 
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_packer_shared_weight_matches_oracle(cfg):
+    for lay in synth.workload(cfg):
+        p = PackedLayer.pack_host(lay.w, lay.s, lay.v, want_prequant=True, form="shared")
+        oc, os_ = OF.quantize_nvfp4(p["w_prequant"])
+        assert np.array_equal(p["w_codes"], oc) and np.array_equal(p["w_scales"], os_)
+        o = OA.pack_weight(lay.w, lay.s, lay.v, form="shared")
+        assert np.mean(p["w_prequant"] != o["w_prequant"]) <= 1e-5
+        assert np.mean(p["w_codes"] != o["w_codes"]) <= 1e-5
+        wv = synth.bf16_bits(o["wv"].astype(np.float32))
+        assert np.mean(p["wv"] != wv) <= 1e-4
+        # the one weight's codes are the rank-0 packer's
+        p0 = PackedLayer.pack_host(lay.w, lay.s, None)
+        assert np.array_equal(p["w_codes"], p0["w_codes"])
+
+
 def test_packer_rank_zero_and_threads():
     lay = synth.make_layer("r0", 4, 256, 48, 0, seed=5, dtype="f32")
     p1 = PackedLayer.pack_host(lay.w, lay.s, None, n_threads=1)

@@ -179,7 +179,7 @@ def _bf_quant_block(vals):
     return out
 
 
-def _bf_forward(x, w, b, s, v):
+def _bf_forward(x, w, b, s, v, shared=False):
     m, k = x.shape
     n = w.shape[0]
     r = 0 if v is None else v.shape[1]
@@ -206,7 +206,19 @@ def _bf_forward(x, w, b, s, v):
         return u, q
 
     wt = [rot([float(w[o, i]) * float(s[i]) for i in range(k)]) for o in range(n)]
-    wside = [side(row) for row in wt]
+    if not shared:
+        wside = [side(row) for row in wt]
+    else:
+        # shared-weight arm: the rotated weight itself is quantised, and the
+        # low-rank factor is that decoded weight times V
+        wside = []
+        for row in wt:
+            r32 = np.array(row, dtype=np.float32)
+            q = []
+            for blk in range(k // 16):
+                q += _bf_quant_block(r32[blk * 16:(blk + 1) * 16])
+            lw = [sum(q[i] * vv[i][c] for i in range(k)) for c in range(r)]
+            wside.append((lw, q))
     y = np.zeros((m, n))
     for a in range(m):
         xt = rot([float(x[a, i]) / float(s[i]) for i in range(k)])
@@ -226,6 +238,47 @@ def test_brute_force_tiny_layers(m, r):
     y = A.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
     yb = _bf_forward(lay.x, lay.w, lay.b, lay.s, lay.v)
     assert np.abs(y - yb).max() <= 1e-9 * np.abs(yb).max()
+
+
+@pytest.mark.parametrize("m,r", [(1, 1), (2, 3)])
+def test_brute_force_tiny_layers_shared_weight(m, r):
+    lay = synth.make_layer("tiny", m, 128, 16, r, seed=200 + 10 * m + r, dtype="f32")
+    y = A.forward(lay.x, lay.w, lay.b, lay.s, lay.v, form="shared")
+    yb = _bf_forward(lay.x, lay.w, lay.b, lay.s, lay.v, shared=True)
+    assert np.abs(y - yb).max() <= 1e-9 * np.abs(yb).max()
+
+
+# ------------------------------------------------------- shared-weight arm
+
+
+@pytest.mark.parametrize("rank", [0, 32])
+def test_shared_weight_quantization_off_identity(layer0, rank):
+    # the projector on the activation side alone already makes the two terms sum to x W^T
+    v = _orthonormal(layer0.v)[:, :rank] if rank else None
+    y = A.forward(layer0.x, layer0.w, layer0.b, layer0.s, v, quantize=False, form="shared")
+    ref = layer0.x.astype(np.float64) @ layer0.w.astype(np.float64).T + layer0.b
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 1e-12
+
+
+def test_shared_weight_codes_are_the_undeflated_weight(layer0):
+    # one weight: its codes are those of the rank-0 (no subspace) packer
+    sh = A.pack_weight(layer0.w, layer0.s, layer0.v, form="shared")
+    r0 = A.pack_weight(layer0.w, layer0.s, None)
+    assert np.array_equal(sh["w_codes"], r0["w_codes"])
+    assert np.array_equal(sh["w_scales"], r0["w_scales"])
+    dfl = A.pack_weight(layer0.w, layer0.s, layer0.v)
+    assert not np.array_equal(sh["w_codes"], dfl["w_codes"])
+
+
+def test_shared_weight_equals_deflated_without_subspace(layer0):
+    a = A.forward(layer0.x, layer0.w, layer0.b, layer0.s, None, form="shared")
+    b = A.forward(layer0.x, layer0.w, layer0.b, layer0.s, None)
+    assert np.array_equal(a, b)
+
+
+def test_unknown_weight_form_rejected(layer0):
+    with pytest.raises(ValueError):
+        A.pack_weight(layer0.w, layer0.s, layer0.v, form="other")
 
 
 # ------------------------------------------------------- residency figures

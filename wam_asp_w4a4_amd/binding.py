@@ -34,6 +34,7 @@ SIGNATURES = {
     "asp_gemm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
     "asp_packed_sizes": (_i32, [_i64, _i64, _i32, _psz, _psz, _psz]),
     "asp_pack_weight": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32]),
+    "asp_pack_weight_shared": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i32]),
     "asp_quantize_nvfp4_host": (_i32, [_p, _i64, _i64, _p, _p]),
     "asp_prep_pack_bytes": (_i32, [_i64, _i32, _psz]),
     "asp_pack_prep": (_i32, [_i64, _i32, _p, _p, _p]),
@@ -148,6 +149,12 @@ def asp_pack_prep(K, r, s, v, prep_pack):
 def asp_pack_weight(N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant=None, n_threads=0):
     _check(lib().asp_pack_weight(N, K, r, _ptr(w), _ptr(s), _ptr(v), _ptr(w_codes),
                                  _ptr(w_scales), _ptr(wv), _ptr(w_prequant), n_threads))
+
+
+def asp_pack_weight_shared(N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant=None,
+                           n_threads=0):
+    _check(lib().asp_pack_weight_shared(N, K, r, _ptr(w), _ptr(s), _ptr(v), _ptr(w_codes),
+                                        _ptr(w_scales), _ptr(wv), _ptr(w_prequant), n_threads))
 
 
 def asp_quantize_nvfp4_host(inp, rows, cols, codes, scales):

@@ -101,6 +101,7 @@ struct PackJob {
   uint8_t *codes, *scales;
   uint16_t* wv;
   float* pre;
+  bool shared;  // the shared-weight arm: W_tilde itself is quantised, L = DQ(W_q) V
 };
 
 static void pack_rows(const PackJob& j, int64_t row0, int64_t row1) {
@@ -112,16 +113,30 @@ static void pack_rows(const PackJob& j, int64_t row0, int64_t row1) {
     const float* wr = j.w + n * K;
     for (int64_t k = 0; k < K; ++k) t[k] = (double)wr[k] * (double)j.s[k];
     for (int64_t b = 0; b < K; b += 128) fwht128(&t[b]);
+    uint8_t* crow = j.codes + n * (K / 2);
+    uint8_t* srow = j.scales + n * (K / 16);
     for (int c = 0; c < r; ++c) low[c] = 0.0;
-    for (int64_t k = 0; k < K; ++k)
-      for (int c = 0; c < r; ++c) low[c] += t[k] * (double)j.v[k * r + c];
-    for (int64_t k = 0; k < K; ++k) {
-      double d = t[k];
-      double proj = 0.0;
-      for (int c = 0; c < r; ++c) proj += low[c] * (double)j.v[k * r + c];
-      d32[k] = (float)(d - proj);
+    if (!j.shared) {
+      for (int64_t k = 0; k < K; ++k)
+        for (int c = 0; c < r; ++c) low[c] += t[k] * (double)j.v[k * r + c];
+      for (int64_t k = 0; k < K; ++k) {
+        double d = t[k];
+        double proj = 0.0;
+        for (int c = 0; c < r; ++c) proj += low[c] * (double)j.v[k * r + c];
+        d32[k] = (float)(d - proj);
+      }
+      quantize_row(d32.data(), K, crow, srow);
+    } else {
+      // one weight: W_tilde itself; the low-rank factor is that quantised
+      // weight (decoded exactly) times V
+      for (int64_t k = 0; k < K; ++k) d32[k] = (float)t[k];
+      quantize_row(d32.data(), K, crow, srow);
+      for (int64_t k = 0; k < K; ++k) {
+        const uint32_t code = (crow[k >> 1] >> (4 * (k & 1))) & 0xFu;
+        const double dq = (double)e2m1_decode(code) * (double)e4m3_decode(srow[k >> 4]);
+        for (int c = 0; c < r; ++c) low[c] += dq * (double)j.v[k * r + c];
+      }
     }
-    quantize_row(d32.data(), K, j.codes + n * (K / 2), j.scales + n * (K / 16));
     for (int c = 0; c < r; ++c) j.wv[n * r + c] = bf16_from_double(low[c]);
     if (j.pre) memcpy(j.pre + n * K, d32.data(), K * sizeof(float));
   }
@@ -225,9 +240,10 @@ int32_t asp_quantize_nvfp4_host(const float* in, int64_t rows, int64_t cols,
   return ASP_OK;
 }
 
-int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w, const float* s,
-                        const float* v, uint8_t* w_codes, uint8_t* w_scales, uint16_t* wv,
-                        float* w_prequant, int32_t n_threads) {
+static int32_t pack_weight_impl(bool shared, int64_t N, int64_t K, int32_t r, const float* w,
+                                const float* s, const float* v, uint8_t* w_codes,
+                                uint8_t* w_scales, uint16_t* wv, float* w_prequant,
+                                int32_t n_threads) {
   clear_error();
   if (int32_t st = check_k(K)) return st;
   if (int32_t st = check_rank(r)) return st;
@@ -237,7 +253,7 @@ int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w, const f
   for (int64_t k = 0; k < K; ++k)
     if (!(s[k] > 0.0f) || !isfinite(s[k]))
       return fail(ASP_ERR_ARG, "s[%lld]=%g must be finite and > 0", (long long)k, (double)s[k]);
-  PackJob job{N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant};
+  PackJob job{N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant, shared};
   int64_t nt = n_threads > 0 ? n_threads : (int64_t)std::thread::hardware_concurrency();
   nt = std::max<int64_t>(1, std::min<int64_t>(nt, N));
   if (nt == 1) {
@@ -253,6 +269,18 @@ int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w, const f
   }
   for (auto& th : pool) th.join();
   return ASP_OK;
+}
+
+int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w, const float* s,
+                        const float* v, uint8_t* w_codes, uint8_t* w_scales, uint16_t* wv,
+                        float* w_prequant, int32_t n_threads) {
+  return pack_weight_impl(false, N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant, n_threads);
+}
+
+int32_t asp_pack_weight_shared(int64_t N, int64_t K, int32_t r, const float* w, const float* s,
+                               const float* v, uint8_t* w_codes, uint8_t* w_scales,
+                               uint16_t* wv, float* w_prequant, int32_t n_threads) {
+  return pack_weight_impl(true, N, K, r, w, s, v, w_codes, w_scales, wv, w_prequant, n_threads);
 }
 
 }  // extern "C"

@@ -28,8 +28,11 @@ class PackedLayer:
 
     @staticmethod
     def pack_host(w: np.ndarray, s: np.ndarray, v: np.ndarray | None, n_threads: int = 0,
-                  want_prequant: bool = False) -> dict:
-        """Run the host packer; returns NumPy buffers."""
+                  want_prequant: bool = False, form: str = "deflated") -> dict:
+        """Run the host packer; returns NumPy buffers.  form: "deflated" (the
+        deployed arm) or "shared" (one quantised weight, L = DQ(W_q) V)."""
+        if form not in ("deflated", "shared"):
+            raise ValueError(f"unknown weight form {form!r}")
         w = np.ascontiguousarray(w, dtype=np.float32)
         s = np.ascontiguousarray(s, dtype=np.float32)
         n, k = w.shape
@@ -43,8 +46,9 @@ class PackedLayer:
             "w_prequant": np.empty((n, k), np.float32) if want_prequant else None,
         }
         assert out["w_codes"].nbytes == nc and out["w_scales"].nbytes == ns
-        B.asp_pack_weight(n, k, r, w, s, v, out["w_codes"], out["w_scales"], out["wv"],
-                          out["w_prequant"], n_threads)
+        pack = B.asp_pack_weight if form == "deflated" else B.asp_pack_weight_shared
+        pack(n, k, r, w, s, v, out["w_codes"], out["w_scales"], out["wv"], out["w_prequant"],
+             n_threads)
         out["prep"] = np.empty(B.asp_prep_pack_bytes(k, r), np.uint8)
         B.asp_pack_prep(k, r, s, v, out["prep"])
         return out
@@ -68,8 +72,9 @@ class PackedLayer:
                    up(None if bias is None else np.asarray(bias, np.float32)))
 
     @classmethod
-    def pack(cls, w, s, v, bias, device="cuda", n_threads: int = 0) -> "PackedLayer":
-        return cls.from_host(cls.pack_host(w, s, v, n_threads), bias, device)
+    def pack(cls, w, s, v, bias, device="cuda", n_threads: int = 0,
+             form: str = "deflated") -> "PackedLayer":
+        return cls.from_host(cls.pack_host(w, s, v, n_threads, form=form), bias, device)
 
     def workspace(self, M: int) -> torch.Tensor:
         n = B.asp_workspace_bytes(M, self.N, self.K, self.r)
