@@ -116,9 +116,9 @@ int32_t asp_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
                         int32_t n_threads);
 
 /*
- * The shared-weight arm of the same page ("What ASP is, and what the
- * deflated form means": the variant that quantises one weight and stores V
- * alone).  Reading taken: the 4-bit weight is W_tilde itself (not deflated),
+ * The shared-weight arm of the same page (section "What ASP is, and what
+ * the deflated form means": a cheaper variant with a single 4-bit weight and
+ * only the basis V kept beside it).  Reading taken: the 4-bit weight is W_tilde itself (not deflated),
  * and the low-rank factor is derived from that one quantised weight, L =
  * DQ(Q(W_tilde)) V (decoded exactly, products in float64, rounded to bf16).
  * Arguments, layouts and the device path (asp_forward with the same

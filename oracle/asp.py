@@ -31,8 +31,8 @@ x: M x K, W: N x K, y = x W^T + b):
 ``quantize=False`` replaces NVFP4 quantise/dequantise and the bf16 roundings
 by the identity; then y equals x W^T + b up to float64 rounding.
 
-The same section names a cheaper shared-weight arm, which quantises one weight
-and stores V alone (``form="shared"``).  Reading taken: the 4-bit weight is
+The same section mentions a cheaper shared-weight arm that keeps a single 4-bit
+weight with only the basis V beside it (``form="shared"``).  Reading taken: the 4-bit weight is
 W_tilde itself, not deflated, and the low-rank factor is derived from that one
 quantised weight, L = DQ(Q(W_tilde)) V.  The activation side is the same.
 Without quantisation it also gives x W^T + b: (x_tilde V)(W_tilde V)^T +
