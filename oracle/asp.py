@@ -11,8 +11,8 @@ Hadamard, V the rank-32 basis and W_tilde the smoothed weight,
 
 "Deflated" means the protected subspace is removed from the 4-bit path on both
 sides; the low-rank branch holds the exact W_tilde V and stays in bf16.  The
-same page's verification section attributes its per-layer error to "the bf16
-output cast".  The Q-WAM abstract describes the same split: a 16-bit low-rank
+same page's verification section puts its per-layer error down to rounding the
+output to bf16.  The Q-WAM abstract describes the same split: a 16-bit low-rank
 branch plus the 4-bit complement of weights and activations.
 
 Readings taken where the page is silent or loose (row-vector convention,
@@ -32,8 +32,8 @@ x: M x K, W: N x K, y = x W^T + b):
 by the identity; then y equals x W^T + b up to float64 rounding.
 
 The same section mentions a cheaper shared-weight arm that keeps a single 4-bit
-weight with only the basis V beside it (``form="shared"``).  Reading taken: the 4-bit weight is
-W_tilde itself, not deflated, and the low-rank factor is derived from that one
+weight with only the basis V beside it (``form="shared"``).  Reading taken:
+the 4-bit weight is W_tilde itself, not deflated, and the low-rank factor is derived from that one
 quantised weight, L = DQ(Q(W_tilde)) V.  The activation side is the same.
 Without quantisation it also gives x W^T + b: (x_tilde V)(W_tilde V)^T +
 (x_tilde - x_tilde V V^T) W_tilde^T = x_tilde W_tilde^T, the projector being
