@@ -112,6 +112,9 @@ def parse():
     ap.add_argument("--kernel-timing-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--search", action="store_true",
+                    help="time the per-layer smoothing search (the 39-candidate grid) on the "
+                         "workload's first layer instead of the forward step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (the reference "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -162,6 +165,9 @@ def main():
     torch.cuda.set_device(dev)
 
     layers = synth.workload(args.workload)
+    if args.search:
+        search_bench(args, layers[0], dev)
+        return
     y_dtype = "bf16"
     yb = 2
 
@@ -383,6 +389,48 @@ def main():
                                     "max": round(replays[-1], 6), "replays": len(replays)},
         },
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def search_bench(args, lay, dev):
+    """Wall time of the per-layer smoothing search (host packing of every candidate
+    plus the device forward and error per candidate), and the oracle's search on a
+    bounded subset of the same grid."""
+    import torch
+    from wam_asp_w4a4_amd import synth
+    from wam_asp_w4a4_amd.layer import smoothing_grid, smoothing_search
+    xh = synth.bf16_bits(lay.x) if lay.x_dtype == "bf16" else lay.x
+    x = torch.from_numpy(np.ascontiguousarray(xh))
+    x = (x.view(torch.bfloat16) if lay.x_dtype == "bf16" else x).to(dev)
+    grid = smoothing_grid()
+    smoothing_search(x, lay.w, lay.b, lay.v, grid[:2])  # warm-up (code objects, pools)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a, b, mse, best = smoothing_search(x, lay.w, lay.b, lay.v, grid)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    cpu = None
+    if args.cpu_seconds > 0:
+        from oracle import smoothing as oracle_smoothing
+        n = 0
+        t1 = time.perf_counter()
+        while n < len(grid) and time.perf_counter() - t1 < args.cpu_seconds:
+            oracle_smoothing.search(lay.x, lay.w, lay.b, lay.v, [grid[n]])
+            n += 1
+        cel = time.perf_counter() - t1
+        cpu = {"value": round(n / cel, 4), "unit": "candidates/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"{n} of the {len(grid)} candidates, {cel:.1f} s"}
+    out = {
+        "metric": "per-layer smoothing search, candidates per second",
+        "value": round(len(grid) / el, 3), "unit": "candidates/s", "n_gpus": 1,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": synth.WORKLOADS[args.workload], "layer": lay.name, "M": lay.M,
+                   "K": lay.K, "N": lay.N, "r": lay.r, "candidates": len(grid),
+                   "seconds": round(el, 4), "best": [a, b],
+                   "note": "each candidate: host float64 packing of the weight, upload, "
+                           "device forward and squared-error reduction"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -312,6 +312,39 @@ int32_t asp_forward_group_stages(int32_t stages, int32_t n_layers,
                                  void* const* workspace,
                                  const size_t* workspace_bytes, void* stream);
 
+/* ------------------------------------------------------- calibration */
+
+/*
+ * Per-layer smoothing search (model card, section "What ASP is, and what the
+ * deflated form means": the smoothing exponents of each layer are picked
+ * from a grid by that layer's own deflated-ASP NVFP4 output error on
+ * calibration activations).  For candidate c the smoothing vector is
+ *     s_k = max_m |x_mk|^alphas[c] / max_n |W_nk|^betas[c]
+ * in float64 (a zero maximum replaced by 1e-5), rounded to float32; the weight
+ * is packed with it (asp_pack_weight, host), the layer runs on the device
+ * (asp_forward, float32 output) and mse[c] is the mean over the M x N outputs
+ * of the squared difference to the unquantised x W^T + b (a float32 GEMM on
+ * the device; squares summed in float64 in a fixed order, so the result is
+ * deterministic).  *best = the index of the smallest mse (ties: the earlier).
+ * Runs on `stream` and synchronises it before returning (offline use).
+ *   x              device, M x K calibration activations (x_dtype)
+ *   w, bias, v     host float32: N x K, N or NULL, K x r (NULL iff r == 0)
+ *   alphas, betas  host, n_candidates each
+ *   mse, best      host out, n_candidates doubles and one index
+ *   workspace      device, asp_smoothing_search_workspace_bytes bytes,
+ *                  256-byte aligned
+ */
+int32_t asp_smoothing_search_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                             int32_t r, int32_t n_candidates,
+                                             size_t* bytes);
+int32_t asp_smoothing_search(const void* x, int32_t x_dtype, int64_t M,
+                             int64_t K, const float* w, const float* bias,
+                             int64_t N, const float* v, int32_t r,
+                             const float* alphas, const float* betas,
+                             int32_t n_candidates, double* mse,
+                             int32_t* best, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

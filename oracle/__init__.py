@@ -18,11 +18,13 @@ Modules:
   formats  -- E2M1 / E4M3FN codecs (round-to-nearest-even, saturating) and the
               NVFP4 block quantiser / dequantiser.
   hadamard -- Sylvester Hadamard matrices and the block Hadamard rotation.
-  asp      -- fp64/fp32/bf16 rounding helpers, the weight side (pack), the
-              activation side and the layer forward.
+  asp      -- fp64/fp32/bf16 rounding helpers, the weight side (pack; the
+              deflated and the shared-weight arm), the activation side and the
+              layer forward.
+  smoothing -- the per-layer (alpha, beta) smoothing search.
 
 Every function here is pinned by tests under ``tests/test_oracle_*.py`` against
 closed forms, hand-derived vectors (``tests/golden/``), invariants and brute force.
 """
 
-from . import formats, hadamard, asp  # noqa: F401
+from . import formats, hadamard, asp, smoothing  # noqa: F401

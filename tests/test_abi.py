@@ -187,6 +187,34 @@ def test_forward_group_validation():
                                  None) == 0
 
 
+def test_smoothing_search_validation():
+    lib = B.lib()
+    need = B.asp_smoothing_search_workspace_bytes(8, 64, 256, 32, 3)
+    assert need > 0
+    w = np.zeros((64, 256), np.float32)
+    v = np.zeros((256, 32), np.float32)
+    al = np.zeros(3, np.float32)
+    mse = np.zeros(3, np.float64)
+    best = ctypes.c_int32(0)
+    P = ctypes.c_void_p
+
+    def call(x=FAKE, K=256, wp=w.ctypes.data, vp=v.ctypes.data, ws=FAKE, nb=need, n=3):
+        return lib.asp_smoothing_search(x, 1, 8, K, wp, None, 64, vp, 32, al.ctypes.data,
+                                        al.ctypes.data, n, mse.ctypes.data,
+                                        ctypes.cast(ctypes.byref(best), P).value, ws, nb, None)
+
+    assert call(K=100) == 2
+    assert call(n=0) == 1
+    assert call(wp=None) == 1
+    assert call(vp=None) == 1
+    assert call(x=None) == 1
+    assert call(x=MIS) == 3
+    assert call(ws=FAKE + 16) == 3
+    assert call(nb=need - 1) == 5
+    with pytest.raises(B.ASPError):
+        B.asp_smoothing_search_workspace_bytes(8, 64, 256, 32, 0)
+
+
 def test_host_quantizer_validation():
     a = np.zeros((2, 24), np.float32)
     with pytest.raises(B.ASPError):

@@ -423,3 +423,30 @@ def test_forward_shared_weight_arm(lay):
           f"error vs the unquantised layer: shared {shr:.3e}, deflated {dfl:.3e}")
     assert e32 <= 2e-3 and e16 <= 2e-3
     assert tight <= 1e-5
+
+
+# ------------------------------------------------- per-layer smoothing search
+
+
+@pytest.mark.parametrize("lay,step", [(synth.workload(0)[0], 1), (synth.workload(1)[0], 3)],
+                         ids=["single-M64-K512", "attn-M256-K1024"])
+def test_smoothing_search_against_oracle(lay, step):
+    """The device search's error table against the float64 oracle's, and the
+    same choice (or, on a near tie, one the oracle scores as good).  Tolerance:
+    the device output is within ~1e-5 of the oracle's relative to y, the error
+    itself ~7% of y, so each mean squared error agrees to ~3e-4 relative; the
+    gate is 2e-3."""
+    from oracle import smoothing as OS
+    from wam_asp_w4a4_amd.layer import smoothing_grid, smoothing_search
+    assert smoothing_grid() == OS.grid()
+    cands = OS.grid()[::step]
+    x = x_device(lay)
+    a, b, mse, best = smoothing_search(x, lay.w, lay.b, lay.v, cands)
+    omse, obest = OS.search(lay.x, lay.w, lay.b, lay.v, cands)
+    rel = np.abs(mse - omse) / omse
+    print(f"search {lay.name}: {len(cands)} candidates, device best {cands[best]} "
+          f"oracle best {cands[obest]}, max rel diff of the errors {rel.max():.2e}")
+    assert rel.max() <= 2e-3
+    assert best == obest or omse[best] <= omse[obest] * (1 + 2e-3)
+    assert (a, b) == cands[best]
+

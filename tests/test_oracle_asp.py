@@ -302,3 +302,43 @@ def test_residency_matches_model_card():
     assert per_weight_code * 8 == g["code_bits_per_weight"]
     assert round(g["weights"] * per_weight_code / 2 ** 20) == g["code_mib"]
     assert round(g["weights"] * per_weight_scale / 2 ** 20, 1) == g["scale_mib"]
+
+
+# ------------------------------------------------- smoothing search (oracle)
+
+from oracle import smoothing as SM  # noqa: E402
+
+
+def test_smoothing_grid_reading():
+    g = SM.grid()
+    assert len(g) == 39 and len(set(g)) == 39
+    assert g[0] == (0.0, 0.0) and (0.0, 1.0) not in g
+    assert all(b == 0.0 or abs(a + b - 1.0) < 1e-12 for a, b in g)
+    assert sorted({a for a, _ in g}) == [i / 20 for i in range(20)]
+
+
+def test_smoothing_vector_by_hand():
+    # hand values: sqrt(4)/sqrt(1) = 2, sqrt(1)/sqrt(16) = 1/4, zero maxima -> 1e-5 each:
+    # sqrt(1e-5)/sqrt(1e-5) = 1; alpha = 1, beta = 0: the activation maxima themselves
+    s = SM.smoothing_vector([4.0, 1.0, 0.0], [1.0, 16.0, 0.0], 0.5, 0.5)
+    assert np.array_equal(s, np.float32([2.0, 0.25, 1.0]))
+    s = SM.smoothing_vector([3.0, 0.5, 0.0], [7.0, 2.0, 9.0], 1.0, 0.0)
+    assert np.array_equal(s, np.float32([3.0, 0.5, 1e-5]))
+    assert SM.smoothing_vector([5.0], [2.0], 0.0, 0.0)[0] == 1.0
+
+
+def test_smoothing_search_brute_force_tiny():
+    # the error table from the independent brute-force layer
+    lay = synth.make_layer("tiny", 2, 128, 8, 2, seed=301, dtype="f32")
+    cands = [(0.0, 0.0), (0.5, 0.5), (0.9, 0.0)]
+    mse, best = SM.search(lay.x, lay.w, lay.b, lay.v, cands)
+    x64 = lay.x.astype(np.float64)
+    ref = x64 @ lay.w.astype(np.float64).T + lay.b
+    want = []
+    for a, b in cands:
+        xm, wm = np.abs(x64).max(axis=0), np.abs(lay.w.astype(np.float64)).max(axis=0)
+        s = ((xm ** a) / (wm ** b)).astype(np.float32)
+        want.append(np.mean((_bf_forward(lay.x, lay.w, lay.b, s, lay.v) - ref) ** 2))
+    want = np.array(want)
+    assert np.allclose(mse, want, rtol=1e-9, atol=0)
+    assert best == int(np.argmin(want))

@@ -48,6 +48,9 @@ SIGNATURES = {
     "asp_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
     "asp_forward": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32,
                            _p, _sz, _p]),
+    "asp_smoothing_search_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, _psz]),
+    "asp_smoothing_search": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i64, _p, _i32, _p, _p, _i32,
+                                    _p, _p, _p, _sz, _p]),
     "asp_forward_group": (_i32, [_i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p,
                                  _i32, _p, _p, _p]),
     "asp_forward_group_stages": (_i32, [_i32, _i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p,
@@ -209,6 +212,31 @@ def asp_gemm_lowrank(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, wv, bi
     _check(lib().asp_gemm_lowrank(_ptr(x_codes), _ptr(x_scales), _ptr(u), M, N, K, r,
                                   _ptr(w_codes), _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y),
                                   y_dtype, _stream(stream, y)))
+
+
+def asp_smoothing_search_workspace_bytes(M, N, K, r, n_candidates):
+    out = ctypes.c_size_t(0)
+    _check(lib().asp_smoothing_search_workspace_bytes(M, N, K, r, n_candidates, ctypes.byref(out)))
+    return out.value
+
+
+def asp_smoothing_search(x, x_dtype, M, K, w, bias, N, v, r, alphas, betas, workspace,
+                         workspace_bytes, stream=None):
+    """Returns (mse per candidate as a NumPy float64 array, best index)."""
+    # converted copies are held in locals until the call returns
+    alphas = np.ascontiguousarray(alphas, np.float32)
+    betas = np.ascontiguousarray(betas, np.float32)
+    w = np.ascontiguousarray(w, np.float32)
+    bias = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    v = None if v is None else np.ascontiguousarray(v, np.float32)
+    n = len(alphas)
+    mse = np.empty(n, np.float64)
+    best = ctypes.c_int32(0)
+    _check(lib().asp_smoothing_search(
+        _ptr(x), x_dtype, M, K, _ptr(w), _ptr(bias), N, _ptr(v), r, _ptr(alphas), _ptr(betas), n,
+        _ptr(mse), ctypes.cast(ctypes.byref(best), ctypes.c_void_p).value, _ptr(workspace),
+        workspace_bytes, _stream(stream, x)))
+    return mse, int(best.value)
 
 
 def _ptr_array(items):

@@ -118,3 +118,27 @@ def forward_group(layers, x, y_dtype: str = "f32", workspaces=None, ys=None, str
                         [l.bias for l in layers], [l.N for l in layers], ys, B.DTYPES[y_dtype],
                         workspaces, [w.numel() for w in workspaces], stream)
     return ys
+
+
+def smoothing_grid():
+    """The per-layer smoothing candidates (alpha, beta): alpha = 0, 0.05, ..., 0.95
+    with beta = 0, then alpha > 0 with beta = 1 - alpha (39 pairs)."""
+    alphas = [i / 20.0 for i in range(20)]
+    return [(a, 0.0) for a in alphas] + [(a, 1.0 - a) for a in alphas if a > 0.0]
+
+
+def smoothing_search(x, w, bias, v, candidates=None, stream=None):
+    """Pick the layer's smoothing exponents by its own quantised output error on the
+    calibration activations x (device, M x K).  Returns (alpha, beta, mse array, index)."""
+    cands = smoothing_grid() if candidates is None else list(candidates)
+    M, K = x.shape
+    N = w.shape[0]
+    r = 0 if v is None else v.shape[1]
+    x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
+    nbytes = B.asp_smoothing_search_workspace_bytes(M, N, K, r, len(cands))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    mse, best = B.asp_smoothing_search(x, x_dtype, M, K, w, bias, N, v, r,
+                                       [a for a, _ in cands], [b for _, b in cands], ws,
+                                       nbytes, stream)
+    return cands[best][0], cands[best][1], mse, best
+
