@@ -22,9 +22,10 @@ Modules:
               deflated and the shared-weight arm), the activation side and the
               layer forward.
   smoothing -- the per-layer (alpha, beta) smoothing search.
+  eigen    -- the top-r eigenspace of a symmetric PSD metric (the basis V).
 
 Every function here is pinned by tests under ``tests/test_oracle_*.py`` against
 closed forms, hand-derived vectors (``tests/golden/``), invariants and brute force.
 """
 
-from . import formats, hadamard, asp, smoothing  # noqa: F401
+from . import formats, hadamard, asp, smoothing, eigen  # noqa: F401

@@ -104,6 +104,29 @@ def draw_basis(rng, K, r):
     return q.astype(np.float32)
 
 
+def draw_metric(rng, K, decay=8.0, floor=1e-6, rank=None):
+    """Synthetic symmetric PSD K x K metric with a fast-falling spectrum.
+
+    Stands in for a layer's action metric (an expectation of J^T J, which needs
+    the trained model): Q = orthogonal factor of the QR of a K x K N(0, 1) draw,
+    lam_i = exp(-i / decay) + floor for i < rank (rank = K by default) and 0
+    beyond, G = Q diag(lam) Q^T in float64, made exactly symmetric and rounded
+    to float32.  Returns (G float32, lam float64 descending, Q float64).
+    """
+    rank = K if rank is None else rank
+    q, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    i = np.arange(K, dtype=np.float64)
+    lam = np.where(i < rank, np.exp(-i / decay) + floor, 0.0)
+    g = (q * lam) @ q.T
+    g = 0.5 * (g + g.T)
+    return g.astype(np.float32), lam, q
+
+
+def draw_start(rng, K, p):
+    """K x p float32 N(0, 1) starting block for a subspace iteration."""
+    return rng.standard_normal((K, p)).astype(np.float32)
+
+
 def make_layer(name, M, K, N, r, *, seed=DEFAULT_SEED, dtype="bf16",
                outlier_frac=0.01, outlier_gain=20.0, gelu=False, alpha=0.5,
                x=None, v=None) -> Layer:
