@@ -46,10 +46,16 @@ KERNEL_SOURCES = {
     "k_prep_u": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
     "k_prep_q": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
     "k_gemm": ["asp_gemm.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+    "k_eig_gv": ["asp_eig.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
 }
 WORKLOAD_SLUGS = {0: "single_M64_K512_N512", 1: "action_attn_M256_K1024_N1024",
                   2: "action_ffn_M256", 3: "video_attn_M4096_K3072_N3072"}
 COPY_CALIBRATION_BYTES = 256 << 20
+F64_PEAK_TFLOPS = 78.6      # MI355X dense fp64 MFMA
+# the basis solve: the action expert's widest layer input (ffn.2, K = 4096),
+# rank 32 with a block of 64, 8 products with the metric
+EIG_K, EIG_P, EIG_R, EIG_ITERS = 4096, 64, 32, 8
+EIG_SLUG = "metric_K4096_p64"
 
 
 def layer_flops(M, N, K, r):
@@ -115,6 +121,9 @@ def parse():
     ap.add_argument("--search", action="store_true",
                     help="time the per-layer smoothing search (the 39-candidate grid) on the "
                          "workload's first layer instead of the forward step")
+    ap.add_argument("--eigen", action="store_true",
+                    help="time the basis solve instead: the top-32 eigenspace of a synthetic "
+                         "4096 x 4096 action metric (block 64, 8 iterations)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (the reference "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -132,7 +141,8 @@ def kernel_source_digest(kernel):
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{WORKLOAD_SLUGS[workload]}.md")
+    slug = workload if isinstance(workload, str) else WORKLOAD_SLUGS[workload]
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{slug}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -164,6 +174,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.eigen:
+        eigen_bench(args, dev)
+        return
     layers = synth.workload(args.workload)
     if args.search:
         search_bench(args, layers[0], dev)
@@ -431,6 +444,130 @@ def search_bench(args, lay, dev):
                    "seconds": round(el, 4), "best": [a, b],
                    "note": "each candidate: host float64 packing of the weight, upload, "
                            "device forward and squared-error reduction"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def eigen_bench(args, dev):
+    """Solves per second of the top-r eigenspace (subspace iteration, Rayleigh-Ritz)
+    of a synthetic action metric resident in HBM, the metric-product kernel timed
+    alone for the roofline, and the oracle's solve (float64 eigh) on the host."""
+    import torch
+    from wam_asp_w4a4_amd import binding as B
+    from wam_asp_w4a4_amd import synth
+    K, p, r, iters = EIG_K, EIG_P, EIG_R, EIG_ITERS
+    steps = max(1, min(args.steps, 200))
+    warm = max(1, min(args.warmup, 20))
+    rng = np.random.default_rng(synth.DEFAULT_SEED)
+    g, lam, _ = synth.draw_metric(rng, K)
+    v0 = synth.draw_start(rng, K, p)
+    gd = torch.from_numpy(g).to(dev)
+    vd = torch.from_numpy(v0).to(dev)
+    nbytes = B.asp_top_eigenspace_workspace_bytes(K, p, r)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    v = torch.empty((K, r), dtype=torch.float32, device=dev)
+    ev = torch.empty(r, dtype=torch.float32, device=dev)
+    res = torch.empty(r, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def solve():
+        B.asp_top_eigenspace(gd, K, vd, p, r, iters, v, ev, res, ws, nbytes, sp)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(warm):
+        solve()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        solve()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev_h = ev.cpu().numpy().astype(np.float64)
+    err = float(np.max(np.abs(ev_h - lam[:r])) / lam[0])
+
+    # the metric product alone (the kernel the solve spends most of its time in)
+    S = B.asp_top_eigenspace_slices(K, p)
+    v64 = torch.from_numpy(np.linalg.qr(v0.astype(np.float64))[0]).to(dev)
+    yp = torch.empty((S, K, p), dtype=torch.float64, device=dev)
+    n_launch = max(10, min(args.kernel_timing_steps, 400))
+    for _ in range(3):
+        B.asp_metric_product_partials(gd, K, v64, p, yp, sp)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n_launch):
+        B.asp_metric_product_partials(gd, K, v64, p, yp, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kms = e0.elapsed_time(e1) / n_launch
+    kflops = 2 * K * K * p
+    kbytes = 4 * K * K + 8 * K * p + 8 * S * K * p
+    tfs = kflops / (kms * 1e-3) / 1e12
+    gbs = kbytes / (kms * 1e-3) / 1e9
+    ridge = F64_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if kflops / kbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": F64_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfs / F64_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof.update({
+        "traffic": measured_traffic("k_eig_gv", EIG_SLUG),
+        "kernel": f"k_eig_gv<{p}>",
+        "source_digest": kernel_source_digest("k_eig_gv"),
+        "avg_launch_us": round(kms * 1e3, 3),
+        "launches": n_launch,
+        "algorithmic_bytes_per_launch": kbytes,
+        "algorithmic_flops_per_launch": kflops,
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "dtype": "f64 MFMA (float32 metric widened in registers)",
+        "slices": S,
+        "timing": "HIP events on the launch stream around back-to-back launches; the "
+                  "67 MB metric stays in the 256 MB Infinity Cache between launches, as it "
+                  "does between the iterations of a solve",
+    })
+    cpu = None
+    if args.cpu_seconds > 0:
+        from oracle import eigen as oracle_eigen
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+        except Exception:
+            threads = 1
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle_eigen.top_eigenspace(g, r)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n >= 100:
+                break
+        cpu = {"value": round(n / el, 4), "unit": "solves/s", "cores": int(threads),
+               "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{n} full solves of the same metric (float64 NumPy eigh), "
+                         f"{el:.1f} s; cores = BLAS threads"}
+    out = {
+        "metric": f"top-{r} eigenspace of a {K}x{K} action metric, solves per second",
+        "value": round(1e3 / ms, 3), "unit": "solves/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"basis solve: K={K}, block p={p}, r={r}, {iters} products with "
+                               f"G, spectrum exp(-i/8) + 1e-6 (synthetic metric)",
+                   "K": K, "p": p, "r": r, "iters": iters,
+                   "max_eigenvalue_error_rel_lam1": err,
+                   "max_residual": float(res.max().item()),
+                   "timing": "HIP events on the launch stream around back-to-back solves"},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -345,6 +345,60 @@ int32_t asp_smoothing_search(const void* x, int32_t x_dtype, int64_t M,
                              int32_t* best, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * Top-r eigenspace of a layer's action metric: the protected basis V.
+ * Model card "FastWAM UR3 3-task -- 4-bit quantisations", section "What ASP
+ * is, and what the deflated form means": V spans the top eigenspace of the
+ * metric G = E[J^T J] (J: the action's sensitivity to the layer input);
+ * Q-WAM, Figure 3(b): its leading eigenvalues fall quickly.  G itself is the
+ * caller's (it needs the trained model); this finds its leading eigenpairs.
+ *
+ * Subspace iteration on G + mu I (mu = 2^-16 ||G||_F, or 1 when G = 0, so the
+ * iterates keep full rank) from the caller's random start V0, Cholesky QR
+ * after every product, a second Cholesky QR pass, then Rayleigh-Ritz on
+ * G itself (Jacobi rotations on the p x p projection).  All arithmetic is
+ * float64.  Convergence of pair i goes as ((lam_{p+1} + mu)/(lam_i + mu))^iters:
+ * choose p above r and iters from the spectrum's decay; resid reports
+ * ||G v_i - theta_i v_i|| so the caller can check it.
+ *
+ *   g        device float32 K x K, symmetric positive semi-definite (only
+ *            symmetric G is meaningful: its rows are read as its columns)
+ *   K        a positive multiple of 128, at most 65536
+ *   v0       device float32 K x p, full column rank (e.g. N(0, 1) draws)
+ *   p        block width: 16, 32, 48 or 64
+ *   r        1 <= r <= p: eigenpairs returned
+ *   iters    >= 0 products with G before the Rayleigh-Ritz step
+ *   v        device out float32 K x r, orthonormal columns, column i the Ritz
+ *            vector of the i-th largest Ritz value; its entry of largest
+ *            magnitude (first row on ties) is positive
+ *   evals    device out float32 r, largest first; all NaN when the
+ *            orthonormalisation broke down (G not finite, or far from PSD)
+ *   resid    device out float32 r or NULL: ||G v_i - evals_i v_i||_2
+ *   workspace device, asp_top_eigenspace_workspace_bytes bytes, 256-byte
+ *            aligned; overwritten
+ * Results are bitwise reproducible (every reduction has a fixed order).
+ * asp_top_eigenspace_slices reports how many K-slices the G V product uses
+ * (each slice's partial product is summed in a fixed order).
+ */
+int32_t asp_top_eigenspace_workspace_bytes(int64_t K, int32_t p, int32_t r,
+                                           size_t* bytes);
+int32_t asp_top_eigenspace_slices(int64_t K, int32_t p, int32_t* slices);
+/*
+ * The metric product the eigenspace iteration is built on, as K-sliced
+ * partial sums: yp[s] = G[:, slice s] V[slice s, :] for s < S, with
+ * S = asp_top_eigenspace_slices(K, p) equal slices of K, so that
+ * G V = yp[0] + ... + yp[S-1].  float64 MFMA arithmetic.
+ *   g   device float32 K x K (K, p as for asp_top_eigenspace)
+ *   v   device float64 K x p
+ *   yp  device out float64 S x K x p
+ */
+int32_t asp_metric_product_partials(const float* g, int64_t K, const double* v,
+                                    int32_t p, double* yp, void* stream);
+int32_t asp_top_eigenspace(const float* g, int64_t K, const float* v0,
+                           int32_t p, int32_t r, int32_t iters, float* v,
+                           float* evals, float* resid, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

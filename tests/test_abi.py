@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == B.ABI_VERSION == 6
+    assert B.asp_abi_version() == B.ABI_VERSION == 7
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
@@ -213,6 +213,42 @@ def test_smoothing_search_validation():
     assert call(nb=need - 1) == 5
     with pytest.raises(B.ASPError):
         B.asp_smoothing_search_workspace_bytes(8, 64, 256, 32, 0)
+
+
+def test_top_eigenspace_validation():
+    lib = B.lib()
+    need = B.asp_top_eigenspace_workspace_bytes(256, 32, 8)
+    assert need > 0
+    assert B.asp_top_eigenspace_slices(4096, 64) == 8
+    assert B.asp_top_eigenspace_slices(1024, 64) == 4
+    assert B.asp_top_eigenspace_slices(128, 64) == 1
+
+    def call(g=FAKE, K=256, v0=FAKE, p=32, r=8, iters=4, v=FAKE, ev=FAKE, res=None, ws=FAKE,
+             nb=need):
+        return lib.asp_top_eigenspace(g, K, v0, p, r, iters, v, ev, res, ws, nb, None)
+
+    assert call(K=100) == 2
+    assert call(K=128 * 513) == 2
+    assert call(p=24) == 2
+    assert call(p=80) == 2
+    assert call(r=0) == 2
+    assert call(r=33) == 2
+    assert call(iters=-1) == 1
+    assert call(g=None) == 1
+    assert call(v0=None) == 1
+    assert call(v=None) == 1
+    assert call(ev=None) == 1
+    assert call(g=MIS) == 3
+    assert call(res=MIS) == 3
+    assert call(ws=None) == 1
+    assert call(ws=FAKE + 16) == 3
+    assert call(nb=need - 1) == 5
+    with pytest.raises(B.ASPError):
+        B.asp_top_eigenspace_workspace_bytes(256, 32, 40)
+    assert lib.asp_metric_product_partials(FAKE, 100, FAKE, 32, FAKE, None) == 2
+    assert lib.asp_metric_product_partials(FAKE, 256, FAKE, 40, FAKE, None) == 2
+    assert lib.asp_metric_product_partials(None, 256, FAKE, 32, FAKE, None) == 1
+    assert lib.asp_metric_product_partials(FAKE, 256, MIS, 32, FAKE, None) == 3
 
 
 def test_host_quantizer_validation():

@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
 
 ASP_F32 = 0
@@ -51,6 +51,10 @@ SIGNATURES = {
     "asp_smoothing_search_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, _psz]),
     "asp_smoothing_search": (_i32, [_p, _i32, _i64, _i64, _p, _p, _i64, _p, _i32, _p, _p, _i32,
                                     _p, _p, _p, _sz, _p]),
+    "asp_top_eigenspace_workspace_bytes": (_i32, [_i64, _i32, _i32, _psz]),
+    "asp_top_eigenspace_slices": (_i32, [_i64, _i32, ctypes.POINTER(ctypes.c_int32)]),
+    "asp_metric_product_partials": (_i32, [_p, _i64, _p, _i32, _p, _p]),
+    "asp_top_eigenspace": (_i32, [_p, _i64, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
     "asp_forward_group": (_i32, [_i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p,
                                  _i32, _p, _p, _p]),
     "asp_forward_group_stages": (_i32, [_i32, _i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p,
@@ -237,6 +241,30 @@ def asp_smoothing_search(x, x_dtype, M, K, w, bias, N, v, r, alphas, betas, work
         _ptr(mse), ctypes.cast(ctypes.byref(best), ctypes.c_void_p).value, _ptr(workspace),
         workspace_bytes, _stream(stream, x)))
     return mse, int(best.value)
+
+
+def asp_top_eigenspace_workspace_bytes(K, p, r):
+    out = ctypes.c_size_t(0)
+    _check(lib().asp_top_eigenspace_workspace_bytes(K, p, r, ctypes.byref(out)))
+    return out.value
+
+
+def asp_top_eigenspace_slices(K, p):
+    out = ctypes.c_int32(0)
+    _check(lib().asp_top_eigenspace_slices(K, p, ctypes.byref(out)))
+    return int(out.value)
+
+
+def asp_metric_product_partials(g, K, v, p, yp, stream=None):
+    _check(lib().asp_metric_product_partials(_ptr(g), K, _ptr(v), p, _ptr(yp),
+                                             _stream(stream, g)))
+
+
+def asp_top_eigenspace(g, K, v0, p, r, iters, v, evals, resid, workspace, workspace_bytes,
+                       stream=None):
+    _check(lib().asp_top_eigenspace(_ptr(g), K, _ptr(v0), p, r, iters, _ptr(v), _ptr(evals),
+                                    _ptr(resid), _ptr(workspace), workspace_bytes,
+                                    _stream(stream, g)))
 
 
 def _ptr_array(items):

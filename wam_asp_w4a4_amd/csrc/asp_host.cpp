@@ -148,7 +148,7 @@ using namespace asp;
 
 extern "C" {
 
-int32_t asp_abi_version(void) { return 6; }
+int32_t asp_abi_version(void) { return 7; }
 
 const char* asp_status_string(int32_t status) {
   switch (status) {

@@ -142,3 +142,20 @@ def smoothing_search(x, w, bias, v, candidates=None, stream=None):
                                        nbytes, stream)
     return cands[best][0], cands[best][1], mse, best
 
+
+
+def top_eigenspace(g, v0, r, iters, workspace=None, stream=None):
+    """Leading r eigenpairs of the symmetric PSD metric g (device float32 K x K) by
+    subspace iteration from v0 (device float32 K x p, p in {16, 32, 48, 64}).
+    Returns device tensors (V K x r, eigenvalues r, residual norms r)."""
+    K, p = v0.shape
+    if tuple(g.shape) != (K, K):
+        raise ValueError("g must be K x K with K = v0.shape[0]")
+    nbytes = B.asp_top_eigenspace_workspace_bytes(K, p, r)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=g.device)
+    v = torch.empty((K, r), dtype=torch.float32, device=g.device)
+    evals = torch.empty(r, dtype=torch.float32, device=g.device)
+    resid = torch.empty(r, dtype=torch.float32, device=g.device)
+    B.asp_top_eigenspace(g, K, v0, p, r, iters, v, evals, resid, workspace, nbytes, stream)
+    return v, evals, resid
