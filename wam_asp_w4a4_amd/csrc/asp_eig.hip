@@ -33,6 +33,26 @@ namespace {
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
+// 1/sqrt(d) and 1/x for positive normal d and nonzero normal x: the hardware
+// estimate (v_rsq_f64, v_rcp_f64) refined by two Newton-Raphson steps
+// (y <- y + y (1 - d y^2) / 2 and y <- y + y (1 - x y)), each of which roughly
+// doubles the number of correct bits, to within a few ulps.
+__device__ __forceinline__ double rsqrt_nr(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double r = fma(-(d * y), y, 1.0);
+    y = fma(0.5 * y, r, y);
+  }
+  return y;
+}
+__device__ __forceinline__ double rcp_nr(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = fma(y, fma(-x, y, 1.0), y);
+  return y;
+}
+
 constexpr int kEigMaxP = 64;
 constexpr int64_t kEigMaxK = 65536;
 constexpr int kRows = 64;   // rows per block of the row-blocked kernels
@@ -110,18 +130,39 @@ __global__ void __launch_bounds__(256) k_eig_gv(const float* __restrict__ g,
 
 // ------------------------------------------------------- row-blocked passes
 
-// Partial Gram sums of one 64-row block: part[a][b] = sum_rows L[row][a] R[row][b],
-// rows in ascending order (L = R gives an exactly symmetric result).
+// Rows of the per-block LDS tiles are padded to P + 2 doubles (16-byte aligned
+// rows, consecutive rows on different banks).
 template <int P>
-__device__ __forceinline__ void block_gram(const double (*L)[P + 1], const double (*R)[P + 1],
+using Tile = double[kRows][P + 2];
+
+// Partial Gram sums of one 64-row block: part[a][b] = sum_rows L[row][a] R[row][b],
+// rows in ascending order (L = R gives an exactly symmetric result).  Thread t
+// owns a 4 x 4 block of entries, so each pair of 4-wide row reads feeds 16 FMAs.
+template <int P>
+__device__ __forceinline__ void block_gram(const double (*L)[P + 2], const double (*R)[P + 2],
                                            double* __restrict__ part) {
-  for (int e = threadIdx.x; e < P * P; e += 256) {
-    const int a = e / P, b = e % P;
-    double s = 0.0;
-#pragma unroll 8
-    for (int i = 0; i < kRows; ++i) s = fma(L[i][a], R[i][b], s);
-    part[e] = s;
+  constexpr int NB = P / 4;
+  const int t = threadIdx.x;
+  if (t >= NB * NB) return;
+  const int a0 = (t / NB) * 4, b0 = (t % NB) * 4;
+  double acc[4][4] = {};
+#pragma unroll 4
+  for (int i = 0; i < kRows; ++i) {
+    double la[4], rb[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      la[x] = L[i][a0 + x];
+      rb[x] = R[i][b0 + x];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = fma(la[x], rb[y], acc[x][y]);
   }
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) part[(a0 + x) * P + b0 + y] = acc[x][y];
 }
 
 enum GramMode { kCast = 0, kShift = 1, kCross = 2 };
@@ -130,30 +171,39 @@ enum GramMode { kCast = 0, kShift = 1, kCross = 2 };
 //   kCast : Y = float64(v0)                      part = Y^T Y
 //   kShift: Y = sum_s yp[s] + mu V               part = Y^T Y
 //   kCross: Y = sum_s yp[s]                      part = V^T Y
-// slices are added in ascending order.
+// slices are added in ascending order; each thread keeps its P/4 elements'
+// loads of one slice in flight together.
 template <int P, int MODE>
 __global__ void __launch_bounds__(256) k_eig_gram(const float* __restrict__ v0,
                                                   const double* __restrict__ yp, int nslices,
                                                   const double* __restrict__ v,
                                                   const double* __restrict__ scal, int K,
                                                   double* __restrict__ y, double* __restrict__ cp) {
-  __shared__ double ys[kRows][P + 1];
-  __shared__ double vsh[MODE == kCross ? kRows : 1][P + 1];
+  constexpr int EPT = kRows * P / 256;
+  __shared__ __attribute__((aligned(16))) Tile<P> ys;
+  __shared__ __attribute__((aligned(16))) double vsh[MODE == kCross ? kRows : 1][P + 2];
+  const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * kRows * P;
-  const double mu = MODE == kShift ? scal[0] : 0.0;
-  for (int e = threadIdx.x; e < kRows * P; e += 256) {
-    const int i = e / P, c = e % P;
-    double val;
-    if constexpr (MODE == kCast) {
-      val = (double)v0[base + e];
-    } else {
-      val = 0.0;
-      for (int s = 0; s < nslices; ++s) val += yp[(int64_t)s * K * P + base + e];
-      if constexpr (MODE == kShift) val = fma(mu, v[base + e], val);
-      if constexpr (MODE == kCross) vsh[i][c] = v[base + e];
+  double acc[EPT];
+  if constexpr (MODE == kCast) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) acc[q] = (double)v0[base + tid + 256 * q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) acc[q] = 0.0;
+    for (int s = 0; s < nslices; ++s) {
+      const double* src = yp + (int64_t)s * K * P + base + tid;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) acc[q] += src[256 * q];
     }
-    ys[i][c] = val;
-    y[base + e] = val;
+  }
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = tid + 256 * q, i = e / P, c = e % P;
+    if constexpr (MODE == kShift) acc[q] = fma(scal[0], v[base + e], acc[q]);
+    if constexpr (MODE == kCross) vsh[i][c] = v[base + e];
+    ys[i][c] = acc[q];
+    y[base + e] = acc[q];
   }
   __syncthreads();
   block_gram<P>(MODE == kCross ? vsh : ys, ys, cp + (int64_t)blockIdx.x * P * P);
@@ -161,43 +211,61 @@ __global__ void __launch_bounds__(256) k_eig_gram(const float* __restrict__ v0,
 
 // c[e] = sum over blocks b (ascending) of cp[b][e].
 template <int P>
-__global__ void __launch_bounds__(256) k_eig_reduce(const double* __restrict__ cp, int nb,
-                                                    double* __restrict__ c) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= P * P) return;
+__global__ void __launch_bounds__(64) k_eig_reduce(const double* __restrict__ cp, int nb,
+                                                   double* __restrict__ c) {
+  const int e = blockIdx.x * 64 + threadIdx.x;
   double s = 0.0;
+#pragma unroll 8
   for (int b = 0; b < nb; ++b) s += cp[(int64_t)b * P * P + e];
   c[e] = s;
 }
 
 // vout = Y X^T for one 64-row block (X lower triangular, so column j of the
-// output mixes Y's columns 0..j); with GRAM, also the Gram partial of vout.
+// output mixes Y's columns 0..j, in ascending order; the zeros above X's
+// diagonal that a 4-wide block also reads add exactly nothing).  Thread t owns
+// a 4 x 4 block of outputs.  With GRAM, also the Gram partial of vout.
 template <int P, bool GRAM>
 __global__ void __launch_bounds__(256) k_eig_apply(const double* __restrict__ yin,
                                                    const double* __restrict__ xm,
                                                    double* __restrict__ vout,
                                                    double* __restrict__ cp) {
-  __shared__ double ys[kRows][P + 1];
-  __shared__ double xs[P][P + 1];
+  constexpr int NB = P / 4;
+  __shared__ __attribute__((aligned(16))) Tile<P> ys;
+  __shared__ __attribute__((aligned(16))) double xs[P][P + 2];
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * kRows * P;
   for (int e = tid; e < kRows * P; e += 256) ys[e / P][e % P] = yin[base + e];
   for (int e = tid; e < P * P; e += 256) xs[e / P][e % P] = xm[e];
   __syncthreads();
-  const int i = tid >> 2;
-  double o[P / 4];
+  const bool owner = tid < 16 * NB;
+  const int i0 = (tid / NB) * 4, j0 = (tid % NB) * 4;
+  double acc[4][4] = {};
+  if (owner) {
+    for (int k = 0; k < j0 + 4; ++k) {
+      double a[4], b[4];
 #pragma unroll
-  for (int m = 0; m < P / 4; ++m) {
-    const int j = (tid & 3) + 4 * m;
-    double s = 0.0;
-    for (int k = 0; k <= j; ++k) s = fma(ys[i][k], xs[j][k], s);
-    o[m] = s;
-    vout[base + (int64_t)i * P + j] = s;
+      for (int x = 0; x < 4; ++x) {
+        a[x] = ys[i0 + x][k];
+        b[x] = xs[j0 + x][k];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) vout[base + (int64_t)(i0 + x) * P + j0 + y] = acc[x][y];
   }
   if constexpr (GRAM) {
     __syncthreads();  // every thread is done reading ys
+    if (owner) {
 #pragma unroll
-    for (int m = 0; m < P / 4; ++m) ys[i][(tid & 3) + 4 * m] = o[m];
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) ys[i0 + x][j0 + y] = acc[x][y];
+    }
     __syncthreads();
     block_gram<P>(ys, ys, cp + (int64_t)blockIdx.x * P * P);
   }
@@ -205,48 +273,96 @@ __global__ void __launch_bounds__(256) k_eig_apply(const double* __restrict__ yi
 
 // --------------------------------------------------------- one-workgroup steps
 
-// Cholesky C = L L^T (right-looking, in LDS) and X = L^-1 (column c solved by
-// thread c, forward substitution).  A pivot that is not a positive finite
-// number is replaced by 1 and recorded in scal[1].
+// Cholesky C = L L^T and X = L^-1 by four waves.  Lane i of wave q holds
+// row i's entries in columns k = 4u + q (u < P/4) in registers.  Step j:
+// every thread takes the pivot published by the previous step, the owners of
+// column j scale it and publish it to LDS, and after a barrier every row below
+// j updates its trailing entries (right-looking order); the owner of the next
+// diagonal publishes it as soon as it is updated.  The inverse is formed the
+// same way, column c of X held by lane c of every wave: step k, the owner of
+// row k finishes x_k = (delta_{k,c} - sum_{m<k} L[k][m] x_m) / L[k][k] and
+// publishes it, and every later row adds its L[r][k] x_k.  A pivot that is not
+// a positive finite normal number is replaced by 1 and recorded in scal[1].
 template <int P>
 __global__ void __launch_bounds__(256) k_eig_chol(const double* __restrict__ cin,
                                                   double* __restrict__ xm,
                                                   double* __restrict__ scal) {
-  __shared__ double C[P][P + 1];
-  __shared__ double X[P][P + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < P * P; e += 256) C[e / P][e % P] = cin[e];
+  constexpr int U = P / 4;
+  __shared__ double col[P];
+  __shared__ double diag[2];
+  __shared__ double Ls[P][P + 1];
+  __shared__ double dinv[P];
+  __shared__ double xk[2][P];
+  const int q = threadIdx.x >> 6, i = threadIdx.x & 63;
+  const bool row_ok = i < P;
+  const int ii = row_ok ? i : P - 1;
+  double c[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) c[u] = cin[ii * P + 4 * u + q];
+  if (threadIdx.x == 0) diag[0] = cin[0];
   __syncthreads();
   bool bad_any = false;
+  // fully unrolled: every register slot index below is a compile-time constant
+#pragma unroll
   for (int j = 0; j < P; ++j) {
-    double d = C[j][j];
-    const bool bad = !(d > 0.0) || __builtin_isinf(d);
+    double d = diag[j & 1];
+    const bool bad = !(d >= 2.2250738585072014e-308) || __builtin_isinf(d);
     if (bad) d = 1.0;
     bad_any |= bad;
-    const double piv = sqrt(d), inv = 1.0 / piv;
-    for (int i = j + 1 + tid; i < P; i += 256) C[i][j] *= inv;
+    const double inv = rsqrt_nr(d), piv = d * inv;
+    if (q == (j & 3) && row_ok && ii >= j) {
+      const double l = ii == j ? piv : c[j >> 2] * inv;
+      c[j >> 2] = l;
+      if (ii > j) col[ii] = l;
+      else dinv[j] = inv;
+    }
     __syncthreads();
-    if (tid == 0) C[j][j] = piv;
-    const int m = P - 1 - j;
-    for (int e = tid; e < m * m; e += 256) {
-      const int i = j + 1 + e / m, k = j + 1 + e % m;
-      if (k <= i) C[i][k] = fma(-C[i][j], C[k][j], C[i][k]);
+    if (row_ok && ii > j) {
+      // every load is issued (all indices are in range), the update selected
+      const double li = col[ii];
+#pragma unroll
+      for (int u = (j + 1) / 4; u < U; ++u) {
+        const int k = 4 * u + q;
+        const double nv = fma(-li, col[k], c[u]);
+        c[u] = k > j && k <= ii ? nv : c[u];
+      }
+      if (j + 1 < P && ii == j + 1 && q == ((j + 1) & 3)) diag[(j + 1) & 1] = c[(j + 1) >> 2];
     }
     __syncthreads();
   }
-  if (tid < P) {
-    const int c = tid;
-    for (int i = 0; i < c; ++i) X[i][c] = 0.0;
-    X[c][c] = 1.0 / C[c][c];
-    for (int i = c + 1; i < P; ++i) {
-      double s = 0.0;
-      for (int k = c; k < i; ++k) s = fma(C[i][k], X[k][c], s);
-      X[i][c] = -s / C[i][i];
+  if (row_ok) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = 4 * u + q;
+      Ls[ii][k] = k <= ii ? c[u] : 0.0;
     }
   }
   __syncthreads();
-  for (int e = tid; e < P * P; e += 256) xm[e] = X[e / P][e % P];
-  if (tid == 0 && bad_any) scal[1] = 1.0;
+  double acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = 0.0;
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    if (q == (k & 3) && row_ok) {
+      const double x = ((ii == k ? 1.0 : 0.0) - acc[k >> 2]) * dinv[k];
+      xk[k & 1][ii] = x;
+      acc[k >> 2] = x;
+    }
+    __syncthreads();
+    if (row_ok) {
+      const double xv = xk[k & 1][ii];
+#pragma unroll
+      for (int u = (k + 1) / 4; u < U; ++u) {
+        const double nv = fma(Ls[4 * u + q][k], xv, acc[u]);
+        acc[u] = 4 * u + q > k ? nv : acc[u];
+      }
+    }
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) xm[(4 * u + q) * P + ii] = acc[u];
+  }
+  if (threadIdx.x == 0 && bad_any) scal[1] = 1.0;
 }
 
 // mu = 2^-16 sqrt(sum of the Frobenius partials) (1 when that is 0); clears
@@ -283,9 +399,10 @@ __global__ void __launch_bounds__(256) k_eig_frob(const float* __restrict__ g, i
 
 // Symmetric eigendecomposition of T = (C + C^T)/2 (p x p) by cyclic Jacobi
 // with the round-robin ordering: each step rotates p/2 disjoint index pairs
-// at once (one thread computes each pair's rotation; all threads apply the
-// row and then the column updates).  Sweeps stop when the off-diagonal
-// Frobenius norm falls to 1e-15 of the whole, or after 40.  Outputs the
+// at once (one thread computes each pair's rotation; then all threads apply
+// them to 2 x 2 blocks of T and to Z).  Sweeps stop when the off-diagonal
+// Frobenius norm falls to 1e-13 of the whole (rounding keeps it near 1e-16
+// times a small factor, so a tighter bound might never be met), or after 40.  Outputs the
 // eigenvalues largest first (equal ones in index order) and the matching
 // eigenvector columns zs[:, m].
 template <int P>
@@ -293,10 +410,14 @@ __global__ void __launch_bounds__(256) k_eig_jacobi(const double* __restrict__ c
                                                     double* __restrict__ theta,
                                                     double* __restrict__ zs,
                                                     double* __restrict__ scal) {
+  constexpr int NP = P / 2;
+  constexpr int NBLK = (NP * NP + 255) / 256;  // 2 x 2 blocks of T per thread
+  constexpr int NZ = (NP * P + 255) / 256;     // (row, pair) items of Z per thread
   __shared__ double T[P][P + 1];
   __shared__ double Z[P][P + 1];
-  __shared__ double cs[P / 2][2];
-  __shared__ int pq[P / 2][2];
+  __shared__ double cs[NP][2];
+  __shared__ int pq[NP][2];
+  __shared__ unsigned char sched[P - 1][NP][2];  // round-robin pairs, smaller index first
   __shared__ double red[256][2];
   __shared__ int perm[P];
   const int tid = threadIdx.x;
@@ -304,6 +425,13 @@ __global__ void __launch_bounds__(256) k_eig_jacobi(const double* __restrict__ c
     const int a = e / P, b = e % P;
     T[a][b] = 0.5 * (cin[a * P + b] + cin[b * P + a]);
     Z[a][b] = a == b ? 1.0 : 0.0;
+  }
+  for (int e = tid; e < (P - 1) * NP; e += 256) {
+    const int rnd = e / NP, i = e % NP;
+    auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + rnd) % (P - 1); };
+    const int a = player(i), b = player(P - 1 - i);
+    sched[rnd][i][0] = (unsigned char)(a < b ? a : b);
+    sched[rnd][i][1] = (unsigned char)(a < b ? b : a);
   }
   __syncthreads();
   for (int sweep = 0; sweep < 40; ++sweep) {
@@ -323,22 +451,25 @@ __global__ void __launch_bounds__(256) k_eig_jacobi(const double* __restrict__ c
       }
       __syncthreads();
     }
-    const bool done = !(red[0][0] > 1e-30 * red[0][1]);
+    const bool done = !(red[0][0] > 1e-26 * red[0][1]);
     __syncthreads();  // everyone has read red before it is reused
     if (done) break;
     for (int rnd = 0; rnd < P - 1; ++rnd) {
-      if (tid < P / 2) {
-        auto player = [&](int pos) { return pos == 0 ? 0 : 1 + (pos - 1 + rnd) % (P - 1); };
-        int a = player(tid), b = player(P - 1 - tid);
-        if (a > b) { const int t = a; a = b; b = t; }
+      if (tid < NP) {
+        const int a = sched[rnd][tid][0], b = sched[rnd][tid][1];
         const double app = T[a][a], aqq = T[b][b], apq = T[a][b];
         double c = 1.0, s = 0.0;
-        if (apq != 0.0) {
-          const double tau = (aqq - app) / (2.0 * apq);
+        if (fabs(apq) > 1e-300) {  // smaller entries are left as they are
+          const double tau = (aqq - app) * rcp_nr(2.0 * apq);
           // the smaller root of t^2 + 2 tau t - 1 = 0; 1 / (2 tau) once tau^2 would overflow
-          const double t = fabs(tau) > 1e150 ? 0.5 / tau
-                                             : (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-          c = 1.0 / sqrt(1.0 + t * t);
+          double t;
+          if (fabs(tau) > 1e150) {
+            t = 0.5 * rcp_nr(tau);
+          } else {
+            const double h = fma(tau, tau, 1.0);
+            t = (tau >= 0.0 ? 1.0 : -1.0) * rcp_nr(fabs(tau) + h * rsqrt_nr(h));
+          }
+          c = rsqrt_nr(fma(t, t, 1.0));
           s = t * c;
         }
         cs[tid][0] = c;
@@ -347,25 +478,58 @@ __global__ void __launch_bounds__(256) k_eig_jacobi(const double* __restrict__ c
         pq[tid][1] = b;
       }
       __syncthreads();
-      for (int e = tid; e < (P / 2) * P; e += 256) {  // rows a and b of T
-        const int i = e / P, k = e % P, a = pq[i][0], b = pq[i][1];
-        const double c = cs[i][0], s = cs[i][1];
-        const double ta = T[a][k], tb = T[b][k];
-        T[a][k] = c * ta - s * tb;
-        T[b][k] = s * ta + c * tb;
+      // T = J^T T J, one 2 x 2 block (pair i's rows, pair i2's columns) per
+      // item: each block is rebuilt from its own four entries (rows first,
+      // then columns), so the blocks are independent; a diagonal block's
+      // off-diagonal entries are the ones the rotation zeroes.  All of a
+      // thread's loads are issued before its stores.
+      {
+        int ia[NBLK], ib[NBLK], ja[NBLK], jb[NBLK];
+        double c1[NBLK], s1[NBLK], c2[NBLK], s2[NBLK], t4[NBLK][4];
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n) {
+          const int e = min(tid + 256 * n, NP * NP - 1), i = e / NP, i2 = e % NP;
+          ia[n] = pq[i][0]; ib[n] = pq[i][1]; ja[n] = pq[i2][0]; jb[n] = pq[i2][1];
+          c1[n] = cs[i][0]; s1[n] = cs[i][1]; c2[n] = cs[i2][0]; s2[n] = cs[i2][1];
+        }
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n) {
+          t4[n][0] = T[ia[n]][ja[n]]; t4[n][1] = T[ia[n]][jb[n]];
+          t4[n][2] = T[ib[n]][ja[n]]; t4[n][3] = T[ib[n]][jb[n]];
+        }
+#pragma unroll
+        for (int n = 0; n < NBLK; ++n) {
+          if (tid + 256 * n >= NP * NP) continue;
+          const double c = c1[n], s = s1[n], cc = c2[n], ss = s2[n];
+          const double raa = c * t4[n][0] - s * t4[n][2], rab = c * t4[n][1] - s * t4[n][3];
+          const double rba = s * t4[n][0] + c * t4[n][2], rbb = s * t4[n][1] + c * t4[n][3];
+          const bool diag_blk = ia[n] == ja[n];
+          T[ia[n]][ja[n]] = cc * raa - ss * rab;
+          T[ia[n]][jb[n]] = diag_blk ? 0.0 : ss * raa + cc * rab;
+          T[ib[n]][ja[n]] = diag_blk ? 0.0 : cc * rba - ss * rbb;
+          T[ib[n]][jb[n]] = ss * rba + cc * rbb;
+        }
       }
-      __syncthreads();
-      for (int e = tid; e < (P / 2) * P; e += 256) {  // columns a and b of T and Z
-        const int i = e / P, k = e % P, a = pq[i][0], b = pq[i][1];
-        const double c = cs[i][0], s = cs[i][1];
-        const double ta = T[k][a], tb = T[k][b];
-        T[k][a] = c * ta - s * tb;
-        T[k][b] = s * ta + c * tb;
-        if (k == a) T[a][b] = 0.0;
-        if (k == b) T[b][a] = 0.0;
-        const double za = Z[k][a], zb = Z[k][b];
-        Z[k][a] = c * za - s * zb;
-        Z[k][b] = s * za + c * zb;
+      {  // Z = Z J: columns a and b of every row
+        int za_[NZ], zb_[NZ], zk[NZ];
+        double zc[NZ], zs_[NZ], va[NZ], vb[NZ];
+#pragma unroll
+        for (int n = 0; n < NZ; ++n) {
+          const int e = min(tid + 256 * n, NP * P - 1), i = e / P;
+          zk[n] = e % P; za_[n] = pq[i][0]; zb_[n] = pq[i][1];
+          zc[n] = cs[i][0]; zs_[n] = cs[i][1];
+        }
+#pragma unroll
+        for (int n = 0; n < NZ; ++n) {
+          va[n] = Z[zk[n]][za_[n]];
+          vb[n] = Z[zk[n]][zb_[n]];
+        }
+#pragma unroll
+        for (int n = 0; n < NZ; ++n) {
+          if (tid + 256 * n >= NP * P) continue;
+          Z[zk[n]][za_[n]] = zc[n] * va[n] - zs_[n] * vb[n];
+          Z[zk[n]][zb_[n]] = zs_[n] * va[n] + zc[n] * vb[n];
+        }
       }
       __syncthreads();
     }
@@ -535,10 +699,10 @@ int32_t eig_run(const float* g, int64_t K, const float* v0, int r, int iters, fl
          *cr = d(L.cr), *xm = d(L.xm), *zs = d(L.zs), *th = d(L.th), *scal = d(L.scal),
          *fro = d(L.fro), *res2 = d(L.res2), *amv = d(L.amv), *sgn = d(L.sgn);
   const int nb = L.nb, Ki = (int)K, slice = Ki / L.slices;
-  const dim3 blk(256), rows(nb), gv_grid(nb, L.slices), red_grid((P * P + 255) / 256);
+  const dim3 blk(256), rows(nb), gv_grid(nb, L.slices), red_grid(P * P / 64);
 
   auto chol_apply = [&](const double* yin, double* vo, bool gram) {
-    k_eig_reduce<P><<<red_grid, blk, 0, st>>>(cp, nb, cr);
+    k_eig_reduce<P><<<red_grid, 64, 0, st>>>(cp, nb, cr);
     k_eig_chol<P><<<1, blk, 0, st>>>(cr, xm, scal);
     if (gram)
       k_eig_apply<P, true><<<rows, blk, 0, st>>>(yin, xm, vo, cp);
@@ -558,7 +722,7 @@ int32_t eig_run(const float* g, int64_t K, const float* v0, int r, int iters, fl
   chol_apply(va, vb, false);  // second Cholesky QR pass
   k_eig_gv<P><<<gv_grid, blk, 0, st>>>(g, vb, yp, Ki, slice);
   k_eig_gram<P, kCross><<<rows, blk, 0, st>>>(nullptr, yp, L.slices, vb, scal, Ki, ya, cp);
-  k_eig_reduce<P><<<red_grid, blk, 0, st>>>(cp, nb, cr);
+  k_eig_reduce<P><<<red_grid, 64, 0, st>>>(cp, nb, cr);
   k_eig_jacobi<P><<<1, blk, 0, st>>>(cr, th, zs, scal);
   k_eig_ritz<P><<<rows, blk, 0, st>>>(vb, ya, zs, th, r, vout, res2, amv);
   k_eig_final<<<1, 64, 0, st>>>(th, res2, amv, nb, r, scal, evals, resid, sgn);
