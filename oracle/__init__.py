@@ -23,9 +23,11 @@ Modules:
               layer forward.
   smoothing -- the per-layer (alpha, beta) smoothing search.
   eigen    -- the top-r eigenspace of a symmetric PSD metric (the basis V).
+  svdquant -- the SVDQuant-style INT4 (group 64) W4A4 layer: quantiser, rank-r
+              16-bit branch, residual, forward.
 
 Every function here is pinned by tests under ``tests/test_oracle_*.py`` against
 closed forms, hand-derived vectors (``tests/golden/``), invariants and brute force.
 """
 
-from . import formats, hadamard, asp, smoothing, eigen  # noqa: F401
+from . import formats, hadamard, asp, smoothing, eigen, svdquant  # noqa: F401

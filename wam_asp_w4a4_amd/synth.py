@@ -104,6 +104,38 @@ def draw_basis(rng, K, r):
     return q.astype(np.float32)
 
 
+def make_svdq_layer(name, M, K, N, r, *, seed=DEFAULT_SEED, dtype="bf16", outlier_frac=0.01,
+                    outlier_gain=20.0, planted=32, alpha=0.5) -> Layer:
+    """A seeded layer for the SVDQuant-style arm: the weight carries a planted
+    low-rank part above its N(0, 1/K) bulk, the structure that arm's 16-bit
+    branch is meant to take (after smoothing, a trained weight's leading
+    singular values stand out from the rest).
+
+    Draw order (PCG64 ``default_rng(seed)``): x as ``draw_activation``; the bulk
+    W0 ~ N(0, 1/K); b ~ N(0, 0.01); U (N x planted) and Q (K x planted) from
+    the QR of N(0, 1) draws; W = W0 + U diag(sig) Q^T with
+    sig = (1 + sqrt(N / K)) * linspace(8, 4, planted), i.e. 8 to 4 times the
+    bulk's largest singular value; then x and W are rounded to bf16 and s is
+    drawn from them as for the other layers.  ``r`` is the rank the layer is
+    packed with.
+    """
+    rng = np.random.default_rng(seed)
+    x64, idx = draw_activation(rng, M, K, outlier_frac, outlier_gain)
+    x32 = x64.astype(np.float32)
+    w0 = rng.standard_normal((N, K)) / math.sqrt(K)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    u, _ = np.linalg.qr(rng.standard_normal((N, planted)))
+    q, _ = np.linalg.qr(rng.standard_normal((K, planted)))
+    sig = (1.0 + math.sqrt(N / K)) * np.linspace(8.0, 4.0, planted)
+    w = (w0 + (u * sig) @ q.T).astype(np.float32)
+    if dtype == "bf16":
+        x32 = to_bf16_values(x32)
+        w = to_bf16_values(w)
+    s = smoothing_vector(x32, w, alpha)
+    return Layer(name, M, K, N, r, x32, dtype, w, b, s, None,
+                 {"seed": seed, "outlier_channels": idx, "planted": planted})
+
+
 def draw_metric(rng, K, decay=8.0, floor=1e-6, rank=None):
     """Synthetic symmetric PSD K x K metric with a fast-falling spectrum.
 
