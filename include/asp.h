@@ -399,6 +399,60 @@ int32_t asp_top_eigenspace(const float* g, int64_t K, const float* v0,
                            float* evals, float* resid, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * SVDQuant-style INT4 W4A4 arm.  Model card "FastWAM UR3 3-task -- 4-bit
+ * quantisations": method table (the second checkpoint: INT4 with groups of 64
+ * for weights and activations, contracted on INT8 tensor cores, exact for
+ * 4-bit codes) and section "Verification -- INT4 SVDQuant".  The smoothed
+ * weight W_hat = W diag(s) is split into a rank-r bfloat16 branch L1 L2 (its
+ * truncated SVD: L2 = V_r^T, the top right singular vectors, L1 = W_hat V_r)
+ * and a residual R = W_hat - L1 L2 quantised to INT4 together with
+ * x_hat = float32(x * float32(1/s)):
+ *     y = bfloat16(u) L1^T + sum_g sx[m,g] sw[n,g] sum_{k in g} qx qw + b,
+ *     u = x diag(1/s) V_r (float32 accumulation).
+ * Group quantiser (both operands): scale = bfloat16(float32(amax) / 7), code =
+ * clamp(rint(v / scale), -8, 7) in float32 (ties to even); a zero scale gives
+ * zero codes.  Codes: two's-complement nibbles, element 2j in the low nibble
+ * of byte j, rows of K/2 bytes.  Scales: bfloat16 bits, group-major: (K/64)
+ * rows of N128 (weights) or M128 (activations) entries, the count rounded up
+ * to 128, padding zero (weights) or undefined (activations).
+ *
+ * asp_svdq_packed_sizes: bytes of the codes, scales, L1 (N x rp32 bf16, r
+ *   rounded up to 32, zero padded) and prep pack of one layer (host).
+ * asp_svdq_gram: g (host, K x K float32, exactly symmetric) = W_hat^T W_hat
+ *   in float64; its top-r eigenvectors (asp_top_eigenspace) are V_r.
+ * asp_svdq_pack_weight (host): from W (N x K), s (K, positive) and V_r
+ *   (K x r float32, orthonormal columns; NULL iff r == 0) writes codes,
+ *   scales, l1 and prep (1/s and diag(1/s) V_r for u), all host buffers of
+ *   asp_svdq_packed_sizes bytes.
+ * asp_svdq_act_quant (device): x (M x K, f32 or bf16) -> x_codes (M x K/2)
+ *   and x_scales ((K/64) x M128 bf16), using the 1/s of prep_pack.
+ * asp_svdq_gemm (device): y from activation codes/scales, u (M x r float32,
+ *   rounded to bfloat16 inside), the packed weight, l1 and bias (N or NULL).
+ * asp_svdq_forward (device): the whole layer, with u, the activation codes
+ *   and scales in the caller's workspace (asp_svdq_workspace_bytes bytes,
+ *   256-byte aligned).  K a multiple of 128; 0 <= r <= 64; M >= 0.
+ */
+int32_t asp_svdq_packed_sizes(int64_t N, int64_t K, int32_t r, size_t* code_bytes,
+                              size_t* scale_bytes, size_t* l1_bytes, size_t* prep_bytes);
+int32_t asp_svdq_gram(int64_t N, int64_t K, const float* w, const float* s, float* g);
+int32_t asp_svdq_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
+                             const float* s, const float* v, uint8_t* codes,
+                             uint16_t* scales, uint16_t* l1, uint8_t* prep);
+int32_t asp_svdq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, size_t* bytes);
+int32_t asp_svdq_act_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                           const uint8_t* prep_pack, uint8_t* x_codes,
+                           uint16_t* x_scales, void* stream);
+int32_t asp_svdq_gemm(const uint8_t* x_codes, const uint16_t* x_scales, const float* u,
+                      int64_t M, int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
+                      const uint16_t* w_scales, const uint16_t* l1, const float* bias,
+                      void* y, int32_t y_dtype, void* stream);
+int32_t asp_svdq_forward(const void* x, int32_t x_dtype, int64_t M, int64_t K, int32_t r,
+                         const uint8_t* prep_pack, const uint8_t* w_codes,
+                         const uint16_t* w_scales, const uint16_t* l1, const float* bias,
+                         int64_t N, void* y, int32_t y_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

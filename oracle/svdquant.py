@@ -23,10 +23,11 @@ Readings taken where the page is silent (each used identically everywhere):
   scale giving zero codes; the division and the rounding are float32, so a
   code is a float32 decision on both sides;
 * low-rank branch: L1 L2 is the rank-r truncated SVD of W_hat in float64
-  (L2 = the top right singular vectors as rows, L1 = W_hat L2^T), stored in
-  bfloat16; R = W_hat - L1 L2 from the unrounded factors, rounded to float32,
-  then quantised; u = x_hat L2^T in float64 then rounded to bfloat16, and the
-  branch is u times bfloat16(L1)^T;
+  (L2 = the top right singular vectors as rows, each with its largest-magnitude
+  entry positive, L1 = W_hat L2^T), stored in bfloat16; R = W_hat - L1 L2
+  from the unrounded factors, rounded to float32, then quantised; u = x_hat
+  L2^T in float64 then rounded to bfloat16, and the branch is u times
+  bfloat16(L1)^T;
 * the group products are exact integers; each is scaled by the product of
   its two bfloat16 scales (exact in float32); everything else is float64 here.
 """
@@ -74,9 +75,12 @@ def smoothed_activation(x, s):
 
 
 def low_rank(w_hat, r):
-    """(L1 N x r, L2 r x K) of the rank-r truncated SVD of w_hat, float64."""
+    """(L1 N x r, L2 r x K) of the rank-r truncated SVD of w_hat, float64; each
+    row of L2 (a right singular vector) has its largest-magnitude entry positive."""
     _, _, vt = np.linalg.svd(np.asarray(w_hat, np.float64), full_matrices=False)
-    l2 = vt[:r]
+    l2 = vt[:r].copy()
+    idx = np.argmax(np.abs(l2), axis=1)
+    l2 *= np.where(l2[np.arange(r), idx] < 0, -1.0, 1.0)[:, None]
     return np.asarray(w_hat, np.float64) @ l2.T, l2
 
 

@@ -251,6 +251,31 @@ def test_top_eigenspace_validation():
     assert lib.asp_metric_product_partials(FAKE, 256, MIS, 32, FAKE, None) == 3
 
 
+def test_svdq_device_validation():
+    lib = B.lib()
+    need = B.asp_svdq_workspace_bytes(64, 96, 256, 16)
+    assert need > 0
+
+    def fwd(x=FAKE, K=256, r=16, l1=FAKE, ws=FAKE, nb=need, yd=0, xd=1):
+        return lib.asp_svdq_forward(x, xd, 64, K, r, FAKE, FAKE, FAKE, l1, None, 96, FAKE, yd, ws,
+                                    nb, None)
+
+    assert fwd(K=100) == 2
+    assert fwd(r=65) == 2
+    assert fwd(x=None) == 1
+    assert fwd(l1=None) == 1
+    assert fwd(yd=7) == 1
+    assert fwd(xd=9) == 1
+    assert fwd(ws=FAKE + 16) == 3
+    assert fwd(nb=need - 1) == 5
+    assert lib.asp_svdq_gemm(FAKE, FAKE, None, 8, 8, 128, 16, FAKE, FAKE, FAKE, None, FAKE, 0,
+                             None) == 1
+    assert lib.asp_svdq_gemm(FAKE, MIS, FAKE, 8, 8, 128, 16, FAKE, FAKE, FAKE, None, FAKE, 0,
+                             None) == 3
+    assert lib.asp_svdq_act_quant(FAKE, 1, 8, 100, FAKE, FAKE, FAKE, None) == 2
+    assert lib.asp_svdq_act_quant(None, 1, 8, 128, FAKE, FAKE, FAKE, None) == 1
+
+
 def test_host_quantizer_validation():
     a = np.zeros((2, 24), np.float32)
     with pytest.raises(B.ASPError):

@@ -92,6 +92,8 @@ def test_branch_is_the_best_rank_r_part():
     pk = SQ.pack_weight(lay.w, lay.s, 16)
     l2, resid = pk["l2"], pk["w_hat"] - pk["l1"] @ pk["l2"]
     np.testing.assert_allclose(l2 @ l2.T, np.eye(16), atol=1e-12)
+    idx = np.argmax(np.abs(l2), axis=1)
+    assert np.all(l2[np.arange(16), idx] > 0)
     assert np.abs(resid @ l2.T).max() <= 1e-9 * np.abs(pk["w_hat"]).max()
     best = np.linalg.norm(resid)
     for _ in range(20):

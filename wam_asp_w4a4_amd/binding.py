@@ -55,6 +55,14 @@ SIGNATURES = {
     "asp_top_eigenspace_slices": (_i32, [_i64, _i32, ctypes.POINTER(ctypes.c_int32)]),
     "asp_metric_product_partials": (_i32, [_p, _i64, _p, _i32, _p, _p]),
     "asp_top_eigenspace": (_i32, [_p, _i64, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
+    "asp_svdq_packed_sizes": (_i32, [_i64, _i64, _i32, _psz, _psz, _psz, _psz]),
+    "asp_svdq_gram": (_i32, [_i64, _i64, _p, _p, _p]),
+    "asp_svdq_pack_weight": (_i32, [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p]),
+    "asp_svdq_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _psz]),
+    "asp_svdq_act_quant": (_i32, [_p, _i32, _i64, _i64, _p, _p, _p, _p]),
+    "asp_svdq_gemm": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
+    "asp_svdq_forward": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i64, _p, _i32,
+                                _p, _sz, _p]),
     "asp_forward_group": (_i32, [_i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p,
                                  _i32, _p, _p, _p]),
     "asp_forward_group_stages": (_i32, [_i32, _i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p,
@@ -265,6 +273,47 @@ def asp_top_eigenspace(g, K, v0, p, r, iters, v, evals, resid, workspace, worksp
     _check(lib().asp_top_eigenspace(_ptr(g), K, _ptr(v0), p, r, iters, _ptr(v), _ptr(evals),
                                     _ptr(resid), _ptr(workspace), workspace_bytes,
                                     _stream(stream, g)))
+
+
+def asp_svdq_packed_sizes(N, K, r):
+    """(code bytes, scale bytes, L1 bytes, prep-pack bytes) of one packed layer."""
+    out = [ctypes.c_size_t(0) for _ in range(4)]
+    _check(lib().asp_svdq_packed_sizes(N, K, r, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def asp_svdq_gram(N, K, w, s, g):
+    _check(lib().asp_svdq_gram(N, K, _ptr(w), _ptr(s), _ptr(g)))
+
+
+def asp_svdq_pack_weight(N, K, r, w, s, v, codes, scales, l1, prep):
+    _check(lib().asp_svdq_pack_weight(N, K, r, _ptr(w), _ptr(s), _ptr(v), _ptr(codes),
+                                      _ptr(scales), _ptr(l1), _ptr(prep)))
+
+
+def asp_svdq_workspace_bytes(M, N, K, r):
+    out = ctypes.c_size_t(0)
+    _check(lib().asp_svdq_workspace_bytes(M, N, K, r, ctypes.byref(out)))
+    return out.value
+
+
+def asp_svdq_act_quant(x, x_dtype, M, K, prep_pack, x_codes, x_scales, stream=None):
+    _check(lib().asp_svdq_act_quant(_ptr(x), x_dtype, M, K, _ptr(prep_pack), _ptr(x_codes),
+                                    _ptr(x_scales), _stream(stream, x)))
+
+
+def asp_svdq_gemm(x_codes, x_scales, u, M, N, K, r, w_codes, w_scales, l1, bias, y, y_dtype,
+                  stream=None):
+    _check(lib().asp_svdq_gemm(_ptr(x_codes), _ptr(x_scales), _ptr(u), M, N, K, r, _ptr(w_codes),
+                               _ptr(w_scales), _ptr(l1), _ptr(bias), _ptr(y), y_dtype,
+                               _stream(stream, y)))
+
+
+def asp_svdq_forward(x, x_dtype, M, K, r, prep_pack, w_codes, w_scales, l1, bias, N, y, y_dtype,
+                     workspace, workspace_bytes, stream=None):
+    _check(lib().asp_svdq_forward(_ptr(x), x_dtype, M, K, r, _ptr(prep_pack), _ptr(w_codes),
+                                  _ptr(w_scales), _ptr(l1), _ptr(bias), N, _ptr(y), y_dtype,
+                                  _ptr(workspace), workspace_bytes, _stream(stream, x)))
 
 
 def _ptr_array(items):

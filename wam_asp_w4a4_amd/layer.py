@@ -159,3 +159,64 @@ def top_eigenspace(g, v0, r, iters, workspace=None, stream=None):
     resid = torch.empty(r, dtype=torch.float32, device=g.device)
     B.asp_top_eigenspace(g, K, v0, p, r, iters, v, evals, resid, workspace, nbytes, stream)
     return v, evals, resid
+
+
+@dataclass
+class SvdqLayer:
+    """One SVDQuant-style INT4 (group 64) W4A4 layer, packed for the device."""
+    N: int
+    K: int
+    r: int
+    codes: object    # N x K/2 uint8, nibble-packed INT4 of the residual
+    scales: object   # (K/64) x N128 bf16 bits, group-major, zero padded
+    l1: object       # N x rp32 bf16 bits (W_hat V, zero padded)
+    prep: object     # prep pack: 1/s and diag(1/s) V for u = x diag(1/s) V
+    bias: object = None
+
+    @staticmethod
+    def right_basis(w, s, r, iters=24, block=64, seed=0, device="cuda"):
+        """Top-r right singular vectors of W diag(s) (K x r float32): the Gram
+        matrix on the host, its top-r eigenspace on the device."""
+        w = np.ascontiguousarray(w, np.float32)
+        s = np.ascontiguousarray(s, np.float32)
+        N, K = w.shape
+        g = np.empty((K, K), np.float32)
+        B.asp_svdq_gram(N, K, w, s, g)
+        v0 = np.random.default_rng(seed).standard_normal((K, block)).astype(np.float32)
+        v, _, _ = top_eigenspace(torch.from_numpy(g).to(device), torch.from_numpy(v0).to(device),
+                                 r, iters)
+        return v.cpu().numpy()
+
+    @classmethod
+    def pack_host(cls, w, s, r, v, bias=None):
+        w = np.ascontiguousarray(w, np.float32)
+        s = np.ascontiguousarray(s, np.float32)
+        N, K = w.shape
+        cb, sb, lb, pb = B.asp_svdq_packed_sizes(N, K, r)
+        codes = np.empty(cb, np.uint8)
+        scales = np.empty(sb // 2, np.uint16)
+        l1 = np.empty(max(lb // 2, 1), np.uint16)
+        prep = np.empty(pb, np.uint8)
+        vv = None if r == 0 else np.ascontiguousarray(v, np.float32)
+        B.asp_svdq_pack_weight(N, K, r, w, s, vv, codes, scales, l1, prep)
+        b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+        return cls(N, K, r, codes, scales, l1, prep, b)
+
+    def to(self, device):
+        t = lambda a: None if a is None else torch.from_numpy(a).to(device)
+        return SvdqLayer(self.N, self.K, self.r, t(self.codes), t(self.scales), t(self.l1),
+                         t(self.prep), t(self.bias))
+
+    def forward(self, x, y_dtype="f32", workspace=None, y=None, stream=None):
+        M = x.shape[0]
+        x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
+        nbytes = B.asp_svdq_workspace_bytes(M, self.N, self.K, self.r)
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+        if y is None:
+            y = torch.empty((M, self.N), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32,
+                            device=x.device)
+        B.asp_svdq_forward(x, x_dtype, M, self.K, self.r, self.prep, self.codes, self.scales,
+                           self.l1 if self.r else None, self.bias, self.N, y, B.DTYPES[y_dtype],
+                           workspace, nbytes, stream)
+        return y
