@@ -47,11 +47,13 @@ KERNEL_SOURCES = {
     "k_prep_q": ["asp_prep.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
     "k_gemm": ["asp_gemm.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
     "k_eig_gv": ["asp_eig.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
+    "k_svdq_gemm": ["asp_svdq.hip", "asp_device.h", "nvfp4_codec.h", "asp_internal.h"],
 }
 WORKLOAD_SLUGS = {0: "single_M64_K512_N512", 1: "action_attn_M256_K1024_N1024",
                   2: "action_ffn_M256", 3: "video_attn_M4096_K3072_N3072"}
 COPY_CALIBRATION_BYTES = 256 << 20
 F64_PEAK_TFLOPS = 78.6      # MI355X dense fp64 MFMA
+I8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA
 # the basis solve: the action expert's widest layer input (ffn.2, K = 4096),
 # rank 32 with a block of 64, 8 products with the metric
 EIG_K, EIG_P, EIG_R, EIG_ITERS = 4096, 64, 32, 8
@@ -124,6 +126,9 @@ def parse():
     ap.add_argument("--eigen", action="store_true",
                     help="time the basis solve instead: the top-32 eigenspace of a synthetic "
                          "4096 x 4096 action metric (block 64, 8 iterations)")
+    ap.add_argument("--svdq", action="store_true",
+                    help="time the SVDQuant-style INT4 (group 64) W4A4 arm on the workload's "
+                         "layer shapes instead of the deflated-ASP NVFP4 path")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (the reference "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -176,6 +181,9 @@ def main():
 
     if args.eigen:
         eigen_bench(args, dev)
+        return
+    if args.svdq:
+        svdq_bench(args, dev)
         return
     layers = synth.workload(args.workload)
     if args.search:
@@ -567,6 +575,176 @@ def eigen_bench(args, dev):
                    "max_eigenvalue_error_rel_lam1": err,
                    "max_residual": float(res.max().item()),
                    "timing": "HIP events on the launch stream around back-to-back solves"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def svdq_bench(args, dev):
+    """The SVDQuant-style INT4 W4A4 arm on the workload's layer shapes: one step =
+    u (k_prep_u), the group quantiser and the INT8 GEMM for every layer, on
+    replicas of every buffer resident in HBM; then each kernel timed alone."""
+    import torch
+    from wam_asp_w4a4_amd import binding as B
+    from wam_asp_w4a4_amd import synth
+    from wam_asp_w4a4_amd.layer import SvdqLayer
+    base = synth.workload(args.workload)
+    layers = [synth.make_svdq_layer(l.name, l.M, l.K, l.N, l.r or 32, seed=synth.DEFAULT_SEED + i)
+              for i, l in enumerate(base)]
+    packed = []
+    for lay in layers:
+        v = SvdqLayer.right_basis(lay.w, lay.s, lay.r)
+        packed.append(SvdqLayer.pack_host(lay.w, lay.s, lay.r, v, lay.b))
+    flops = sum(2 * l.M * l.N * l.K + 2 * l.M * l.K * l.r + 2 * l.M * l.N * l.r for l in layers)
+
+    def per_replica(l, h):
+        return (h.codes.nbytes + h.scales.nbytes + h.l1.nbytes + h.prep.nbytes + l.M * l.K * 2
+                + l.M * l.N * 2 + B.asp_svdq_workspace_bytes(l.M, l.N, l.K, l.r))
+    per = sum(per_replica(l, h) for l, h in zip(layers, packed))
+    R = max(2, int(np.ceil(args.min_replica_gib * 2 ** 30 / per)))
+    reps = []
+    for _ in range(R):
+        rep = []
+        for l, h in zip(layers, packed):
+            d = h.to(dev)
+            x = torch.from_numpy(synth.bf16_bits(l.x)).view(torch.bfloat16).to(dev)
+            nb = B.asp_svdq_workspace_bytes(l.M, l.N, l.K, l.r)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+            y = torch.empty((l.M, l.N), dtype=torch.bfloat16, device=dev)
+            rep.append((l, d, x, ws, nb, y))
+        reps.append(rep)
+    # launches go to torch's current stream (the capture stream inside a graph)
+    sp = None
+
+    def step(i):
+        for l, d, x, ws, nb, y in reps[i % R]:
+            B.asp_svdq_forward(x, B.ASP_BF16, l.M, l.K, l.r, d.prep, d.codes, d.scales, d.l1, d.bias,
+                               l.N, y, B.ASP_BF16, ws, nb, sp)
+
+    for i in range(args.warmup):
+        step(i)
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # each kernel alone: graphs of its launches over the replicas
+    nk = max(R, min(args.kernel_timing_steps, 4 * R))
+    ubufs = [[torch.zeros((l.M, (l.r + 31) // 32 * 32), dtype=torch.float32, device=dev)
+              for l in layers] for _ in range(R)]
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(nk):
+                fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nk
+
+    def k_u(i):
+        for l, d, x, ws, nb, y in reps[i % R]:
+            B.asp_act_prep_u(x, B.ASP_BF16, l.M, l.K, l.r, d.prep, ws, nb, sp)
+
+    def k_q(i):
+        for l, d, x, ws, nb, y in reps[i % R]:
+            B.asp_svdq_act_quant(x, B.ASP_BF16, l.M, l.K, d.prep, ws, ws[l.M * l.K // 2:], sp)
+
+    def k_g(i):
+        for (l, d, x, ws, nb, y), u in zip(reps[i % R], ubufs[i % R]):
+            xs_off = (l.M * l.K // 2 + 255) // 256 * 256
+            B.asp_svdq_gemm(ws, ws[xs_off:], u, l.M, l.N, l.K, l.r, d.codes, d.scales, d.l1,
+                            d.bias, y, B.ASP_BF16, sp)
+
+    t_u, t_q, t_g = timed(k_u), timed(k_q), timed(k_g)
+    gflops = sum(2 * l.M * l.N * l.K + 2 * l.M * l.N * l.r for l in layers)
+    gbytes = sum(l.M * l.K // 2 + l.M * l.K // 32 + l.N * l.K // 2 + l.N * l.K // 32
+                 + l.M * l.r * 4 + l.N * ((l.r + 31) // 32 * 32) * 2 + l.M * l.N * 2 + l.N * 4
+                 for l in layers)
+    tops = gflops / (t_g * 1e-3) / 1e12
+    gbs = gbytes / (t_g * 1e-3) / 1e9
+    ridge = I8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gflops / gbytes >= ridge:
+        roof = {"bound": "mfma", "achieved": round(tops, 2), "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(tops / I8_PEAK_TOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    names = sorted({f"k_svdq_gemm<2, {(l.r + 31) // 32}>" for l in layers})
+    roof.update({
+        "traffic": measured_traffic("k_svdq_gemm", f"svdq_{WORKLOAD_SLUGS[args.workload]}"),
+        "kernel": " + ".join(names),
+        "source_digest": kernel_source_digest("k_svdq_gemm"),
+        "avg_launch_us": round(t_g * 1e3 / len(layers), 3),
+        "launches": nk * len(layers),
+        "algorithmic_bytes_per_launch": gbytes // len(layers),
+        "algorithmic_flops_per_launch": gflops // len(layers),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "dtype": "int8 MFMA on INT4 codes (exact), float32 group scaling, bf16 low-rank branch",
+        "kernels": {"k_prep_u": {"avg_launch_us": round(t_u * 1e3 / len(layers), 3)},
+                    "k_svdq_quant": {"avg_launch_us": round(t_q * 1e3 / len(layers), 3)},
+                    "k_svdq_gemm": {"avg_launch_us": round(t_g * 1e3 / len(layers), 3)}},
+    })
+    cpu = None
+    if args.cpu_seconds > 0:
+        from oracle import svdquant as oracle_sq
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([q.get("num_threads", 1) for q in threadpool_info()] or [1])
+        except Exception:
+            threads = 1
+        opk = [oracle_sq.pack_weight(l.w, l.s, l.r) for l in layers]
+        # the oracle's exact integer group products are slow: large-M layers
+        # run on their first 64 rows (rows are independent), FLOPs counted to match
+        rows = [l.M if l.M <= 256 else 64 for l in layers]
+        sflops = sum(2 * m * l.N * l.K + 2 * m * l.K * l.r + 2 * m * l.N * l.r
+                     for m, l in zip(rows, layers))
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            for l, pk, m in zip(layers, opk, rows):
+                oracle_sq.forward(l.x[:m], l.w, l.b, l.s, l.r, packed=pk)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or n >= 1000:
+                break
+        cpu = {"value": round(sflops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+               "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{n} passes over {rows} rows of the layers (float64 NumPy oracle with "
+                         f"exact integer group products, weights pre-packed), {el:.1f} s; "
+                         "cores = BLAS threads"}
+    out = {
+        "metric": "SVDQuant-style INT4 W4A4 linear effective TFLOP/s + % of roofline, 1 MI355X",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": synth.WORKLOADS[args.workload] + " (SVDQuant-style INT4 arm)",
+                   "layers": [{"name": l.name, "M": l.M, "K": l.K, "N": l.N, "r": l.r} for l in layers],
+                   "flops_per_step": flops, "replicas": R,
+                   "timing": "one HIP graph of K steps, events on the capture stream"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

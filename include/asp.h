@@ -427,8 +427,9 @@ int32_t asp_top_eigenspace(const float* g, int64_t K, const float* v0,
  *   asp_svdq_packed_sizes bytes.
  * asp_svdq_act_quant (device): x (M x K, f32 or bf16) -> x_codes (M x K/2)
  *   and x_scales ((K/64) x M128 bf16), using the 1/s of prep_pack.
- * asp_svdq_gemm (device): y from activation codes/scales, u (M x r float32,
- *   rounded to bfloat16 inside), the packed weight, l1 and bias (N or NULL).
+ * asp_svdq_gemm (device): y from activation codes/scales, u (M x rp32
+ *   float32, the columns past r zero; rounded to bfloat16 inside), the packed
+ *   weight, l1 and bias (N or NULL).
  * asp_svdq_forward (device): the whole layer, with u, the activation codes
  *   and scales in the caller's workspace (asp_svdq_workspace_bytes bytes,
  *   256-byte aligned).  K a multiple of 128; 0 <= r <= 64; M >= 0.

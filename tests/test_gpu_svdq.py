@@ -85,6 +85,8 @@ def test_act_quant_bit_exact(M, K, dtype):
 GEMM_CASES = [  # M, N, K, r
     (64, 64, 128, 0), (128, 128, 512, 32), (200, 96, 1024, 16), (37, 300, 256, 64),
     (256, 1024, 1024, 32), (1, 16, 128, 24), (512, 384, 3072, 32),
+    # large and ragged grids
+    (2048, 2048, 256, 8), (2000, 2100, 128, 40),
 ]
 
 
@@ -103,9 +105,11 @@ def test_gemm_on_oracle_codes(M, N, K, r):
     rp = (r + 31) // 32 * 32
     l1p = np.zeros((N, max(rp, 1)), np.uint16)
     l1p[:, :r] = bf16_bits(l1)
+    up = np.zeros((M, max(rp, 1)), np.float32)  # u is M x rp32, the columns past r zero
+    up[:, :r] = u
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     args = [t(pack_codes(xc)), t(pack_scales(xs, M).view(np.int16)),
-            t(u.astype(np.float32)) if r else None, M, N, K, r, t(pack_codes(wc)),
+            t(up) if r else None, M, N, K, r, t(pack_codes(wc)),
             t(pack_scales(ws, N).view(np.int16)), t(l1p.view(np.int16)) if r else None, t(bias)]
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)
     B.asp_svdq_gemm(*args, y, B.ASP_F32)

@@ -24,8 +24,6 @@ namespace {
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupK = 64;
-constexpr int kTile = 128;    // output tile of a workgroup (128 x 128, 4 waves of 64 x 64)
-constexpr int kStages = 4;    // groups in flight through LDS
 
 inline int64_t pad128(int64_t v) { return (v + 127) / 128 * 128; }
 
@@ -99,7 +97,8 @@ __global__ void __launch_bounds__(256) k_svdq_quant(const XT* __restrict__ x,
 struct SvdqGemmArgs {
   const uint8_t* xc;   // M x K/2 codes
   const uint16_t* xs;  // (K/64) x Mp bfloat16 scales
-  const float* u;      // u_slices partial sums, [s][M][u_ld] float32 (summed in slice order)
+  const float* u;      // u_slices partial sums, [s][M][u_ld] float32, u_ld = r rounded up to 32,
+                       // the columns past r zero (summed in slice order)
   const uint8_t* wc;   // N x K/2 codes
   const uint16_t* ws;  // (K/64) x Np bfloat16 scales
   const uint16_t* l1;  // N x RP bfloat16 (zero padded)
@@ -115,78 +114,83 @@ __device__ __forceinline__ i32x4_t unpack16(uint2 w) {
   return i32x4_t{(int)((w.x << 4) & m), (int)(w.x & m), (int)((w.y << 4) & m), (int)(w.y & m)};
 }
 
-// Workgroup: a 128 x 128 tile of y, 4 waves of 64 x 64 (wave w: rows 64 (w/2),
-// columns 64 (w%2)), 4 x 4 MFMA tiles of 16 x 16 per wave.  Per group of 64:
-// both operands' 128 code rows (32 bytes each) and scales are copied into one
-// of kStages LDS buffers with direct global-to-LDS copies; every wave issues
-// exactly three copies per group (two of codes, one of scales), so one
-// vmcnt per pipeline depth serves all waves.  MFMA lane layout (checked on
-// gfx950): lane l supplies row l%16 of A (column l%16 of B) with the 16 bytes
-// of K-quarter l/16; output element v is row 4 (l/16) + v, column l%16.
-template <int RPK>
+// Workgroup: a BM x BN tile of y (BM = BN = 32 TI; TI = 2 is launched), 4
+// waves as 2 x 2, each wave TI x TI MFMA tiles of 16 x 16.  Per group of 64 the workgroup's code
+// rows (32 bytes each) and scales are loaded into registers two groups ahead
+// and written to one of two LDS buffers one group ahead, so each load has two
+// groups of compute to land in; the compiler waits only on the registers a
+// write uses.  MFMA lane layout (checked on gfx950): lane l supplies row l%16
+// of A (column l%16 of B) with the 16 bytes of K-quarter l/16; output element
+// v is row 4 (l/16) + v, column l%16.
+template <int TI, int RPK>
 __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t sxc[kStages][kTile * 32];
-  __shared__ __attribute__((aligned(16))) uint8_t swc[kStages][kTile * 32];
-  __shared__ __attribute__((aligned(16))) uint16_t sxs[kStages][kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t sws[kStages][kTile];
+  constexpr int BM = 32 * TI, BN = 32 * TI;
+  constexpr int CX = BM * 2, CW = BN * 2;  // 16-byte pieces of codes per group
+  static_assert(CX + CW <= 512, "two pieces of codes per thread at most");
+  __shared__ __attribute__((aligned(16))) uint8_t sxc[2][BM * 32];
+  __shared__ __attribute__((aligned(16))) uint8_t swc[2][BN * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t sxs[2][BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sws[2][BN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, l16 = lane & 15;
-  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = a.M, N = a.N, KB = a.K / 2, G = a.K / kGroupK;
 
-  auto issue = [&](int g, int st) {
-    // 128 rows x 32 bytes = 256 copies of 16 bytes per operand: thread t copies
-    // half t%2 of row t/2, landing at byte 16 t of the stage buffer
-    {
-      const int row = tid >> 1, half = tid & 1;
-      const int64_t mr = min(m0 + row, M - 1), nr = min(n0 + row, N - 1);
-      lds_copy16(a.xc + mr * KB + 32 * g + 16 * half, &sxc[st][64 * wave * 16]);
-      lds_copy16(a.wc + nr * KB + 32 * g + 16 * half, &swc[st][64 * wave * 16]);
-    }
-    // 128 scales of each operand = 16 copies of 8: lanes 0-7 of waves 0/1 and
-    // lanes 8-15 of waves 2/3 (x scales by waves 0 and 2, w scales by 1 and 3)
-    const bool mine = (wave < 2) ? lane < 8 : (lane >= 8 && lane < 16);
-    const int chunk = min(lane, 15);
-    if (mine) {
-      if ((wave & 1) == 0)
-        lds_copy16(a.xs + (int64_t)g * a.Mp + m0 + 8 * chunk, &sxs[st][0]);
-      else
-        lds_copy16(a.ws + (int64_t)g * a.Np + n0 + 8 * chunk, &sws[st][0]);
-    }
+  // the pieces this thread moves: code piece tid (and tid + 256 when there are
+  // more than 256), and scale piece tid - 0 / tid - BM/8 for the first threads
+  struct Regs {
+    u32x4_t c0, c1, sc;
   };
-
-  f32x4_t out[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < G) issue(s, s);
-  for (int g = 0; g < G; ++g) {
-    // This wave's copies of group g have landed (later groups may stay in
-    // flight) and its LDS reads are done; then a bare s_barrier: every wave's
-    // copies of group g are in LDS and group g-1's buffer is free.  (A fenced
-    // __syncthreads would wait for every copy in flight.)
-    const int ahead = min(kStages - 2, G - 1 - g);
-    if (ahead >= 2)
-      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
-    else if (ahead == 1)
-      asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  auto piece_src = [&](int P, int g) -> const uint8_t* {
+    const int64_t mr = min(m0 + (P >> 1), M - 1);
+    const int64_t nr = min(n0 + max((P - CX) >> 1, 0), N - 1);
+    return P < CX ? a.xc + mr * KB + 32 * g + 16 * (P & 1)
+                  : a.wc + nr * KB + 32 * g + 16 * ((P - CX) & 1);
+  };
+  auto piece_dst = [&](int P, int b) -> uint8_t* {
+    return P < CX ? &sxc[b][16 * P] : &swc[b][16 * (P - CX)];
+  };
+  constexpr int SX = BM / 8, SW = BN / 8;  // 16-byte pieces of scales
+  // every thread issues the same loads (no lane-dependent branch around a
+  // load, so the compiler can count them and wait only for the ones a store
+  // needs): scale piece min(tid, SX + SW - 1), its address selected per lane
+  static_assert(CX + CW == 256 || CX + CW == 512, "one or two code pieces per thread");
+  auto gload = [&](int g, Regs& r) {
+    r.c0 = *reinterpret_cast<const u32x4_t*>(piece_src(tid, g));
+    if constexpr (CX + CW == 512) r.c1 = *reinterpret_cast<const u32x4_t*>(piece_src(tid + 256, g));
+    const int sp = min(tid, SX + SW - 1);
+    const uint16_t* src = sp < SX ? a.xs + (int64_t)g * a.Mp + m0 + 8 * sp
+                                  : a.ws + (int64_t)g * a.Np + n0 + 8 * max(sp - SX, 0);
+    r.sc = *reinterpret_cast<const u32x4_t*>(src);
+  };
+  auto sstore = [&](int b, const Regs& r) {
+    *reinterpret_cast<u32x4_t*>(piece_dst(tid, b)) = r.c0;
+    if constexpr (CX + CW == 512) *reinterpret_cast<u32x4_t*>(piece_dst(tid + 256, b)) = r.c1;
+    if (tid < SX)
+      *reinterpret_cast<u32x4_t*>(&sxs[b][8 * tid]) = r.sc;
+    else if (tid < SX + SW)
+      *reinterpret_cast<u32x4_t*>(&sws[b][8 * (tid - SX)]) = r.sc;
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (g + kStages - 1 < G) issue(g + kStages - 1, (g + kStages - 1) % kStages);
-    const int st = g % kStages;
-    i32x4_t A[4], B[4];
-    float sx[4][4], sw[4];
+  };
+
+  f32x4_t out[TI][TI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wm + 16 * i + l16;
-      A[i] = unpack16(*reinterpret_cast<const uint2*>(&sxc[st][row * 32 + 8 * q]));
-      const uint2 s2 = *reinterpret_cast<const uint2*>(&sxs[st][64 * wm + 16 * i + 4 * q]);
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TI; ++j) out[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int b) {
+    i32x4_t A[TI], B[TI];
+    float sx[TI][4], sw[TI];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = 16 * (TI * wm + i) + l16;
+      A[i] = unpack16(*reinterpret_cast<const uint2*>(&sxc[b][row * 32 + 8 * q]));
+      const uint2 s2 = *reinterpret_cast<const uint2*>(&sxs[b][16 * (TI * wm + i) + 4 * q]);
       // the 2^-8 undoes the 16 x 16 of the byte encoding (exact)
       sx[i][0] = bf16_to_f32(s2.x & 0xFFFFu) * 0.00390625f;
       sx[i][1] = bf16_to_f32(s2.x >> 16) * 0.00390625f;
@@ -194,65 +198,98 @@ __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
       sx[i][3] = bf16_to_f32(s2.y >> 16) * 0.00390625f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 64 * wn + 16 * j + l16;
-      B[j] = unpack16(*reinterpret_cast<const uint2*>(&swc[st][row * 32 + 8 * q]));
-      sw[j] = bf16_to_f32(sws[st][row]);
+    for (int j = 0; j < TI; ++j) {
+      const int row = 16 * (TI * wn + j) + l16;
+      B[j] = unpack16(*reinterpret_cast<const uint2*>(&swc[b][row * 32 + 8 * q]));
+      sw[j] = bf16_to_f32(sws[b][row]);
     }
     const i32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < TI; ++j) {
         const i32x4_t acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], B[j], zero, 0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 4; ++v) out[i][j][v] = fmaf((float)acc[v], sx[i][v] * sw[j], out[i][j][v]);
       }
+  };
+
+  // group k is held in register set k % 2 and LDS buffer k % 2 (G is even).
+  // Loads past the last group re-read group G - 1 (valid memory, never used),
+  // so that no load sits behind a branch.
+  Regs r0, r1;
+  gload(0, r0);
+  gload(1, r1);
+  sstore(0, r0);
+  gload(min(2, G - 1), r0);
+  barrier();
+  for (int g = 0; g < G; g += 2) {
+    compute(0);
+    sstore(1, r1);                   // group g + 1 (buffer 1 was last read at g - 1)
+    gload(min(g + 3, G - 1), r1);
+    barrier();
+    compute(1);
+    sstore(0, r0);                   // group g + 2 (unused after the last pair)
+    gload(min(g + 4, G - 1), r0);
+    barrier();
   }
 
   // rank-r branch: bfloat16(u) L1^T on v_mfma_f32_16x16x32_bf16 (lane l: row
-  // l%16, k-slots 8 (l/16) .. +7 of both operands), then the bias
+  // l%16, k-slots 8 (l/16) .. +7 of both operands), then the bias.  u is
+  // [slices][M][RP] float32 with the columns past r zero; the slices are added
+  // in order, every load in flight together.
   if constexpr (RPK > 0) {
+    constexpr int RP = 32 * RPK;
 #pragma unroll
     for (int ks = 0; ks < RPK; ++ks) {
-      bf16x8_t au[4], bl[4];
+      bf16x8_t au[TI], bl[TI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = min(m0 + 64 * wm + 16 * i + l16, M - 1);
+      for (int i = 0; i < TI; ++i) {
+        const int64_t m = min(m0 + 16 * (TI * wm + i) + l16, M - 1);
+        f32x4_t lo[8], hi[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const float* p = a.u + ((int64_t)min(sl, a.u_slices - 1) * M + m) * RP + 32 * ks + 8 * q;
+          lo[sl] = *reinterpret_cast<const f32x4_t*>(p);
+          hi[sl] = *reinterpret_cast<const f32x4_t*>(p + 4);
+        }
         float f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 32 * ks + 8 * q + e;
-          float s = 0.0f;
-          if (k < a.r)
-            for (int sl = 0; sl < a.u_slices; ++sl) s += a.u[((int64_t)sl * M + m) * a.u_ld + k];
-          f[e] = s;
+        for (int e = 0; e < 4; ++e) {
+          float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+          for (int sl = 0; sl < 8; ++sl) {
+            s0 += sl < a.u_slices ? lo[sl][e] : 0.0f;
+            s1 += sl < a.u_slices ? hi[sl][e] : 0.0f;
+          }
+          f[e] = s0;
+          f[4 + e] = s1;
         }
         au[i] = bf16x8_rne(f);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = min(n0 + 64 * wn + 16 * j + l16, N - 1);
-        bl[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                  a.l1 + n * (32 * RPK) + 32 * ks + 8 * q));
+      for (int j = 0; j < TI; ++j) {
+        const int64_t n = min(n0 + 16 * (TI * wn + j) + l16, N - 1);
+        bl[j] = __builtin_bit_cast(bf16x8_t,
+                                   *reinterpret_cast<const u32x4_t*>(a.l1 + n * RP + 32 * ks + 8 * q));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TI; ++j)
           out[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[i], bl[j], out[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 64 * wn + 16 * j + l16;
+  for (int j = 0; j < TI; ++j) {
+    const int n = n0 + 16 * (TI * wn + j) + l16;
     if (n >= N) continue;
     const float b = a.bias ? a.bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * q + v;
+        const int m = m0 + 16 * (TI * wm + i) + 4 * q + v;
         if (m >= M) continue;
         const float val = out[i][j][v] + b;
         if (a.y_bf16)
@@ -303,14 +340,15 @@ int32_t launch_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K, const
 }
 
 int32_t launch_gemm(const SvdqGemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + kTile - 1) / kTile), (unsigned)((a.M + kTile - 1) / kTile));
+  // 64 x 64 tiles (2 x 2 MFMA tiles per wave, 4 waves per SIMD): the
+  // per-group scaling after every MFMA is a chain of dependent VALU steps,
+  // hidden by other waves.  (A 128 x 128 tile, 4 x 4 per wave, needs 256
+  // VGPRs -- 2 waves per SIMD -- and was slower at M = 4096, K = N = 3072.)
   const int rp = a.r == 0 ? 0 : (a.r + 31) / 32;
-  if (rp == 0)
-    k_svdq_gemm<0><<<grid, 256, 0, st>>>(a);
-  else if (rp == 1)
-    k_svdq_gemm<1><<<grid, 256, 0, st>>>(a);
-  else
-    k_svdq_gemm<2><<<grid, 256, 0, st>>>(a);
+  const dim3 grid((unsigned)((a.N + 63) / 64), (unsigned)((a.M + 63) / 64));
+  if (rp == 0) k_svdq_gemm<2, 0><<<grid, 256, 0, st>>>(a);
+  else if (rp == 1) k_svdq_gemm<2, 1><<<grid, 256, 0, st>>>(a);
+  else k_svdq_gemm<2, 2><<<grid, 256, 0, st>>>(a);
   return launch_status("svdq gemm");
 }
 
@@ -361,8 +399,8 @@ int32_t asp_svdq_gemm(const uint8_t* x_codes, const uint16_t* x_scales, const fl
   ASP_TRY(check_ptr(bias, "bias", false));
   ASP_TRY(check_ptr(y, "y", true));
   SvdqGemmArgs a = {x_codes, x_scales, u, w_codes, w_scales, l1, bias, y,
-                    (int)M, (int)N, (int)K, r, (int)pad128(M), (int)pad128(N), 1, r,
-                    y_dtype == ASP_BF16};
+                    (int)M, (int)N, (int)K, r, (int)pad128(M), (int)pad128(N), 1,
+                    (r + 31) / 32 * 32, y_dtype == ASP_BF16};
   return launch_gemm(a, (hipStream_t)stream);
 }
 
