@@ -413,9 +413,10 @@ int32_t asp_top_eigenspace(const float* g, int64_t K, const float* v0,
  * Group quantiser (both operands): scale = bfloat16(float32(amax) / 7), code =
  * clamp(rint(v / scale), -8, 7) in float32 (ties to even); a zero scale gives
  * zero codes.  Codes: two's-complement nibbles, element 2j in the low nibble
- * of byte j, rows of K/2 bytes.  Scales: bfloat16 bits, group-major: (K/64)
- * rows of N128 (weights) or M128 (activations) entries, the count rounded up
- * to 128, padding zero (weights) or undefined (activations).
+ * of byte j, rows of K/2 bytes.  Scales, group-major: (K/64) rows of N128
+ * (weights: bfloat16 bits, padding zero) or M128 (activations: the bfloat16
+ * values held as float32, padding undefined) entries, the count rounded up
+ * to 128.
  *
  * asp_svdq_packed_sizes: bytes of the codes, scales, L1 (N x rp32 bf16, r
  *   rounded up to 32, zero padded) and prep pack of one layer (host).
@@ -426,7 +427,7 @@ int32_t asp_top_eigenspace(const float* g, int64_t K, const float* v0,
  *   scales, l1 and prep (1/s and diag(1/s) V_r for u), all host buffers of
  *   asp_svdq_packed_sizes bytes.
  * asp_svdq_act_quant (device): x (M x K, f32 or bf16) -> x_codes (M x K/2)
- *   and x_scales ((K/64) x M128 bf16), using the 1/s of prep_pack.
+ *   and x_scales ((K/64) x M128 float32), using the 1/s of prep_pack.
  * asp_svdq_gemm (device): y from activation codes/scales, u (M x rp32
  *   float32, the columns past r zero; rounded to bfloat16 inside), the packed
  *   weight, l1 and bias (N or NULL).
@@ -443,8 +444,8 @@ int32_t asp_svdq_pack_weight(int64_t N, int64_t K, int32_t r, const float* w,
 int32_t asp_svdq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, size_t* bytes);
 int32_t asp_svdq_act_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                            const uint8_t* prep_pack, uint8_t* x_codes,
-                           uint16_t* x_scales, void* stream);
-int32_t asp_svdq_gemm(const uint8_t* x_codes, const uint16_t* x_scales, const float* u,
+                           float* x_scales, void* stream);
+int32_t asp_svdq_gemm(const uint8_t* x_codes, const float* x_scales, const float* u,
                       int64_t M, int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
                       const uint16_t* w_scales, const uint16_t* l1, const float* bias,
                       void* y, int32_t y_dtype, void* stream);

@@ -34,6 +34,14 @@ def pack_codes(c):
     return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
 
 
+def pack_scales_f32(vals, rows):
+    """rows x G float64 (bf16 values) -> (G, rows128) float32, group-major."""
+    G = vals.shape[1]
+    out = np.zeros((G, (rows + 127) // 128 * 128), np.float32)
+    out[:, :rows] = np.asarray(vals, np.float32).T
+    return out
+
+
 def pack_scales(vals, rows):
     """rows x G float64 (bf16 values) -> (G, rows128) bf16 bits, group-major, zero padded."""
     G = vals.shape[1]
@@ -71,12 +79,12 @@ def test_act_quant_bit_exact(M, K, dtype):
     h = SvdqLayer.pack_host(lay.w, lay.s, 0, None)
     xc = torch.empty((M, K // 2), dtype=torch.uint8, device=DEV)
     M128 = (M + 127) // 128 * 128
-    xs = torch.empty((K // 64) * M128, dtype=torch.int16, device=DEV)
+    xs = torch.empty((K // 64) * M128, dtype=torch.float32, device=DEV)
     B.asp_svdq_act_quant(x_dev(lay.x, dtype), B.DTYPES[dtype], M, K,
                          torch.from_numpy(h.prep).to(DEV), xc, xs)
     torch.cuda.synchronize()
     codes = unpack_codes(xc.cpu().numpy(), M, K)
-    scales = scales_rows(xs.cpu().numpy().view(np.uint16), M, K)
+    scales = xs.cpu().numpy().reshape(K // 64, M128)[:, :M].T.astype(np.float64)
     oc, os_ = SQ.quantize_int4(SQ.smoothed_activation(lay.x, lay.s))
     np.testing.assert_array_equal(scales, os_)
     np.testing.assert_array_equal(codes, oc)
@@ -108,7 +116,7 @@ def test_gemm_on_oracle_codes(M, N, K, r):
     up = np.zeros((M, max(rp, 1)), np.float32)  # u is M x rp32, the columns past r zero
     up[:, :r] = u
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    args = [t(pack_codes(xc)), t(pack_scales(xs, M).view(np.int16)),
+    args = [t(pack_codes(xc)), t(pack_scales_f32(xs, M)),
             t(up) if r else None, M, N, K, r, t(pack_codes(wc)),
             t(pack_scales(ws, N).view(np.int16)), t(l1p.view(np.int16)) if r else None, t(bias)]
     y = torch.empty((M, N), dtype=torch.float32, device=DEV)

@@ -35,12 +35,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __builtin_bit_
 // 64 share its absolute maximum.  x_hat = float32(x * rs); scale =
 // bfloat16(amax / 7); code = clamp(rint(x_hat / scale), -8, 7) (IEEE float32
 // division, ties to even), stored as two's-complement nibbles, element 2j in
-// the low nibble of byte j.  Scales go to xs[g * Mp + m].
+// the low nibble of byte j.  Scales (bfloat16 values, held as float32 so the
+// GEMM uses them as they are) go to xs[g * Mp + m].
 template <typename XT>
 __global__ void __launch_bounds__(256) k_svdq_quant(const XT* __restrict__ x,
                                                     const float* __restrict__ rs, int M, int K,
                                                     int Mp, uint8_t* __restrict__ xc,
-                                                    uint16_t* __restrict__ xs) {
+                                                    float* __restrict__ xs) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int cpr = K / 16;  // 16-element chunks per row (a multiple of 4)
   if (t >= (int64_t)M * cpr) return;  // whole 4-lane groups leave together
@@ -89,14 +90,14 @@ __global__ void __launch_bounds__(256) k_svdq_quant(const XT* __restrict__ x,
     w[e >> 3] |= (uint32_t)(q & 15) << (4 * (e & 7));
   }
   *reinterpret_cast<uint2*>(xc + m * (K / 2) + 8 * c) = make_uint2(w[0], w[1]);
-  if ((c & 3) == 0) xs[(int64_t)(c >> 2) * Mp + m] = sb;
+  if ((c & 3) == 0) xs[(int64_t)(c >> 2) * Mp + m] = sc;
 }
 
 // ---------------------------------------------------------------- the GEMM
 
 struct SvdqGemmArgs {
   const uint8_t* xc;   // M x K/2 codes
-  const uint16_t* xs;  // (K/64) x Mp bfloat16 scales
+  const float* xs;     // (K/64) x Mp scales (bfloat16 values as float32)
   const float* u;      // u_slices partial sums, [s][M][u_ld] float32, u_ld = r rounded up to 32,
                        // the columns past r zero (summed in slice order)
   const uint8_t* wc;   // N x K/2 codes
@@ -129,7 +130,7 @@ __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
   static_assert(CX + CW <= 512, "two pieces of codes per thread at most");
   __shared__ __attribute__((aligned(16))) uint8_t sxc[2][BM * 32];
   __shared__ __attribute__((aligned(16))) uint8_t swc[2][BN * 32];
-  __shared__ __attribute__((aligned(16))) uint16_t sxs[2][BM];
+  __shared__ __attribute__((aligned(16))) float sxs[2][BM];
   __shared__ __attribute__((aligned(16))) uint16_t sws[2][BN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, q = lane >> 4, l16 = lane & 15;
@@ -150,7 +151,7 @@ __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
   auto piece_dst = [&](int P, int b) -> uint8_t* {
     return P < CX ? &sxc[b][16 * P] : &swc[b][16 * (P - CX)];
   };
-  constexpr int SX = BM / 8, SW = BN / 8;  // 16-byte pieces of scales
+  constexpr int SX = BM / 4, SW = BN / 8;  // 16-byte pieces of scales (float32 x, bf16 w)
   // every thread issues the same loads (no lane-dependent branch around a
   // load, so the compiler can count them and wait only for the ones a store
   // needs): scale piece min(tid, SX + SW - 1), its address selected per lane
@@ -159,15 +160,16 @@ __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
     r.c0 = *reinterpret_cast<const u32x4_t*>(piece_src(tid, g));
     if constexpr (CX + CW == 512) r.c1 = *reinterpret_cast<const u32x4_t*>(piece_src(tid + 256, g));
     const int sp = min(tid, SX + SW - 1);
-    const uint16_t* src = sp < SX ? a.xs + (int64_t)g * a.Mp + m0 + 8 * sp
-                                  : a.ws + (int64_t)g * a.Np + n0 + 8 * max(sp - SX, 0);
+    const void* src = sp < SX ? static_cast<const void*>(a.xs + (int64_t)g * a.Mp + m0 + 4 * sp)
+                              : static_cast<const void*>(a.ws + (int64_t)g * a.Np + n0 +
+                                                         8 * max(sp - SX, 0));
     r.sc = *reinterpret_cast<const u32x4_t*>(src);
   };
   auto sstore = [&](int b, const Regs& r) {
     *reinterpret_cast<u32x4_t*>(piece_dst(tid, b)) = r.c0;
     if constexpr (CX + CW == 512) *reinterpret_cast<u32x4_t*>(piece_dst(tid + 256, b)) = r.c1;
     if (tid < SX)
-      *reinterpret_cast<u32x4_t*>(&sxs[b][8 * tid]) = r.sc;
+      *reinterpret_cast<u32x4_t*>(&sxs[b][4 * tid]) = r.sc;
     else if (tid < SX + SW)
       *reinterpret_cast<u32x4_t*>(&sws[b][8 * (tid - SX)]) = r.sc;
   };
@@ -190,18 +192,16 @@ __global__ void __launch_bounds__(256) k_svdq_gemm(SvdqGemmArgs a) {
     for (int i = 0; i < TI; ++i) {
       const int row = 16 * (TI * wm + i) + l16;
       A[i] = unpack16(*reinterpret_cast<const uint2*>(&sxc[b][row * 32 + 8 * q]));
-      const uint2 s2 = *reinterpret_cast<const uint2*>(&sxs[b][16 * (TI * wm + i) + 4 * q]);
-      // the 2^-8 undoes the 16 x 16 of the byte encoding (exact)
-      sx[i][0] = bf16_to_f32(s2.x & 0xFFFFu) * 0.00390625f;
-      sx[i][1] = bf16_to_f32(s2.x >> 16) * 0.00390625f;
-      sx[i][2] = bf16_to_f32(s2.y & 0xFFFFu) * 0.00390625f;
-      sx[i][3] = bf16_to_f32(s2.y >> 16) * 0.00390625f;
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(&sxs[b][16 * (TI * wm + i) + 4 * q]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sx[i][v] = s4[v];
     }
 #pragma unroll
     for (int j = 0; j < TI; ++j) {
       const int row = 16 * (TI * wn + j) + l16;
       B[j] = unpack16(*reinterpret_cast<const uint2*>(&swc[b][row * 32 + 8 * q]));
-      sw[j] = bf16_to_f32(sws[b][row]);
+      // the 2^-8 undoes the 16 x 16 of the byte encoding (exact)
+      sw[j] = bf16_to_f32(sws[b][row]) * 0.00390625f;
     }
     const i32x4_t zero = {0, 0, 0, 0};
 #pragma unroll
@@ -311,7 +311,7 @@ SvdqWs svdq_ws(int64_t M, int64_t K, int32_t r) {
   SvdqWs L;
   L.xc = 0;
   L.xs = up((size_t)M * K / 2);
-  L.up = L.xs + up((size_t)pad128(M) * (K / kGroupK) * 2);
+  L.up = L.xs + up((size_t)pad128(M) * (K / kGroupK) * 4);
   L.total = L.up + up(act_prep_scratch_bytes(M, K, r));
   return L;
 }
@@ -326,7 +326,7 @@ int32_t svdq_shape(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype) 
 }
 
 int32_t launch_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K, const float* rs,
-                     uint8_t* xc, uint16_t* xs, hipStream_t st) {
+                     uint8_t* xc, float* xs, hipStream_t st) {
   const int64_t lanes = M * (K / 16);
   const unsigned blocks = (unsigned)((lanes + 255) / 256);
   const int Mp = (int)pad128(M);
@@ -368,7 +368,7 @@ int32_t asp_svdq_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t r, siz
 }
 
 int32_t asp_svdq_act_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K,
-                           const uint8_t* prep_pack, uint8_t* x_codes, uint16_t* x_scales,
+                           const uint8_t* prep_pack, uint8_t* x_codes, float* x_scales,
                            void* stream) {
   clear_error();
   ASP_TRY(check_mk(M, K));
@@ -383,7 +383,7 @@ int32_t asp_svdq_act_quant(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                       x_scales, (hipStream_t)stream);
 }
 
-int32_t asp_svdq_gemm(const uint8_t* x_codes, const uint16_t* x_scales, const float* u, int64_t M,
+int32_t asp_svdq_gemm(const uint8_t* x_codes, const float* x_scales, const float* u, int64_t M,
                       int64_t N, int64_t K, int32_t r, const uint8_t* w_codes,
                       const uint16_t* w_scales, const uint16_t* l1, const float* bias, void* y,
                       int32_t y_dtype, void* stream) {
@@ -437,8 +437,8 @@ int32_t asp_svdq_forward(const void* x, int32_t x_dtype, int64_t M, int64_t K, i
     slices = (int)(act_prep_scratch_bytes(M, K, r) / ((size_t)M * P.rp32 * sizeof(float)));
   }
   ASP_TRY(launch_quant(x, x_dtype, M, K, reinterpret_cast<const float*>(prep_pack + P.cvec),
-                       base + L.xc, reinterpret_cast<uint16_t*>(base + L.xs), st));
-  SvdqGemmArgs a = {base + L.xc, reinterpret_cast<const uint16_t*>(base + L.xs), upart, w_codes,
+                       base + L.xc, reinterpret_cast<float*>(base + L.xs), st));
+  SvdqGemmArgs a = {base + L.xc, reinterpret_cast<const float*>(base + L.xs), upart, w_codes,
                     w_scales, l1, bias, y, (int)M, (int)N, (int)K, r, (int)pad128(M),
                     (int)pad128(N), slices, P.rp32, y_dtype == ASP_BF16};
   return launch_gemm(a, st);
