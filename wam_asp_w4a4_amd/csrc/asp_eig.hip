@@ -273,96 +273,125 @@ __global__ void __launch_bounds__(256) k_eig_apply(const double* __restrict__ yi
 
 // --------------------------------------------------------- one-workgroup steps
 
-// Cholesky C = L L^T and X = L^-1 by four waves.  Lane i of wave q holds
-// row i's entries in columns k = 4u + q (u < P/4) in registers.  Step j:
-// every thread takes the pivot published by the previous step, the owners of
-// column j scale it and publish it to LDS, and after a barrier every row below
-// j updates its trailing entries (right-looking order); the owner of the next
-// diagonal publishes it as soon as it is updated.  The inverse is formed the
-// same way, column c of X held by lane c of every wave: step k, the owner of
-// row k finishes x_k = (delta_{k,c} - sum_{m<k} L[k][m] x_m) / L[k][k] and
-// publishes it, and every later row adds its L[r][k] x_k.  A pivot that is not
-// a positive finite normal number is replaced by 1 and recorded in scal[1].
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Cholesky C = L L^T and X = L^-1, blocked by 16 (P/16 block steps).
+// Step jb: wave 0 factors the 16 x 16 diagonal block in registers (lane l
+// holds row l; the pivot and each finished column element reach the other
+// lanes by readlane, no barrier) and inverts it (lane c solves for column c);
+// then all waves form the panel below it, L_ij = C_ij L_jj^-T, and update the
+// trailing lower triangle, C_ik -= L_ij L_kj^T (right-looking order).  The
+// inverse's off-diagonal blocks follow by block forward substitution,
+// X_ij = -L_ii^-1 sum_{j <= k < i} L_ik X_kj, one block row at a time.  A pivot
+// that is not a positive finite normal number is replaced by 1 and recorded in
+// scal[1].
 template <int P>
 __global__ void __launch_bounds__(256) k_eig_chol(const double* __restrict__ cin,
                                                   double* __restrict__ xm,
                                                   double* __restrict__ scal) {
-  constexpr int U = P / 4;
-  __shared__ double col[P];
-  __shared__ double diag[2];
-  __shared__ double Ls[P][P + 1];
-  __shared__ double dinv[P];
-  __shared__ double xk[2][P];
-  const int q = threadIdx.x >> 6, i = threadIdx.x & 63;
-  const bool row_ok = i < P;
-  const int ii = row_ok ? i : P - 1;
-  double c[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) c[u] = cin[ii * P + 4 * u + q];
-  if (threadIdx.x == 0) diag[0] = cin[0];
+  constexpr int NB = P / 16;
+  __shared__ double C[P][P + 1];
+  __shared__ double X[P][P + 1];
+  __shared__ double Pn[P][17];     // the panel of the current step / T blocks
+  __shared__ int bad_flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < P * P; e += 256) {
+    C[e / P][e % P] = cin[e];
+    X[e / P][e % P] = 0.0;
+  }
+  if (tid == 0) bad_flag = 0;
   __syncthreads();
-  bool bad_any = false;
-  // fully unrolled: every register slot index below is a compile-time constant
+#pragma unroll 1
+  for (int jb = 0; jb < NB; ++jb) {
+    const int b0 = 16 * jb;
+    if (wave == 0) {
+      const int l = lane < 16 ? lane : 15;  // lanes past 16 mirror row 15 and store nothing
+      double d[16], inv[16];
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    double d = diag[j & 1];
-    const bool bad = !(d >= 2.2250738585072014e-308) || __builtin_isinf(d);
-    if (bad) d = 1.0;
-    bad_any |= bad;
-    const double inv = rsqrt_nr(d), piv = d * inv;
-    if (q == (j & 3) && row_ok && ii >= j) {
-      const double l = ii == j ? piv : c[j >> 2] * inv;
-      c[j >> 2] = l;
-      if (ii > j) col[ii] = l;
-      else dinv[j] = inv;
-    }
-    __syncthreads();
-    if (row_ok && ii > j) {
-      // every load is issued (all indices are in range), the update selected
-      const double li = col[ii];
+      for (int m = 0; m < 16; ++m) d[m] = C[b0 + l][b0 + m];
+      bool bad_any = false;
 #pragma unroll
-      for (int u = (j + 1) / 4; u < U; ++u) {
-        const int k = 4 * u + q;
-        const double nv = fma(-li, col[k], c[u]);
-        c[u] = k > j && k <= ii ? nv : c[u];
+      for (int k = 0; k < 16; ++k) {
+        double pv = readlane_f64(d[k], k);
+        const bool bad = !(pv >= 2.2250738585072014e-308) || __builtin_isinf(pv);
+        if (bad) pv = 1.0;
+        bad_any |= bad;
+        inv[k] = rsqrt_nr(pv);
+        const double piv = pv * inv[k];
+        d[k] = l == k ? piv : (l > k ? d[k] * inv[k] : d[k]);
+#pragma unroll
+        for (int m = k + 1; m < 16; ++m) d[m] = fma(-d[k], readlane_f64(d[k], m), d[m]);
       }
-      if (j + 1 < P && ii == j + 1 && q == ((j + 1) & 3)) diag[(j + 1) & 1] = c[(j + 1) >> 2];
-    }
-    __syncthreads();
-  }
-  if (row_ok) {
+      // column l of the block's inverse: x_r = (delta_{r,l} - sum_{t<r} L[r][t] x_t) / L[r][r]
+      double x[16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = 4 * u + q;
-      Ls[ii][k] = k <= ii ? c[u] : 0.0;
-    }
-  }
-  __syncthreads();
-  double acc[U];
+      for (int r = 0; r < 16; ++r) {
+        double acc = r == l ? 1.0 : 0.0;
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = 0.0;
-#pragma unroll
-  for (int k = 0; k < P; ++k) {
-    if (q == (k & 3) && row_ok) {
-      const double x = ((ii == k ? 1.0 : 0.0) - acc[k >> 2]) * dinv[k];
-      xk[k & 1][ii] = x;
-      acc[k >> 2] = x;
-    }
-    __syncthreads();
-    if (row_ok) {
-      const double xv = xk[k & 1][ii];
-#pragma unroll
-      for (int u = (k + 1) / 4; u < U; ++u) {
-        const double nv = fma(Ls[4 * u + q][k], xv, acc[u]);
-        acc[u] = 4 * u + q > k ? nv : acc[u];
+        for (int t = 0; t < r; ++t) acc = fma(-readlane_f64(d[t], r), x[t], acc);
+        x[r] = acc * inv[r];
       }
-    }
-  }
-  if (row_ok) {
+      if (lane < 16) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) xm[(4 * u + q) * P + ii] = acc[u];
+        for (int m = 0; m < 16; ++m)
+          if (m <= l) C[b0 + l][b0 + m] = d[m];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[b0 + r][b0 + l] = x[r];
+      }
+      if (lane == 0 && bad_any) bad_flag = 1;
+    }
+    __syncthreads();
+    const int lo = b0 + 16, rows = P - lo;
+    // panel: Pn[i][c] = sum_{t <= c} C[i][b0 + t] Linv[c][t]
+    for (int e = tid; e < rows * 16; e += 256) {
+      const int i = lo + e / 16, c = e % 16;
+      double acc = 0.0;
+      for (int t = 0; t <= c; ++t) acc = fma(C[i][b0 + t], X[b0 + c][b0 + t], acc);
+      Pn[i][c] = acc;
+    }
+    __syncthreads();
+    // trailing lower triangle, and the panel into L
+    for (int e = tid; e < rows * rows; e += 256) {
+      const int i = lo + e / rows, k = lo + e % rows;
+      if (k > i) continue;
+      double acc = C[i][k];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc = fma(-Pn[i][c], Pn[k][c], acc);
+      C[i][k] = acc;
+    }
+    for (int e = tid; e < rows * 16; e += 256) {
+      const int i = lo + e / 16, c = e % 16;
+      C[i][b0 + c] = Pn[i][c];
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0 && bad_any) scal[1] = 1.0;
+  // off-diagonal blocks of X, block row by block row
+#pragma unroll 1
+  for (int bi = 1; bi < NB; ++bi) {
+    const int r0 = 16 * bi;
+    // T_j = sum_{j <= k < bi} L[bi][k] X[k][j], for every block column j < bi, into Pn
+    for (int e = tid; e < bi * 256; e += 256) {
+      const int bj = e / 256, r = (e / 16) % 16, c = e % 16;
+      double acc = 0.0;
+      for (int t = 16 * bj; t < r0; ++t) acc = fma(C[r0 + r][t], X[t][16 * bj + c], acc);
+      Pn[16 * bj + r][c] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < bi * 256; e += 256) {
+      const int bj = e / 256, r = (e / 16) % 16, c = e % 16;
+      double acc = 0.0;
+      for (int t = 0; t <= r; ++t) acc = fma(-X[r0 + r][r0 + t], Pn[16 * bj + t][c], acc);
+      X[r0 + r][16 * bj + c] = acc;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < P * P; e += 256) xm[e] = X[e / P][e % P];
+  if (tid == 0 && bad_flag) scal[1] = 1.0;
 }
 
 // mu = 2^-16 sqrt(sum of the Frobenius partials) (1 when that is 0); clears
