@@ -395,25 +395,37 @@ __global__ void __launch_bounds__(256) k_eig_chol(const double* __restrict__ cin
 }
 
 // mu = 2^-16 sqrt(sum of the Frobenius partials) (1 when that is 0); clears
-// the breakdown flag.
-__global__ void k_eig_mu(const double* __restrict__ fro, int nb, double* __restrict__ scal) {
-  if (threadIdx.x != 0) return;
+// the breakdown flag.  One wave; fixed-order sums, so the result is the same
+// on every run.
+__global__ void __launch_bounds__(64) k_eig_mu(const double* __restrict__ fro, int nf,
+                                               double* __restrict__ scal) {
+  __shared__ double red[64];
   double s = 0.0;
-  for (int b = 0; b < nb; ++b) s += fro[b];
-  const double mu = ldexp(sqrt(s), -16);
+  for (int b = threadIdx.x; b < nf; b += 64) s += fro[b];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  double t = 0.0;
+  for (int i = 0; i < 64; ++i) t += red[i];
+  const double mu = ldexp(sqrt(t), -16);
   scal[0] = mu > 0.0 ? mu : 1.0;
   scal[1] = 0.0;
 }
 
-// Sum of squares of 64 rows of G (float64, fixed-order tree in LDS).
+constexpr int kFroRows = 8;  // rows of G per block of the Frobenius pass
+
+// Sum of squares of kFroRows rows of G (float64; each thread's share in a
+// fixed order, then a fixed-order tree in LDS).  K/8 blocks keep every CU
+// streaming: the pass reads G once at close to the HBM rate.
 __global__ void __launch_bounds__(256) k_eig_frob(const float* __restrict__ g, int K,
                                                   double* __restrict__ fro) {
   __shared__ double red[256];
-  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(g + (int64_t)blockIdx.x * kRows * K);
-  const int n4 = kRows * K / 4;
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(g + (int64_t)blockIdx.x * kFroRows * K);
+  const int n4 = kFroRows * K / 4;  // a multiple of 256 for K a multiple of 128
   double s = 0.0;
+#pragma unroll 8
   for (int e = threadIdx.x; e < n4; e += 256) {
-    const f32x4_t q = src[e];
+    const f32x4_t q = __builtin_nontemporal_load(src + e);
 #pragma unroll
     for (int j = 0; j < 4; ++j) s = fma((double)q[j], (double)q[j], s);
   }
@@ -702,7 +714,7 @@ EigLayout eig_layout(int64_t K, int p, int r) {
   L.zs = o; o += up(pp);
   L.th = o; o += up((size_t)p * 8);
   L.scal = o; o += up(8 * 8);
-  L.fro = o; o += up((size_t)L.nb * 8);
+  L.fro = o; o += up((size_t)(K / kFroRows) * 8);
   L.res2 = o; o += up((size_t)L.nb * r * 8);
   L.amv = o; o += up((size_t)L.nb * r * 8);
   L.sgn = o; o += up((size_t)r * 8);
@@ -739,8 +751,8 @@ int32_t eig_run(const float* g, int64_t K, const float* v0, int r, int iters, fl
       k_eig_apply<P, false><<<rows, blk, 0, st>>>(yin, xm, vo, nullptr);
   };
 
-  k_eig_frob<<<rows, blk, 0, st>>>(g, Ki, fro);
-  k_eig_mu<<<1, 64, 0, st>>>(fro, nb, scal);
+  k_eig_frob<<<dim3(Ki / kFroRows), blk, 0, st>>>(g, Ki, fro);
+  k_eig_mu<<<1, 64, 0, st>>>(fro, Ki / kFroRows, scal);
   k_eig_gram<P, kCast><<<rows, blk, 0, st>>>(v0, nullptr, 0, nullptr, scal, Ki, ya, cp);
   chol_apply(ya, va, iters == 0);
   for (int t = 0; t < iters; ++t) {
