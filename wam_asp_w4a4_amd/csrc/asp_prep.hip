@@ -369,19 +369,21 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
 #pragma unroll
       for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
     // all S (<= max_slices) partials are loaded before the first is used, so
-    // their latencies overlap; slices past S re-read the last one and are
-    // not added (the sum keeps slice order)
+    // their latencies overlap (the sum keeps slice order).  S is the same for
+    // every lane, so the branches are uniform and only real slices are read:
+    // every 128-column workgroup reads its rows' partials again.
     constexpr int MS = max_slices(KS);
     f32x4_t pa[MS][KS][2];
 #pragma unroll
     for (int s = 0; s < MS; ++s)
+      if (s < S)
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-            u_part + ((int64_t)min(s, S - 1) * M + mc) * RP + 32 * kk + 8 * q);
-        pa[s][kk][0] = p[0];
-        pa[s][kk][1] = p[1];
-      }
+        for (int kk = 0; kk < KS; ++kk) {
+          const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
+              u_part + ((int64_t)s * M + mc) * RP + 32 * kk + 8 * q);
+          pa[s][kk][0] = p[0];
+          pa[s][kk][1] = p[1];
+        }
 #pragma unroll
     for (int s = 0; s < MS; ++s)
       if (s < S)
