@@ -308,7 +308,7 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
 //              acc[b + 2*(c >> 2)][c & 3].
 //  quantise:   per block in one lane: amax, E4M3 scale, codes; one 16-byte
 //              code store and one 2-byte scale store per lane.
-template <typename XT, int KS>
+template <typename XT, int KS, int SMAX>
 __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int K, int r,
                                             const float* __restrict__ cvec,
                                             const uint16_t* __restrict__ vh,
@@ -324,7 +324,6 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   constexpr int RDIV = 16 / PPR;                      // rows sharing a swizzle key
   constexpr int NBQ = 1;                              // blocks per workgroup
   __shared__ u32x4_t sv[NBQ * BLK_PIECES];
-  __shared__ __attribute__((aligned(16))) float scv[NBQ][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int m0 = blockIdx.x * kPrepRows + 16 * wave;
@@ -335,91 +334,76 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   const int bq0 = blockIdx.y * NBQ;
   const int nb = min(NBQ, nblk - bq0);
 
-  if constexpr (KS > 0) {
-    const int pieces = nb * BLK_PIECES;
-    for (int base = 64 * wave; base < pieces; base += 256) {
-      const int P = base + lane;
-      const int i = P / BLK_PIECES, rem = P % BLK_PIECES;
-      const int hl = rem / (128 * PPR), row = (rem / PPR) % 128, slot = rem % PPR;
-      const int piece = slot ^ ((row / RDIV) % PPR);
-      const uint16_t* src = (hl ? vl : vh) + (int64_t)((bq0 + i) * 128 + row) * RP + 8 * piece;
-      lds_copy16(src, &sv[base]);
-    }
-  }
-  f32x4_t cr;
-  if (tid < 32 * nb) cr = reinterpret_cast<const f32x4_t*>(cvec + bq0 * 128)[tid];
+  // Load order: this wave's x first, then the block's 1/(s sqrt 128) for
+  // the lane's columns, then the shared V rows and the partial sums of u.
+  // The transform needs only the first two, so it runs while the rest is in
+  // flight (sx and sv are distinct LDS objects: reading sx waits only for
+  // the copies into sx); the workgroup meets at the barrier before the
+  // deflation, which reads V.
   // x through LDS (XStage) unless that would take static LDS past 64 KB
   // (fp32 x with r > 32): then straight to registers
   static_assert(NBQ == 1, "one block of x per wave is staged");
-  constexpr bool kStageX = sizeof(XT) == 2 || KS < 2;
+  constexpr bool kStageX = false;
   __shared__ u32x4_t sx[kStageX ? 4 : 1][kStageX ? XStage<XT>::PIECES : 1];
   XFrag<XT> xr[NBQ];
   if constexpr (kStageX)
     XStage<XT>::issue(x, m0, M, K, bq0 * 128, sx[wave], lane);
   else
     xr[0].load(x + mc * K, bq0 * 128, q);
+  // columns 64*bb + 16*q .. +15 of the block
+  f32x4_t cq[2][4];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      cq[bb][k] = reinterpret_cast<const f32x4_t*>(cvec + bq0 * 128 + 64 * bb + 16 * q)[k];
+
+  // The block's V rows (hi, lo) through registers: 16 bytes per thread and
+  // copy, written to LDS after the transform.  (A pending direct
+  // global-to-LDS copy would make the compiler wait for every load before
+  // the first use of x.)
+  constexpr int VCOPIES = KS > 0 ? BLK_PIECES / 256 : 1;
+  static_assert(KS == 0 || BLK_PIECES % 256 == 0, "whole copies per thread");
+  u32x4_t vreg[VCOPIES];
+  if constexpr (KS > 0) {
+#pragma unroll
+    for (int j = 0; j < VCOPIES; ++j) {
+      const int P = tid + 256 * j;
+      const int hl = P / (128 * PPR), row = (P / PPR) % 128, slot = P % PPR;
+      const int piece = slot ^ ((row / RDIV) % PPR);
+      vreg[j] = *reinterpret_cast<const u32x4_t*>((hl ? vl : vh) +
+                                                  (int64_t)(bq0 * 128 + row) * RP + 8 * piece);
+    }
+  }
 
   // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
   // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
   bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
+  // all S partials are loaded before the first is used, so their latencies
+  // overlap (the sum keeps slice order).  SMAX, the launch's power of two
+  // >= S, fixes the count (straight-line code); slices past S re-read the
+  // last one and are not added.
+  constexpr int MS = SMAX;
+  static_assert(KS == 0 || (SMAX >= 1 && SMAX <= max_slices(KS)), "slice bound");
+  f32x4_t pa[KS > 0 ? MS : 1][KS > 0 ? KS : 1][2];
   if constexpr (KS > 0) {
-    float us[KS][8];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
-    // all S (<= max_slices) partials are loaded before the first is used, so
-    // their latencies overlap (the sum keeps slice order).  S is the same for
-    // every lane, so the branches are uniform and only real slices are read:
-    // every 128-column workgroup reads its rows' partials again.
-    constexpr int MS = max_slices(KS);
-    f32x4_t pa[MS][KS][2];
 #pragma unroll
     for (int s = 0; s < MS; ++s)
-      if (s < S)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-              u_part + ((int64_t)s * M + mc) * RP + 32 * kk + 8 * q);
-          pa[s][kk][0] = p[0];
-          pa[s][kk][1] = p[1];
-        }
-#pragma unroll
-    for (int s = 0; s < MS; ++s)
-      if (s < S)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            us[kk][e] += pa[s][kk][0][e];
-            us[kk][4 + e] += pa[s][kk][1][e];
-          }
-    if (bq0 == 0 && mok) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (32 * kk + 8 * q + e < r) u_out[(int64_t)m * r + 32 * kk + 8 * q + e] = us[kk][e];
-    }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t hi, lo;
-        split_bf16(-us[kk][e], hi, lo);
-        nuh[kk][e] = bf16_from_bits(hi);
-        nul[kk][e] = bf16_from_bits(lo);
+      for (int kk = 0; kk < KS; ++kk) {
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
+            u_part + ((int64_t)min(s, S - 1) * M + mc) * RP + 32 * kk + 8 * q);
+        pa[s][kk][0] = p[0];
+        pa[s][kk][1] = p[1];
       }
   }
-  if (tid < 32 * nb) reinterpret_cast<f32x4_t*>(&scv[0][0])[tid] = cr;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS copies have landed
-  __syncthreads();
-  if constexpr (kStageX) xr[0].load_lds(sx[wave], q, l16);
 
-#pragma unroll
-  for (int i = 0; i < NBQ; ++i) {
-    if (i >= nb) break;
-    const int col0 = (bq0 + i) * 128;
+  // every load is issued before the transform starts
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kStageX) xr[0].load_lds(sx[wave], q, l16);
+  constexpr int i = 0;
+  const int col0 = bq0 * 128;
+  {
     // w[bb][j]: column 64*bb + 16*q + j of the block times 1/(s sqrt 128); the
     // scaling is folded into the first butterfly stage (pairs j, j+1)
     float w[2][16];
@@ -427,11 +411,9 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
     for (int bb = 0; bb < 2; ++bb) {
       float cv[16], xv[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4_t t = reinterpret_cast<const f32x4_t*>(&scv[i][64 * bb + 16 * q])[k];
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cv[4 * k + e] = t[e];
-      }
+        for (int e = 0; e < 4; ++e) cv[4 * k + e] = cq[bb][k][e];
       xr[i].get(2 * bb, xv);
       xr[i].get(2 * bb + 1, xv + 8);
 #pragma unroll
@@ -471,6 +453,45 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if ((j & 8) == 0) swap32_butterfly(w[bb][j], w[bb][j + 8]);
+
+    if constexpr (KS > 0) {
+      float us[KS][8];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < MS; ++s)
+        if (s < S)
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              us[kk][e] += pa[s][kk][0][e];
+              us[kk][4 + e] += pa[s][kk][1][e];
+            }
+      if (bq0 == 0 && mok) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * kk + 8 * q + e < r) u_out[(int64_t)m * r + 32 * kk + 8 * q + e] = us[kk][e];
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint16_t hi, lo;
+          split_bf16(-us[kk][e], hi, lo);
+          nuh[kk][e] = bf16_from_bits(hi);
+          nul[kk][e] = bf16_from_bits(lo);
+        }
+    }
+    if constexpr (KS > 0) {
+#pragma unroll
+      for (int j = 0; j < VCOPIES; ++j) sv[tid + 256 * j] = vreg[j];
+    }
+    __syncthreads();  // V is in LDS for every wave
     // now w[bb][j] is column 16*t + 4*q + (j & 3) with tile t = (j >> 2) + 4*bb
     f32x4_t acc[8];
 #pragma unroll
@@ -568,11 +589,12 @@ __global__ void __launch_bounds__(256) k_prep_u(const PrepArgs<XT> a, int M, int
   prep_u_body<XT, KS>(L.x, M, K, r, L.vth, L.vtl, L.u_part, bps);
 }
 
-template <typename XT, int KS>
+template <typename XT, int KS, int SMAX>
 __global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int K, int r,
                                                 int S) {
   const PrepLayerArgs<XT>& L = a.l[blockIdx.z];
-  prep_q_body<XT, KS>(L.x, M, K, r, L.cvec, L.vh, L.vl, L.u_part, S, L.xc, L.xs, L.u, L.pre);
+  prep_q_body<XT, KS, SMAX>(L.x, M, K, r, L.cvec, L.vh, L.vl, L.u_part, S, L.xc, L.xs, L.u,
+                            L.pre);
 }
 
 constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
@@ -606,9 +628,21 @@ void launch_ks(hipStream_t st, int stages, int n, const PrepArgs<XT>& a, int M, 
                          dim3(256), lds, st, a, M, K, r, bps);
     }
   }
-  if (stages & kStageQ)
-    hipLaunchKernelGGL((k_prep_q<XT, KS>), dim3((unsigned)tiles64, (unsigned)nblk, (unsigned)n),
-                       dim3(256), 0, st, a, M, K, r, S);
+  if (stages & kStageQ) {
+    const dim3 grid((unsigned)tiles64, (unsigned)nblk, (unsigned)n);
+    if constexpr (KS == 0) {
+      hipLaunchKernelGGL((k_prep_q<XT, 0, 1>), grid, dim3(256), 0, st, a, M, K, r, S);
+    } else if (S <= 1) {
+      hipLaunchKernelGGL((k_prep_q<XT, KS, 1>), grid, dim3(256), 0, st, a, M, K, r, S);
+    } else if (S <= 2) {
+      hipLaunchKernelGGL((k_prep_q<XT, KS, 2>), grid, dim3(256), 0, st, a, M, K, r, S);
+    } else if (KS > 1 || S <= 4) {
+      hipLaunchKernelGGL((k_prep_q<XT, KS, 4>), grid, dim3(256), 0, st, a, M, K, r, S);
+    } else {
+      hipLaunchKernelGGL((k_prep_q<XT, KS, (KS > 1 ? 4 : 8)>), grid, dim3(256), 0, st, a, M, K,
+                         r, S);
+    }
+  }
 }
 
 template <typename XT>
