@@ -16,11 +16,13 @@
 //            split into bf16 high + low) and V'' high + low (about 16
 //            significant bits; the dropped low*low term lies below float32
 //            rounding).  Writes S partial sums of u.
-//  k_prep_q  workgroup = 64 rows x one 128-column Hadamard block, V's rows for
-//            the block and 1/(s sqrt 128) staged in LDS; each wave adds the S
-//            partial sums of u for its 16 rows in a fixed order (so results
-//            are deterministic), then transforms, deflates on MFMA, quantises
-//            and stores.  For r == 0 it runs alone, without u and V.
+//  k_prep_q  workgroup = 64 rows x one 128-column Hadamard block.  Each wave
+//            loads its 16 rows of x, the block's 1/(s sqrt 128), its share of
+//            the block's V rows and the S partial sums of u for its rows, all
+//            at once into registers; it transforms x while the rest arrives,
+//            puts V in LDS for the workgroup, adds the partial sums in a fixed
+//            order (so results are deterministic), then deflates on MFMA,
+//            quantises and stores.  For r == 0 it runs alone, without u and V.
 //
 // S depends on K only, so a row's results do not depend on the batch it is in.
 #include "asp_device.h"
@@ -335,21 +337,15 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   const int nb = min(NBQ, nblk - bq0);
 
   // Load order: this wave's x first, then the block's 1/(s sqrt 128) for
-  // the lane's columns, then the shared V rows and the partial sums of u.
-  // The transform needs only the first two, so it runs while the rest is in
-  // flight (sx and sv are distinct LDS objects: reading sx waits only for
-  // the copies into sx); the workgroup meets at the barrier before the
-  // deflation, which reads V.
-  // x through LDS (XStage) unless that would take static LDS past 64 KB
-  // (fp32 x with r > 32): then straight to registers
-  static_assert(NBQ == 1, "one block of x per wave is staged");
-  constexpr bool kStageX = false;
-  __shared__ u32x4_t sx[kStageX ? 4 : 1][kStageX ? XStage<XT>::PIECES : 1];
+  // the lane's columns, then the block's V rows and the partial sums of u,
+  // all as straight-line register loads so that the compiler waits for each
+  // by count.  The transform needs only the first two, so it runs while the
+  // rest is in flight; V goes to LDS after it, and the workgroup meets at
+  // the barrier before the deflation, which reads V.
+  // x straight into registers (the lane's 32 values of its row)
+  static_assert(NBQ == 1, "one block of x per wave");
   XFrag<XT> xr[NBQ];
-  if constexpr (kStageX)
-    XStage<XT>::issue(x, m0, M, K, bq0 * 128, sx[wave], lane);
-  else
-    xr[0].load(x + mc * K, bq0 * 128, q);
+  xr[0].load(x + mc * K, bq0 * 128, q);
   // columns 64*bb + 16*q .. +15 of the block
   f32x4_t cq[2][4];
 #pragma unroll
@@ -400,7 +396,6 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
 
   // every load is issued before the transform starts
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kStageX) xr[0].load_lds(sx[wave], q, l16);
   constexpr int i = 0;
   const int col0 = bq0 * 128;
   {
