@@ -165,6 +165,23 @@ def test_act_prep_against_oracle(lay):
     assert np.mean(xs != act["x_scales"]) <= 1e-3
 
 
+@pytest.mark.parametrize("M,K,r,dtype", [(4096, 2048, 32, "bf16"), (2000, 4096, 32, "bf16"),
+                                          (4096, 2048, 64, "f32"), (4096, 2048, 0, "bf16")],
+                         ids=["S4", "S8-ragged-M", "r64-f32", "r0"])
+def test_act_prep_rows_bitwise_large_batch(M, K, r, dtype):
+    """Rows of a large batch (at least 1024 workgroups of 64 rows x 128
+    columns) and the same rows prepared as a batch of a few hundred give the
+    same codes, scales, u and pre-quantisation values, bit for bit."""
+    lay = synth.make_layer("loop", M, K, 32, r, seed=M + K + r, dtype=dtype)
+    assert (M + 63) // 64 * (K // 128) >= 1024
+    full = gpu_act_prep(lay)
+    rows = np.unique(np.r_[0:64, M - 64:M, 1000:1010, 1234])
+    part = gpu_act_prep(dataclasses.replace(lay, M=len(rows), x=lay.x[rows]))
+    for a, b in zip(full, part):
+        if a is not None:
+            assert np.array_equal(a[rows], b)
+
+
 @pytest.mark.parametrize("lay", prep_cases(), ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-r{l.r}")
 def test_act_prep_stages_equal_combined(lay):
     """asp_act_prep_u then asp_act_prep_q reproduce asp_act_prep bit for bit."""

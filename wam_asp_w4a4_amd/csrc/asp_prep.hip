@@ -310,6 +310,263 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
 //              acc[b + 2*(c >> 2)][c & 3].
 //  quantise:   per block in one lane: amax, E4M3 scale, codes; one 16-byte
 //              code store and one 2-byte scale store per lane.
+// One wave's loads for one 16-row x 128-column unit: its rows of x and the
+// partial sums of u for those rows.  SMAX, the launch's power of two >= S,
+// fixes the count (straight-line code, so the compiler waits for each load
+// by count); slices past S re-read the last one and are not added.
+template <typename XT, int KS, int SMAX>
+struct QUnit {
+  static constexpr int MS = KS > 0 ? SMAX : 1, KK = KS > 0 ? KS : 1;
+  static_assert(KS == 0 || (SMAX >= 1 && SMAX <= max_slices(KS)), "slice bound");
+  XFrag<XT> x;
+  f32x4_t pa[MS][KK][2];
+
+  // row mc (already clamped to M - 1) of this lane, the block at column col0
+  __device__ __forceinline__ void issue(const XT* __restrict__ xp, int M, int K, int col0,
+                                        const float* __restrict__ u_part, int S, int64_t mc,
+                                        int q) {
+    x.load(xp + mc * K, col0, q);
+    issue_u(M, u_part, S, mc, q);
+  }
+  __device__ __forceinline__ void issue_u(int M, const float* __restrict__ u_part, int S,
+                                          int64_t mc, int q) {
+    if constexpr (KS > 0) {
+      constexpr int RP = KS * 32;
+#pragma unroll
+      for (int s = 0; s < MS; ++s)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
+              u_part + ((int64_t)min(s, S - 1) * M + mc) * RP + 32 * kk + 8 * q);
+          pa[s][kk][0] = p[0];
+          pa[s][kk][1] = p[1];
+        }
+    }
+  }
+};
+
+// 1/(s sqrt 128) of the lane's 32 columns 64*bb + 16*q + j of the block
+__device__ __forceinline__ void load_col_scales(const float* __restrict__ cvec, int col0, int q,
+                                                f32x4_t (&cq)[2][4]) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      cq[bb][k] = reinterpret_cast<const f32x4_t*>(cvec + col0 + 64 * bb + 16 * q)[k];
+}
+
+// The block's V rows (hi, lo) through registers, 16 bytes per thread and
+// copy; written to LDS by store_v.  (A pending direct global-to-LDS copy
+// would make the compiler wait for every load before the first use of any.)
+template <int KS>
+struct VRows {
+  static constexpr int RP = KS * 32;
+  static constexpr int PPR = KS > 0 ? RP / 8 : 1;          // 16-byte pieces per V row
+  static constexpr int PIECES = KS > 0 ? 2 * 128 * PPR : 1;
+  static constexpr int RDIV = 16 / PPR;                     // rows sharing a swizzle key
+  static constexpr int COPIES = KS > 0 ? PIECES / 256 : 1;
+  static_assert(KS == 0 || PIECES % 256 == 0, "whole copies per thread");
+  u32x4_t reg[COPIES];
+  // piece p of row `row` (hi rows first, then lo) sits in slot
+  // p ^ ((row / RDIV) % PPR): the 16 lanes of a quarter read one piece of 16
+  // consecutive rows and hit 16 different bank groups
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ vh,
+                                        const uint16_t* __restrict__ vl, int bq, int tid) {
+    if constexpr (KS > 0) {
+#pragma unroll
+      for (int j = 0; j < COPIES; ++j) {
+        const int P = tid + 256 * j;
+        const int hl = P / (128 * PPR), row = (P / PPR) % 128, slot = P % PPR;
+        const int piece = slot ^ ((row / RDIV) % PPR);
+        reg[j] = *reinterpret_cast<const u32x4_t*>((hl ? vl : vh) +
+                                                   (int64_t)(bq * 128 + row) * RP + 8 * piece);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(u32x4_t* sv, int tid) const {
+    if constexpr (KS > 0) {
+#pragma unroll
+      for (int j = 0; j < COPIES; ++j) sv[tid + 256 * j] = reg[j];
+    }
+  }
+};
+
+// Smoothing and the Sylvester transform of one unit: w[bb][j] is afterwards
+// column 16*t + 4*q + (j & 3) of the block, tile t = (j >> 2) + 4*bb.
+template <typename XT>
+__device__ __forceinline__ void q_transform(const XFrag<XT>& xr, const f32x4_t (&cq)[2][4],
+                                            float (&w)[2][16]) {
+  // column 64*bb + 16*q + j of the block times 1/(s sqrt 128); the scaling
+  // is folded into the first butterfly stage (pairs j, j+1)
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    float cv[16], xv[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cv[4 * k + e] = cq[bb][k][e];
+    xr.get(2 * bb, xv);
+    xr.get(2 * bb + 1, xv + 8);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const float t = xv[j + 1] * cv[j + 1];
+      w[bb][j] = __builtin_fmaf(xv[j], cv[j], t);
+      w[bb][j + 1] = __builtin_fmaf(xv[j], cv[j], -t);
+    }
+  }
+  // Sylvester butterflies on column bits 1..3 (j) and 6 (bb)
+#pragma unroll
+  for (int hs = 2; hs < 16; hs <<= 1)
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if ((j & hs) == 0) {
+          const float a = w[bb][j], c = w[bb][j + hs];
+          w[bb][j] = a + c;
+          w[bb][j + hs] = a - c;
+        }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float a = w[0][j], c = w[1][j];
+    w[0][j] = a + c;
+    w[1][j] = a - c;
+  }
+  // column bit 4 (lane bit q0) against column bit 2 (j bit 2), then column
+  // bit 5 (lane bit q1) against column bit 3 (j bit 3)
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & 4) == 0) swap16_butterfly(w[bb][j], w[bb][j + 4]);
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((j & 8) == 0) swap32_butterfly(w[bb][j], w[bb][j + 8]);
+}
+
+// The rest of one unit, after the transform and with the block's V in LDS:
+// u from its partial sums (slice order), the deflation on MFMA, the
+// transpose to whole NVFP4 blocks per lane, quantisation and the stores.
+// Row m of this lane (mc = min(m, M - 1)), block bq at column col0.
+template <typename XT, int KS, int SMAX>
+__device__ __forceinline__ void q_finish(float (&w)[2][16], const QUnit<XT, KS, SMAX>& U, int S,
+                                         const u32x4_t* sv, int M, int K, int r, int bq, int m,
+                                         int64_t mc, int q, int l16,
+                                         uint8_t* __restrict__ codes,
+                                         uint8_t* __restrict__ scales,
+                                         float* __restrict__ u_out, float* __restrict__ pre) {
+  using VR = VRows<KS>;
+  constexpr int MS = QUnit<XT, KS, SMAX>::MS;
+  const bool mok = m < M;
+  const int col0 = bq * 128;
+  // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
+  // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
+  bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
+  if constexpr (KS > 0) {
+    float us[KS][8];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+      if (s < S)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            us[kk][e] += U.pa[s][kk][0][e];
+            us[kk][4 + e] += U.pa[s][kk][1][e];
+          }
+    if (bq == 0 && mok) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (32 * kk + 8 * q + e < r) u_out[(int64_t)m * r + 32 * kk + 8 * q + e] = us[kk][e];
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t hi, lo;
+        split_bf16(-us[kk][e], hi, lo);
+        nuh[kk][e] = bf16_from_bits(hi);
+        nul[kk][e] = bf16_from_bits(lo);
+      }
+  }
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] = w[t >> 2][4 * (t & 3) + e];
+  if constexpr (KS > 0) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      bf16x8_t a_hi[8], a_lo[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = 16 * t + l16, piece = 4 * kk + q;
+        const int slot = row * VR::PPR + (piece ^ ((row / VR::RDIV) % VR::PPR));
+        a_hi[t] = as_bf16x8(sv[slot]);
+        a_lo[t] = as_bf16x8(sv[128 * VR::PPR + slot]);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nuh[kk], acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nul[kk], acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], nuh[kk], acc[t], 0, 0, 0);
+    }
+  }
+  // lane quarters against tile bits: afterwards the lane holds tiles 2q and
+  // 2q+1 whole
+  float a[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[t][e] = acc[t][e];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) swap32(a[t][e], a[t + 4][e]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if ((j & 2) == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) swap16(a[j][e], a[j + 2][e]);
+  uint32_t sc[2];
+  uint2 cw[2];
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = a[bt + 2 * (c >> 2)][c & 3];
+    cw[bt] = quantize_block(v, sc[bt]);
+    if (pre && mok) {
+      float4* pp = reinterpret_cast<float4*>(pre + mc * K + col0 + 32 * q + 16 * bt);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pp[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    }
+  }
+  if (mok) {
+    *reinterpret_cast<uint4*>(codes + mc * (K / 2) + col0 / 2 + 16 * q) =
+        make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
+    *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) =
+        (uint16_t)(sc[0] | (sc[1] << 8));
+  }
+}
+
+// k_prep_q, one unit per wave (workgroup = 64 rows x block blockIdx.y).
+// Every load is issued first: x, the column scales, V, the partial sums;
+// the transform runs while V and u are in flight, and the workgroup meets at
+// one barrier once V is in LDS.
 template <typename XT, int KS, int SMAX>
 __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int K, int r,
                                             const float* __restrict__ cvec,
@@ -320,240 +577,26 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
                                             uint8_t* __restrict__ scales,
                                             float* __restrict__ u_out,
                                             float* __restrict__ pre) {
-  constexpr int RP = KS * 32;
-  constexpr int PPR = KS > 0 ? RP / 8 : 1;           // 16-byte pieces per V row
-  constexpr int BLK_PIECES = KS > 0 ? 2 * 128 * PPR : 1;
-  constexpr int RDIV = 16 / PPR;                      // rows sharing a swizzle key
-  constexpr int NBQ = 1;                              // blocks per workgroup
-  __shared__ u32x4_t sv[NBQ * BLK_PIECES];
+  __shared__ u32x4_t sv[VRows<KS>::PIECES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const int m0 = blockIdx.x * kPrepRows + 16 * wave;
-  const int m = m0 + l16;
+  const int m = blockIdx.x * kPrepRows + 16 * wave + l16;
   const int64_t mc = min(m, M - 1);
-  const bool mok = m < M;
-  const int nblk = K >> 7;
-  const int bq0 = blockIdx.y * NBQ;
-  const int nb = min(NBQ, nblk - bq0);
+  const int bq = blockIdx.y;
 
-  // Load order: this wave's x first, then the block's 1/(s sqrt 128) for
-  // the lane's columns, then the block's V rows and the partial sums of u,
-  // all as straight-line register loads so that the compiler waits for each
-  // by count.  The transform needs only the first two, so it runs while the
-  // rest is in flight; V goes to LDS after it, and the workgroup meets at
-  // the barrier before the deflation, which reads V.
-  // x straight into registers (the lane's 32 values of its row)
-  static_assert(NBQ == 1, "one block of x per wave");
-  XFrag<XT> xr[NBQ];
-  xr[0].load(x + mc * K, bq0 * 128, q);
-  // columns 64*bb + 16*q .. +15 of the block
+  QUnit<XT, KS, SMAX> U;
   f32x4_t cq[2][4];
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      cq[bb][k] = reinterpret_cast<const f32x4_t*>(cvec + bq0 * 128 + 64 * bb + 16 * q)[k];
-
-  // The block's V rows (hi, lo) through registers: 16 bytes per thread and
-  // copy, written to LDS after the transform.  (A pending direct
-  // global-to-LDS copy would make the compiler wait for every load before
-  // the first use of x.)
-  constexpr int VCOPIES = KS > 0 ? BLK_PIECES / 256 : 1;
-  static_assert(KS == 0 || BLK_PIECES % 256 == 0, "whole copies per thread");
-  u32x4_t vreg[VCOPIES];
-  if constexpr (KS > 0) {
-#pragma unroll
-    for (int j = 0; j < VCOPIES; ++j) {
-      const int P = tid + 256 * j;
-      const int hl = P / (128 * PPR), row = (P / PPR) % 128, slot = P % PPR;
-      const int piece = slot ^ ((row / RDIV) % PPR);
-      vreg[j] = *reinterpret_cast<const u32x4_t*>((hl ? vl : vh) +
-                                                  (int64_t)(bq0 * 128 + row) * RP + 8 * piece);
-    }
-  }
-
-  // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
-  // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
-  bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
-  // all S partials are loaded before the first is used, so their latencies
-  // overlap (the sum keeps slice order).  SMAX, the launch's power of two
-  // >= S, fixes the count (straight-line code); slices past S re-read the
-  // last one and are not added.
-  constexpr int MS = SMAX;
-  static_assert(KS == 0 || (SMAX >= 1 && SMAX <= max_slices(KS)), "slice bound");
-  f32x4_t pa[KS > 0 ? MS : 1][KS > 0 ? KS : 1][2];
-  if constexpr (KS > 0) {
-#pragma unroll
-    for (int s = 0; s < MS; ++s)
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-            u_part + ((int64_t)min(s, S - 1) * M + mc) * RP + 32 * kk + 8 * q);
-        pa[s][kk][0] = p[0];
-        pa[s][kk][1] = p[1];
-      }
-  }
-
-  // every load is issued before the transform starts
-  __builtin_amdgcn_sched_barrier(0);
-  constexpr int i = 0;
-  const int col0 = bq0 * 128;
-  {
-    // w[bb][j]: column 64*bb + 16*q + j of the block times 1/(s sqrt 128); the
-    // scaling is folded into the first butterfly stage (pairs j, j+1)
-    float w[2][16];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      float cv[16], xv[16];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cv[4 * k + e] = cq[bb][k][e];
-      xr[i].get(2 * bb, xv);
-      xr[i].get(2 * bb + 1, xv + 8);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const float t = xv[j + 1] * cv[j + 1];
-        w[bb][j] = __builtin_fmaf(xv[j], cv[j], t);
-        w[bb][j + 1] = __builtin_fmaf(xv[j], cv[j], -t);
-      }
-    }
-    // Sylvester butterflies on column bits 1..3 (j) and 6 (bb)
-#pragma unroll
-    for (int hs = 2; hs < 16; hs <<= 1)
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((j & hs) == 0) {
-            const float a = w[bb][j], c = w[bb][j + hs];
-            w[bb][j] = a + c;
-            w[bb][j + hs] = a - c;
-          }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float a = w[0][j], c = w[1][j];
-      w[0][j] = a + c;
-      w[1][j] = a - c;
-    }
-    // column bit 4 (lane bit q0) against column bit 2 (j bit 2), then column
-    // bit 5 (lane bit q1) against column bit 3 (j bit 3)
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((j & 4) == 0) swap16_butterfly(w[bb][j], w[bb][j + 4]);
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if ((j & 8) == 0) swap32_butterfly(w[bb][j], w[bb][j + 8]);
-
-    if constexpr (KS > 0) {
-      float us[KS][8];
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) us[kk][e] = 0.0f;
-#pragma unroll
-      for (int s = 0; s < MS; ++s)
-        if (s < S)
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              us[kk][e] += pa[s][kk][0][e];
-              us[kk][4 + e] += pa[s][kk][1][e];
-            }
-      if (bq0 == 0 && mok) {
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (32 * kk + 8 * q + e < r) u_out[(int64_t)m * r + 32 * kk + 8 * q + e] = us[kk][e];
-      }
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint16_t hi, lo;
-          split_bf16(-us[kk][e], hi, lo);
-          nuh[kk][e] = bf16_from_bits(hi);
-          nul[kk][e] = bf16_from_bits(lo);
-        }
-    }
-    if constexpr (KS > 0) {
-#pragma unroll
-      for (int j = 0; j < VCOPIES; ++j) sv[tid + 256 * j] = vreg[j];
-    }
-    __syncthreads();  // V is in LDS for every wave
-    // now w[bb][j] is column 16*t + 4*q + (j & 3) with tile t = (j >> 2) + 4*bb
-    f32x4_t acc[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = w[t >> 2][4 * (t & 3) + e];
-    if constexpr (KS > 0) {
-      const u32x4_t* vb = sv + i * BLK_PIECES;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        bf16x8_t a_hi[8], a_lo[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int row = 16 * t + l16, piece = 4 * kk + q;
-          const int slot = row * PPR + (piece ^ ((row / RDIV) % PPR));
-          a_hi[t] = as_bf16x8(vb[slot]);
-          a_lo[t] = as_bf16x8(vb[128 * PPR + slot]);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nuh[kk], acc[t], 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nul[kk], acc[t], 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], nuh[kk], acc[t], 0, 0, 0);
-      }
-    }
-    // lane quarters against tile bits: afterwards the lane holds tiles 2q and
-    // 2q+1 whole
-    float a[8][4];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[t][e] = acc[t][e];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) swap32(a[t][e], a[t + 4][e]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((j & 2) == 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) swap16(a[j][e], a[j + 2][e]);
-    uint32_t sc[2];
-    uint2 cw[2];
-#pragma unroll
-    for (int bt = 0; bt < 2; ++bt) {
-      float v[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c) v[c] = a[bt + 2 * (c >> 2)][c & 3];
-      cw[bt] = quantize_block(v, sc[bt]);
-      if (pre && mok) {
-        float4* pp = reinterpret_cast<float4*>(pre + mc * K + col0 + 32 * q + 16 * bt);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          pp[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-      }
-    }
-    if (mok) {
-      *reinterpret_cast<uint4*>(codes + mc * (K / 2) + col0 / 2 + 16 * q) =
-          make_uint4(cw[0].x, cw[0].y, cw[1].x, cw[1].y);
-      *reinterpret_cast<uint16_t*>(scales + mc * (K / 16) + col0 / 16 + 2 * q) =
-          (uint16_t)(sc[0] | (sc[1] << 8));
-    }
-  }
+  VRows<KS> V;
+  U.x.load(x + mc * K, bq * 128, q);
+  load_col_scales(cvec, bq * 128, q, cq);
+  V.issue(vh, vl, bq, tid);
+  U.issue_u(M, u_part, S, mc, q);
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before the transform
+  float w[2][16];
+  q_transform(U.x, cq, w);
+  V.store(sv, tid);
+  __syncthreads();  // V is in LDS for every wave
+  q_finish(w, U, S, sv, M, K, r, bq, m, mc, q, l16, codes, scales, u_out, pre);
 }
 
 // Per-layer pointers of a (grouped) launch; layer = blockIdx.z.
@@ -592,6 +635,7 @@ __global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int
                             L.pre);
 }
 
+
 constexpr int kStageU = 1, kStageQ = 2;  // the two launches of the prep
 
 // Slices of K for the partial sums of u (a function of K and the padded rank
@@ -602,6 +646,14 @@ void u_slicing(int64_t K, int ks, int* S, int* bps) {
   const int s = std::min(nblk, nblk >= 32 ? max_slices(ks) : 4);
   *bps = (nblk + s - 1) / s;
   *S = (nblk + *bps - 1) / *bps;
+}
+
+template <typename XT, int KS, int SMAX>
+void launch_q(hipStream_t st, int n, const PrepArgs<XT>& a, int M, int K, int r, int S) {
+  const int nblk = K / 128;
+  const int tiles64 = (M + kPrepRows - 1) / kPrepRows;
+  hipLaunchKernelGGL((k_prep_q<XT, KS, SMAX>), dim3((unsigned)tiles64, (unsigned)nblk, (unsigned)n),
+                     dim3(256), 0, st, a, M, K, r, S);
 }
 
 template <typename XT, int KS>
@@ -624,18 +676,16 @@ void launch_ks(hipStream_t st, int stages, int n, const PrepArgs<XT>& a, int M, 
     }
   }
   if (stages & kStageQ) {
-    const dim3 grid((unsigned)tiles64, (unsigned)nblk, (unsigned)n);
     if constexpr (KS == 0) {
-      hipLaunchKernelGGL((k_prep_q<XT, 0, 1>), grid, dim3(256), 0, st, a, M, K, r, S);
+      launch_q<XT, 0, 1>(st, n, a, M, K, r, S);
     } else if (S <= 1) {
-      hipLaunchKernelGGL((k_prep_q<XT, KS, 1>), grid, dim3(256), 0, st, a, M, K, r, S);
+      launch_q<XT, KS, 1>(st, n, a, M, K, r, S);
     } else if (S <= 2) {
-      hipLaunchKernelGGL((k_prep_q<XT, KS, 2>), grid, dim3(256), 0, st, a, M, K, r, S);
+      launch_q<XT, KS, 2>(st, n, a, M, K, r, S);
     } else if (KS > 1 || S <= 4) {
-      hipLaunchKernelGGL((k_prep_q<XT, KS, 4>), grid, dim3(256), 0, st, a, M, K, r, S);
+      launch_q<XT, KS, 4>(st, n, a, M, K, r, S);
     } else {
-      hipLaunchKernelGGL((k_prep_q<XT, KS, (KS > 1 ? 4 : 8)>), grid, dim3(256), 0, st, a, M, K,
-                         r, S);
+      launch_q<XT, KS, (KS > 1 ? 4 : 8)>(st, n, a, M, K, r, S);
     }
   }
 }
