@@ -43,8 +43,10 @@
  *     points only enqueue work and return; faults raised while kernels run
  *     surface at the caller's next synchronisation with that stream.
  *   - Device pointers must be 16-byte aligned.  Inputs must be finite.
- *   - Supported shapes: K a positive multiple of 128; M >= 0 (M == 0 is a
- *     no-op); N >= 1; 0 <= r <= 64.
+ *   - Supported shapes: K a positive multiple of 128 (device entry points:
+ *     at most 2^20); 0 <= M < 2^31 (M == 0 is a no-op); 1 <= N < 2^31;
+ *     0 <= r <= 64.  Out-of-range shapes return ASP_ERR_SHAPE before
+ *     anything is enqueued.
  */
 #ifndef ASP_H
 #define ASP_H

@@ -172,6 +172,8 @@ def test_forward_group_validation():
     assert grp(2, arrays=False) == 1
     assert grp(2, wv=False) == 1           # r > 0 needs the wv array
     assert grp(2, K=100) == 2
+    assert grp(2, K=(1 << 20) + 128) == 2   # above the device path's K limit
+    assert "above" in B.asp_last_error()
     assert grp(2, x_dtype=7) == 1
     assert grp(2, N=(64, 0)) == 2
     assert grp(2, ws=(FAKE, FAKE + 16)) == 3

@@ -326,6 +326,37 @@ def test_forward_sampled_rows_of_mot_layers():
         check_layer(lay, rows=rows, label="mot")
 
 
+def test_forward_maximum_k():
+    """K at the device path's limit (2^20, so 8192 Hadamard blocks and 8
+    slices of 131072 for u) with a ragged batch: every output against the
+    float64 oracle at the 2e-3 gate, and against the oracle's contraction of
+    the device's own codes at the usual 1e-5 (each of the 8 waves of the
+    split-K GEMM adds 8192 K-steps in float32)."""
+    lay = synth.make_layer("max-K", 5, 1 << 20, 24, 32, seed=20, dtype="bf16")
+    p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
+    y32 = host(p.forward(x_device(lay), "f32"))
+    want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
+    e32 = rel_fro(y32, want)
+    xc, xs, u, _ = gpu_act_prep(lay)
+    pk = OA.pack_weight(lay.w, lay.s, lay.v)
+    mine = OA.output_from_codes(xc, xs, u.astype(np.float64), pk["w_codes"], pk["w_scales"],
+                                pk["wv"], lay.b)
+    tight = rel_fro(y32, mine)
+    act = OA.activation_side(lay.x, lay.s, lay.v)
+    flips = np.mean(OF.unpack_codes(xc) != OF.unpack_codes(act["x_codes"]))
+    print(f"K = 2^20: rel err {e32:.3e}, vs own codes {tight:.2e}, codes off {flips:.2e}")
+    assert e32 <= 2e-3 and tight <= 1e-5 and flips <= 1e-3
+
+
+def test_forward_large_batch_sampled_rows():
+    """131072 rows (2048 row tiles of the prep, 512 of the GEMM): sampled rows
+    against the float64 oracle, the rest by row independence."""
+    lay = synth.make_layer("large-M", 1 << 17, 256, 48, 32, seed=21, dtype="bf16")
+    rows = np.sort(np.random.default_rng(21).choice(lay.M, size=64, replace=False))
+    rows[-1] = lay.M - 1
+    check_layer(lay, rows=rows, label="large batch")
+
+
 @pytest.mark.parametrize("M,N,K,r", [(1, 16, 128, 0), (37, 48, 256, 1), (200, 200, 384, 16),
                                      (129, 130, 128, 33), (64, 64, 512, 64), (300, 16, 1280, 32),
                                      # 64 x 64 tiles with r % 16 == 8 (a half-empty last
