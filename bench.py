@@ -129,6 +129,11 @@ def parse():
     ap.add_argument("--svdq", action="store_true",
                     help="time the SVDQuant-style INT4 (group 64) W4A4 arm on the workload's "
                          "layer shapes instead of the deflated-ASP NVFP4 path")
+    ap.add_argument("--mot", action="store_true",
+                    help="time the 600-layer two-expert set (30 blocks per expert, 10 linears "
+                         "each) as one stream of quantised linears per denoising step")
+    ap.add_argument("--mot-steps", type=int, default=10,
+                    help="denoising steps timed by --mot (the set's own count is 10)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (the reference "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -184,6 +189,9 @@ def main():
         return
     if args.svdq:
         svdq_bench(args, dev)
+        return
+    if args.mot:
+        mot_bench(args, dev)
         return
     layers = synth.workload(args.workload)
     if args.search:
@@ -746,6 +754,153 @@ def svdq_bench(args, dev):
                    "flops_per_step": flops, "replicas": R,
                    "timing": "one HIP graph of K steps, events on the capture stream"},
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+# Calls per block of one expert in the 600-layer set: projections that read
+# one input in a real block go together (self-attention q, k, v; cross-attention
+# k, v), the others alone.
+MOT_GROUPS = [("self_attn.q", "self_attn.k", "self_attn.v"), ("self_attn.o",),
+              ("cross_attn.q",), ("cross_attn.k", "cross_attn.v"), ("cross_attn.o",),
+              ("ffn.0",), ("ffn.2",)]
+
+
+def mot_bench(args, dev):
+    """The 600-layer two-expert set (video: d 3072, ffn 14336, M 4096, r 0;
+    action: d 1024, ffn 4096, M 256, r 32) as one stream of quantised linears
+    per denoising step, all weights and inputs resident in HBM.  Every layer
+    has its own packed weight, prep pack, input and output; the inputs and
+    weights are random device tensors (the kernels' timing does not depend on
+    the values; parity on sampled layers of this set is in the GPU tests)."""
+    import torch
+    from wam_asp_w4a4_amd import binding as B
+    from wam_asp_w4a4_amd import synth
+
+    gen = torch.Generator(device=dev).manual_seed(synth.DEFAULT_SEED)
+    prep_host = {}
+
+    def prep_pack(K, r):
+        if (K, r) not in prep_host:
+            rng = np.random.default_rng(K + r)
+            s_ = (1.0 + rng.random(K)).astype(np.float32)
+            v = (rng.standard_normal((K, r)) / np.sqrt(K)).astype(np.float32) if r else None
+            pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
+            B.asp_pack_prep(K, r, s_, v, pack)
+            prep_host[(K, r)] = torch.from_numpy(pack)
+        return prep_host[(K, r)].to(dev)
+
+    layers = {}
+    for (name, M, K, N, r, *_rest) in synth.mot_shapes():
+        x = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
+        wv = None
+        if r:
+            wv = (torch.randn(N, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+            wv = wv.view(torch.int16).contiguous()
+        layers[name] = {
+            "M": M, "K": K, "N": N, "r": r, "x": x, "wv": wv,
+            "codes": torch.randint(0, 256, (N, K // 2), generator=gen, device=dev,
+                                   dtype=torch.uint8),
+            "scales": torch.randint(0x30, 0x40, (N, K // 16), generator=gen, device=dev,
+                                    dtype=torch.uint8),
+            "bias": torch.randn(N, generator=gen, device=dev) * 0.1,
+            "prep": prep_pack(K, r),
+            "y": torch.empty(M, N, dtype=torch.bfloat16, device=dev)}
+    # workspaces (no dependence on N), one set per (M, K, r), reused by every
+    # call in stream order
+    wspool = {}
+
+    def workspaces(M, K, r, n):
+        key = (M, K, r)
+        if key not in wspool:
+            nb = B.asp_workspace_bytes(M, 1, K, r)
+            wspool[key] = [torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+                           for _ in range(3)]
+        return wspool[key][:n]
+
+    calls = {"video": [], "action": []}
+    for expert in calls:
+        for blk in range(synth.MOT_BLOCKS):
+            for grp in MOT_GROUPS:
+                calls[expert].append([layers[f"{expert}.{blk}.{p}"] for p in grp])
+    flops = {e: sum(layer_flops(L["M"], L["N"], L["K"], L["r"]) for c in cs for L in c)
+             for e, cs in calls.items()}
+
+    def run(c):
+        L0 = c[0]
+        ws = workspaces(L0["M"], L0["K"], L0["r"], len(c))
+        B.asp_forward_group_stages(
+            7, [L["x"] for L in c], B.DTYPES["bf16"], L0["M"], L0["K"], L0["r"],
+            [L["prep"] for L in c], [L["codes"] for L in c], [L["scales"] for L in c],
+            [L["wv"] for L in c] if L0["r"] else None, [L["bias"] for L in c],
+            [L["N"] for L in c], [L["y"] for L in c], B.DTYPES["bf16"], ws,
+            [w.numel() for w in ws])
+
+    def step(experts):
+        for e in experts:
+            for c in calls[e]:
+                run(c)
+
+    step(("video", "action"))  # warm-up (code objects, launch paths)
+    torch.cuda.synchronize()
+    graphs = {}
+    for key, experts in (("both", ("video", "action")), ("video", ("video",)),
+                         ("action", ("action",))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(experts)
+        graphs[key] = g
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(g, n):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    graphs["both"].replay()
+    ms = timed(graphs["both"], args.mot_steps)
+    ms_video = timed(graphs["video"], 3)
+    ms_action = timed(graphs["action"], 3)
+    total = flops["video"] + flops["action"]
+    tf_video = flops["video"] / (ms_video * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        sample = [synth.make_layer("action.attn", 256, 1024, 1024, 32),
+                  synth.make_layer("video.attn (64 rows)", 64, 3072, 3072, 0,
+                                   outlier_frac=0.005, outlier_gain=30.0)]
+        cpu = cpu_baseline(sample, args.cpu_seconds)
+        cpu["sample"] = ("the oracle's rate on one action attention layer and 64 rows of a video "
+                         "attention layer (TFLOP/s, the same unit as value): " + cpu["sample"])
+    out = {
+        "metric": "deflated-ASP NVFP4 linear effective TFLOP/s, 600-layer two-expert set, 1 MI355X",
+        "value": round(total / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.mot_steps, "warmup": 1, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (random device-resident inputs and packed weights)",
+        "config": {
+            "workload": "600-layer two-expert set: 30 blocks x {self_attn q/k/v/o, cross_attn "
+                        "q/k/v/o, ffn.0, ffn.2} per expert; video d 3072, ffn 14336, M 4096, "
+                        "r 0; action d 1024, ffn 4096, M 256, r 32; one step = all 600 linears",
+            "calls_per_step": sum(len(v) for v in calls.values()),
+            "flops_per_step": total,
+            "video_ms": round(ms_video, 4), "action_ms": round(ms_action, 4),
+            "video_TFLOPs": round(tf_video, 1),
+            "action_TFLOPs": round(flops["action"] / (ms_action * 1e-3) / 1e12, 2),
+            "timing": "one HIP graph per denoising step, replayed; events on the capture stream",
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tf_video, 1), "peak": F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_video / F16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "all launches of the video expert's 300 layers (aggregate, not one "
+                               "kernel): prep and the 4-bit GEMM"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
