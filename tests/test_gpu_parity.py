@@ -443,6 +443,41 @@ def test_forward_group(M, K, r, Ns, dtype):
             assert rel_fro(a, alone) <= 1e-5       # only the float32 summation order differs
 
 
+@pytest.mark.parametrize("M,K,r,Ns", [(256, 1024, 32, (1024, 1024, 1024)),   # q, k, v of a block
+                                      (300, 512, 0, (128, 96)),             # rank 0, ragged M
+                                      (4096, 256, 32, (1536, 1536))])       # 256 x 192 tiles
+def test_forward_group_distinct_inputs(M, K, r, Ns):
+    """A grouped call whose layers read different inputs (the per-layer x
+    pointers of the group): each layer against the float64 oracle on its own
+    input, and bit for bit against a lone call of the same layer when the
+    kernel choice is the same."""
+    lays = [synth.make_layer(f"d{i}", M, K, N, r, seed=1000 + M + i, dtype="bf16")
+            for i, N in enumerate(Ns)]
+    packed = [PackedLayer.pack(l.w, l.s, l.v, l.b, DEV) for l in lays]
+    xs = [x_device(l) for l in lays]
+    ys = [torch.empty((M, l.N), dtype=torch.float32, device=DEV) for l in lays]
+    wss = [p.workspace(M) for p in packed]
+    B.asp_forward_group(xs, B.ASP_BF16, M, K, r, [p.prep for p in packed],
+                        [p.w_codes for p in packed], [p.w_scales for p in packed],
+                        [p.wv for p in packed] if r else None, [p.bias for p in packed],
+                        [p.N for p in packed], ys, B.DTYPES["f32"], wss,
+                        [w.numel() for w in wss])
+    same_kernel = B.asp_gemm_kernel_name(M, sum(Ns), K) == B.asp_gemm_kernel_name(M, Ns[0], K)
+    rows = None if M <= 512 else np.sort(np.random.default_rng(M).choice(M, 48, replace=False))
+    for lay, p, x, y in zip(lays, packed, xs, ys):
+        got = host(y)
+        xo = lay.x if rows is None else lay.x[rows]
+        want = OA.forward(xo, lay.w, lay.b, lay.s, lay.v)
+        e = rel_fro(got if rows is None else got[rows], want)
+        print(f"group with distinct inputs {Ns} {lay.name}: rel err {e:.3e}")
+        assert e <= 2e-3
+        alone = host(p.forward(x, "f32"))
+        if same_kernel:
+            assert np.array_equal(got, alone)
+        else:
+            assert rel_fro(got, alone) <= 1e-5
+
+
 # ------------------------------------------------------- shared-weight arm
 
 
