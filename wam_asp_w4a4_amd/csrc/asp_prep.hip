@@ -321,13 +321,7 @@ struct QUnit {
   XFrag<XT> x;
   f32x4_t pa[MS][KK][2];
 
-  // row mc (already clamped to M - 1) of this lane, the block at column col0
-  __device__ __forceinline__ void issue(const XT* __restrict__ xp, int M, int K, int col0,
-                                        const float* __restrict__ u_part, int S, int64_t mc,
-                                        int q) {
-    x.load(xp + mc * K, col0, q);
-    issue_u(M, u_part, S, mc, q);
-  }
+  // the partial sums of u for row mc (already clamped to M - 1) of this lane
   __device__ __forceinline__ void issue_u(int M, const float* __restrict__ u_part, int S,
                                           int64_t mc, int q) {
     if constexpr (KS > 0) {
