@@ -137,6 +137,8 @@ LAYER_CASES = [  # name, M, K, N, r, x dtype
     ("action-attn", 256, 1024, 1024, 32, "bf16"),
     ("ragged", 77, 384, 200, 16, "bf16"),
     ("video-attn rows", 512, 3072, 3072, 32, "bf16"),
+    # long rows: 256 groups, a 16384 x 16384 Gram for the basis
+    ("long K", 5, 16384, 64, 16, "bf16"),
 ]
 
 
