@@ -196,6 +196,34 @@ def test_full_size_action_metric():
     check_against_oracle(g, v, ev, res, 32)
 
 
+def test_large_metric_known_spectrum():
+    """K = 16384, p = 64, r = 32: a metric built from four Householder
+    reflections, so its spectrum and leading eigenvectors are known without an
+    eigh at this size.  Against the exact float64 eigenpairs the float32
+    rounding of G (||dG||_2 <= ||dG||_F <= 2^-24 ||G||_F) moves each
+    eigenvalue by at most that much (Weyl) and the r-dimensional subspace by
+    at most that over the gap lam_r - lam_{r+1} (Davis-Kahan); the gates add
+    those bounds to the ones above.  Orthonormality, signs and residuals as
+    for every case."""
+    print("eigenspace K=16384 p=64 r=32 (reflected metric)", flush=True)
+    K, p, r = 16384, 64, 32
+    rng = np.random.default_rng(23)
+    g, lam, q = synth.draw_metric_reflected(rng, K, r)
+    v0 = synth.draw_start(rng, K, p)
+    v, ev, res = run(g, v0, r, 8)
+    check_common(g, v, ev, res, lam[0])
+    dg = 2.0 ** -24 * float(np.linalg.norm(g.astype(np.float64)))
+    assert np.all(np.abs(ev - lam[:r]) <= 2.0 ** -23 * lam[:r] + dg + 1e-9 * lam[0]), ev[:4]
+    # the largest sine of the principal angles, as the 2-norm of the part of v
+    # outside span(q) (linear in the error; sqrt(1 - s_min^2) would turn the
+    # float32 rounding of v's orthonormality, about 1e-8, into 1e-4)
+    dist = float(np.linalg.norm(v - q @ (q.T @ v), 2))
+    bound = dg / (lam[r - 1] - lam[r]) + 1e-6
+    print(f"  subspace distance {dist:.2e} (bound {bound:.2e}), "
+          f"max eigenvalue error {np.abs(ev - lam[:r]).max():.2e} (dG {dg:.2e})")
+    assert dist <= bound
+
+
 @pytest.mark.parametrize("K,p", [(4096, 64), (1024, 48), (384, 16)])
 def test_metric_product_partials(K, p):
     """The MFMA product alone: the slices' partial sums add up to G V (float64

@@ -154,6 +154,34 @@ def draw_metric(rng, K, decay=8.0, floor=1e-6, rank=None):
     return g.astype(np.float32), lam, q
 
 
+def draw_metric_reflected(rng, K, r, n_reflections=4, decay=8.0, floor=1e-6):
+    """A large synthetic metric with a known spectrum and known leading
+    eigenvectors, without a dense K x K orthogonal draw: Q = H_1 ... H_n, a
+    product of Householder reflections H = I - 2 u u^T (u random, unit), and
+    G = Q diag(lam) Q^T with lam_i = exp(-i / decay) + floor, built in float64
+    by applying the reflections to diag(lam) (O(n K^2)), made exactly
+    symmetric and rounded to float32.  Returns (G float32, lam float64
+    descending, the first r columns of Q float64)."""
+    lam = np.exp(-np.arange(K, dtype=np.float64) / decay) + floor
+    us = []
+    for _ in range(n_reflections):
+        u = rng.standard_normal(K)
+        us.append(u / np.linalg.norm(u))
+    g = np.diag(lam)
+    # G = H_1 (H_2 (... diag(lam) ...) H_2) H_1: innermost reflection first
+    for u in reversed(us):
+        gu = g @ u
+        ugu = u @ gu
+        g -= 2.0 * np.outer(u, gu)
+        g -= 2.0 * np.outer(gu, u)
+        g += 4.0 * ugu * np.outer(u, u)
+    g = 0.5 * (g + g.T)
+    q = np.eye(K, r)
+    for u in reversed(us):
+        q -= 2.0 * np.outer(u, u @ q)
+    return g.astype(np.float32), lam, q
+
+
 def draw_start(rng, K, p):
     """K x p float32 N(0, 1) starting block for a subspace iteration."""
     return rng.standard_normal((K, p)).astype(np.float32)
