@@ -478,6 +478,45 @@ def test_forward_group_distinct_inputs(M, K, r, Ns):
             assert rel_fro(got, alone) <= 1e-5
 
 
+def test_forward_graph_replays_match_eager():
+    """The grouped forward captured in a HIP graph, as the benchmarks run it,
+    and replayed three times with eager calls on another input through the
+    same workspaces, and synchronisations, between the replays: every replay
+    gives the eager result bit for bit (no state survives in the workspace)."""
+    lays = synth.workload(1)
+    M, K, r = lays[0].M, lays[0].K, lays[0].r
+    packed = [PackedLayer.pack(l.w, l.s, l.v, l.b, DEV) for l in lays]
+    x = x_device(lays[0])
+    x2 = (x.float() * 0.5 + 1.0).to(torch.bfloat16)
+    wss = [p.workspace(M) for p in packed]
+
+    def call(xx, out):
+        B.asp_forward_group([xx] * len(packed), B.ASP_BF16, M, K, r, [p.prep for p in packed],
+                            [p.w_codes for p in packed], [p.w_scales for p in packed],
+                            [p.wv for p in packed], [p.bias for p in packed],
+                            [p.N for p in packed], out, B.DTYPES["bf16"], wss,
+                            [w.numel() for w in wss])
+
+    ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=DEV) for p in packed]
+    ys2 = [torch.empty_like(y) for y in ys]
+    call(x, ys)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(x, ys)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for y in ys:
+            y.zero_()
+        call(x2, ys2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(ys, eager))
+    assert not torch.equal(ys2[0], eager[0])
+
+
 # ------------------------------------------------------- shared-weight arm
 
 
