@@ -179,3 +179,33 @@ def test_forward_empty_and_deterministic():
     assert np.array_equal(a, b)
     y0 = d.forward(x[:0])
     assert y0.shape == (0, 128)
+
+
+def test_forward_graph_replays_match_eager():
+    """The layer captured in a HIP graph, as the benchmark runs it, replayed
+    three times with an eager call on another input through the same workspace
+    between the replays: every replay equals the eager result bit for bit."""
+    print("svdq forward graph replays", flush=True)
+    lay = synth.make_svdq_layer("g", 256, 1024, 1024, 32, seed=31)
+    v = SvdqLayer.right_basis(lay.w, lay.s, 32)
+    d = SvdqLayer.pack_host(lay.w, lay.s, 32, v, lay.b).to(DEV)
+    x = x_dev(lay.x, "bf16")
+    x2 = (x.float() * 0.5 + 1.0).to(torch.bfloat16)
+    ws = torch.empty(B.asp_svdq_workspace_bytes(256, 1024, 1024, 32), dtype=torch.uint8, device=DEV)
+    y = torch.empty((256, 1024), dtype=torch.bfloat16, device=DEV)
+    y2 = torch.empty_like(y)
+    d.forward(x, "bf16", workspace=ws, y=y)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.forward(x, "bf16", workspace=ws, y=y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.zero_()
+        d.forward(x2, "bf16", workspace=ws, y=y2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
+    assert not torch.equal(y2, eager)
