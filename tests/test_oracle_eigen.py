@@ -127,3 +127,20 @@ def test_argument_checks():
         E.top_eigenspace(np.eye(3), 0)
     with pytest.raises(ValueError):
         E.top_eigenspace(np.eye(3), 4)
+
+
+def test_reflected_metric_has_its_stated_eigenpairs():
+    """The large-K test metric (Householder reflections applied to a known
+    spectrum): the returned columns are orthonormal, exact symmetric
+    eigenvectors of the float32 metric up to its rounding, and the oracle's
+    eigensolver finds the same leading eigenvalues at a size it can afford."""
+    rng = np.random.default_rng(5)
+    g, lam, q = synth.draw_metric_reflected(rng, 384, 12)
+    assert np.array_equal(g, g.T)
+    assert np.abs(q.T @ q - np.eye(12)).max() <= 1e-14
+    g64 = g.astype(np.float64)
+    fro = np.linalg.norm(g64)
+    assert np.abs(g64 @ q - q * lam[:12]).max() <= 2.0 ** -24 * fro * 4
+    w, v = E.top_eigenspace(g, 12)
+    assert np.abs(w - lam[:12]).max() <= 2.0 ** -24 * fro * 4
+    assert E.subspace_distance(v, q) <= 1e-6
