@@ -139,13 +139,16 @@ LAYER_CASES = [  # name, M, K, N, r, x dtype
     ("video-attn rows", 512, 3072, 3072, 32, "bf16"),
     # long rows: 256 groups, a 16384 x 16384 Gram for the basis
     ("long K", 5, 16384, 64, 16, "bf16"),
+    # the largest rank (the basis block of the eigensolve equals it)
+    ("rank 64", 96, 512, 256, 64, "bf16"),
 ]
 
 
 @pytest.mark.parametrize("name,M,K,N,r,dtype", LAYER_CASES)
 def test_forward_matches_oracle(name, M, K, N, r, dtype):
     print(f"svdq forward {name} M={M} K={K} N={N} r={r}", flush=True)
-    lay = synth.make_svdq_layer(name, M, K, N, r, seed=M + K + N, dtype=dtype)
+    # the planted low-rank part covers the rank, so the top-r subspace has a gap
+    lay = synth.make_svdq_layer(name, M, K, N, r, seed=M + K + N, dtype=dtype, planted=max(32, r))
     v = SvdqLayer.right_basis(lay.w, lay.s, r)
     h = SvdqLayer.pack_host(lay.w, lay.s, r, v, lay.b)
     pk = SQ.pack_weight(lay.w, lay.s, r)
