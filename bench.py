@@ -71,14 +71,14 @@ def layer_bytes(M, N, K, r, xb, yb):
 
 
 def prep_u_bytes(M, K, r, xb):
-    """Algorithmic bytes of the u stage: x and diag(1/s) H V (two bf16 planes) in, u out."""
-    return M * K * xb + 4 * K * r + 4 * M * r
+    """Algorithmic bytes of the u stage: x and diag(1/s) H V (three bf16 terms) in, u out."""
+    return M * K * xb + 6 * K * r + 4 * M * r
 
 
 def prep_q_bytes(M, K, r, xb):
-    """Algorithmic bytes of the quantise stage: x, 1/s, V (two bf16 planes) and u in;
-    codes, scales and u out."""
-    return M * K * xb + 4 * K + 4 * K * r + 4 * M * r + M * K // 2 + M * K // 16 + 4 * M * r
+    """Algorithmic bytes of the quantise stage: x, 1/(s sqrt 128) (float64), V (three bf16
+    terms) and u in; codes, scales and u out."""
+    return M * K * xb + 8 * K + 6 * K * r + 4 * M * r + M * K // 2 + M * K // 16 + 4 * M * r
 
 
 def gemm_bytes(M, N, K, r, yb):

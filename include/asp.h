@@ -149,9 +149,10 @@ int32_t asp_prep_pack_bytes(int64_t K, int32_t r, size_t* bytes);
  * smoothing vector and the basis that define the layer's transforms (model
  * card, "What ASP is, and what the deflated form means": x_tilde = (x/s) H,
  * u = x_tilde V).  The buffer holds, in float64-derived form:
- *   1 / (s sqrt(128)) per channel (float32);
- *   V'' = diag(1/s) H V, so that u = x V'' (bf16 high and low parts);
- *   V itself, for the deflation (bf16 high and low parts).
+ *   1 / (s sqrt(128)) per channel (float64);
+ *   V'' = diag(1/s) H V, so that u = x V'' (three bf16 terms, each the
+ *   rounding of what the earlier ones leave: 24 or more significant bits);
+ *   V itself, for the deflation (three bf16 terms: a float32 V exactly).
  * Its layout is private to the library; upload it unchanged.
  *   s          host, K float32, all > 0
  *   v          host, K x r float32 (NULL iff r == 0)

@@ -6,14 +6,24 @@ Gates (derived in the design notes):
 * dequantiser: exact;
 * GEMM on the oracle's own codes: relative Frobenius error <= 1e-5 (fp32
   output; only accumulation order differs);
-* whole layer: relative Frobenius error on y <= 2e-3 against the float64
-  oracle, for fp32 and bf16 output.  The float32 pre-quantisation arithmetic
-  of the device (x/s, Hadamard, u, deflation) differs from the oracle's
-  float64 by a few float32 ulps, which moves a value across an E2M1 or E4M3
-  rounding boundary on a small fraction of elements (reported, <= 0.1 %);
-* whole layer, tight: the fp32 output equals, to 1e-5, the oracle's
-  contraction of the device's own activation codes and u -- so everything
-  but those rare boundary decisions is checked at accumulation precision.
+* activation prep: u and the pre-quantisation values within 2e-6 of the
+  float64 oracle (relative to max|u| and max|x_tilde|): the device computes
+  them in float32 arithmetic (three-term bf16 products on MFMA), so they
+  differ from the oracle by a few float32 ulps;
+* boundary decisions: every activation code, block scale and bf16(u) value
+  of the device that differs from the oracle's is certified as a boundary
+  case -- the oracle's exact value lies within 16 float32 ulps (of its row's
+  scale) of the rounding boundary between the two results;
+* whole layer: relative Frobenius error on y <= 1e-4 (fp32 output) and
+  <= 2e-3 (bf16 output, whose own RNE cast costs ~1.7e-3) against the
+  float64 oracle on the workloads and the sampled layers of the 600-layer
+  set; elsewhere 1e-4 plus the oracle-computed cost of the certified
+  boundary decisions (one flipped code can cost 1e-4 in a narrow layer);
+* whole layer, tight: the fp32 output equals the oracle's contraction of
+  the device's own activation codes and u to 1e-5 in relative Frobenius
+  norm, every row to 1e-5 of its largest output, and every element within
+  the worst-case float32 summation bound -- so everything but those rare
+  boundary decisions is checked at accumulation precision.
 """
 
 import dataclasses
@@ -55,6 +65,38 @@ def x_device(lay):
 
 def rel_fro(a, b):
     return float(np.linalg.norm(np.asarray(a, np.float64) - b) / np.linalg.norm(b))
+
+
+Y32_GATE = 1e-4   # fp32 output against the float64 oracle
+Y16_GATE = 2e-3   # bf16 output (spec tolerance; the cast alone costs ~1.7e-3)
+
+
+def row_rel_max(a, b):
+    """Largest per-row ratio max_n |a - b| / max_n |b| (rows of b that are all
+    zero count by their absolute error)."""
+    d = np.abs(np.asarray(a, np.float64) - b).max(axis=1)
+    s = np.abs(b).max(axis=1)
+    return float(np.max(np.where(s > 0, d / np.where(s > 0, s, 1.0), d)))
+
+
+def elementwise_bound(xc, xs, u, wc, ws, wv, bias, K, r):
+    """Worst-case float32 summation error of every output of the 4-bit GEMM.
+
+    The device sums n = K/16 exact block products (each one MFMA K-step of 16
+    exact fp16 products), ceil(r/16) low-rank K-steps and the bias in float32;
+    any recursive float32 sum of n terms is within (n - 1) 2^-24 sum|terms|
+    of the exact sum, and sum|terms| <= (|A||B|^T + |u||wv|^T + |b|).  The
+    element-wise gate allows n + 16 (the MFMA's internal order of its 16
+    products is not fixed)."""
+    A = np.abs(OF.dequantize_nvfp4(xc, xs))
+    Bm = np.abs(OF.dequantize_nvfp4(wc, ws))
+    tot = A @ Bm.T
+    if r:
+        tot += np.abs(OA.round_bf16(u)) @ np.abs(np.asarray(wv, np.float64)).T
+    if bias is not None:
+        tot += np.abs(np.asarray(bias, np.float64))[None, :]
+    n = K // 16 + (r + 15) // 16 + 2 + 16
+    return n * 2.0 ** -24 * tot
 
 
 # ------------------------------------------------------------------ quantiser
@@ -156,13 +198,99 @@ def test_act_prep_against_oracle(lay):
     xt_scale = np.abs(act["x_tilde"]).max()
     e_pre = np.abs(pre - act["x_deflated"]).max() / xt_scale
     e_u = np.abs(u - act["u"]).max() / np.abs(act["u"]).max() if lay.r else 0.0
-    print(f"prep {lay.name}: max |pre - oracle| / max|x_tilde| {e_pre:.2e}, u rel {e_u:.2e}")
-    assert e_pre <= 4e-6
-    assert e_u <= 4e-5
-    # 3. end-to-end code agreement (reported convention: fraction of codes off)
-    mism = OF.unpack_codes(xc) != OF.unpack_codes(act["x_codes"])
-    assert mism.mean() <= 1e-3, mism.mean()
-    assert np.mean(xs != act["x_scales"]) <= 1e-3
+    # 3. every code, scale and bf16(u) that differs from the oracle's is a
+    # boundary decision (the oracle's exact value within a few ulps of it)
+    nc, ns, nu = certify_differences(act, xc, xs, u)
+    print(f"prep {lay.name}: max |pre - oracle| / max|x_tilde| {e_pre:.2e}, u rel {e_u:.2e}, "
+          f"boundary decisions that differ: {nc} codes of {xc.size * 2}, {ns} scales, {nu} bf16(u)")
+    assert e_pre <= 2e-6
+    assert e_u <= 2e-6
+
+
+def _edge_prep_layers():
+    """Activation-prep edge cases (float32 x, so any value can be placed).
+
+    * zero rows: x_tilde, u and the deflated row are exactly 0, so the codes
+      and scales are exactly 0 on both sides;
+    * saturating blocks (s = 1, channels of 1e5): amax / 6 far above 448, so
+      the scale saturates at 448 (0x7E) and every large element at code 7;
+    * V of unit columns (in the rotated coordinates): the deflation cancels
+      those channels of x_tilde, which the oracle makes exactly 0 and the
+      device to within its float32 rounding;
+    * blocks on the E2M1 midpoints: rows whose x_tilde, before the float32
+      rounding of x, is a block scale times grid midpoints (0.25 ... 5) and a
+      6 that fixes the scale -- every element sits within an ulp or two of a
+      rounding boundary, so the fused quantiser's tie handling decides each."""
+    from oracle import hadamard as OH
+    K, r = 512, 32
+    base = synth.make_layer("edge-prep", 96, K, 16, r, seed=31, dtype="f32")
+    x = base.x.copy()
+    x[[0, 5, 63, 64, 95]] = 0.0                      # zero rows (one at each tile edge)
+    zero = dataclasses.replace(base, name="zero-rows", x=x)
+    xs = base.x.copy()
+    xs[10:20, ::37] = 1.0e5                          # saturating blocks
+    xs[20:22, 3] = -3.0e5
+    sat = dataclasses.replace(base, name="saturating", x=xs, s=np.ones(K, np.float32))
+    rng = np.random.default_rng(5)
+    cols = np.sort(rng.choice(K, r, replace=False))
+    vu = np.zeros((K, r), np.float32)
+    vu[cols, np.arange(r)] = 1.0
+    unit = dataclasses.replace(base, name="unit-V", v=vu)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    xt = np.zeros((48, K))
+    for m in range(48):
+        for b in range(K // 16):
+            sd = 2.0 ** rng.integers(-3, 4) * (1 + rng.integers(0, 8) / 8)
+            blk = rng.choice(mids, 16) * rng.choice([-1.0, 1.0], 16)
+            blk[rng.integers(0, 16)] = 6.0
+            xt[m, 16 * b:16 * b + 16] = blk * sd
+    xm = OH.block_rotate(xt, 128).astype(np.float32)  # x = x_tilde H (H is an involution), s = 1
+    mid = dataclasses.replace(base, name="midpoints", M=48, x=xm, s=np.ones(K, np.float32),
+                              v=None, r=0)
+    mid_r = dataclasses.replace(mid, name="midpoints-unit-V", v=vu, r=r)
+    return [zero, sat, unit, mid, mid_r]
+
+
+@pytest.mark.parametrize("lay", _edge_prep_layers(), ids=lambda l: l.name)
+def test_act_prep_edge_cases(lay):
+    """asp_act_prep on edge-case activations: codes and scales bit-exact
+    against the oracle quantiser on the kernel's own pre-quantisation values,
+    the pre-quantisation values and u within 2e-6 of the float64 oracle, and
+    the case-specific expectations."""
+    xc, xs, u, pre = gpu_act_prep(lay)
+    oc, os_ = OF.quantize_nvfp4(pre)
+    assert np.array_equal(xs, os_) and np.array_equal(xc, oc)
+    act = OA.activation_side(lay.x, lay.s, lay.v)
+    scale = max(np.abs(act["x_tilde"]).max(), 1e-30)
+    e_pre = np.abs(pre - act["x_deflated"]).max() / scale
+    e_u = (np.abs(u - act["u"]).max() / max(np.abs(act["u"]).max(), 1e-30)) if lay.r else 0.0
+    gc, ocd = OF.unpack_codes(xc), OF.unpack_codes(act["x_codes"])
+    # a code that differs only in the sign of a zero decodes to the same value
+    off = (gc != ocd) & ~(((gc | ocd) & 7) == 0)
+    print(f"edge {lay.name}: pre {e_pre:.2e}, u {e_u:.2e}, codes off (values) {off.mean():.2e}, "
+          f"scales off {np.mean(xs != act['x_scales']):.2e}")
+    assert e_pre <= 2e-6 and e_u <= 2e-6
+    if lay.name == "zero-rows":
+        z = np.all(lay.x == 0, axis=1)
+        assert np.all((xc[z] & 0x77) == 0) and np.all(xs[z] == 0) and np.all(u[z] == 0)
+        assert np.all(pre[z] == 0)
+    if lay.name == "saturating":
+        hot = np.abs(act["x_deflated"]).reshape(lay.M, -1, 16).max(axis=2) / 6 > 2 * 448
+        assert hot.sum() > 0 and np.all(xs[hot] == 0x7E) and np.all(os_[hot] == 0x7E)
+        assert np.array_equal(xs[hot], act["x_scales"][hot])
+    if "unit-V" in lay.name:
+        cols = np.nonzero(lay.v.any(axis=1))[0]
+        assert np.abs(pre[:, cols]).max() <= 2e-6 * scale
+        assert np.all(act["x_deflated"][:, cols] == 0)
+        assert np.all((gc[:, cols] & 7) == 0)        # the cancelled channels quantise to zero
+    if lay.name.startswith("midpoints"):
+        # the kernel's own float32 values land exactly on midpoints often, so
+        # the in-prep quantiser's ties to the even code are exercised
+        scl = np.repeat(OF.E4M3_VALUES[xs], 16, axis=1)
+        q = np.abs(pre.astype(np.float64)) / np.where(scl > 0, scl, 1.0)
+        ties = int(np.isin(q, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]).sum())
+        print(f"edge {lay.name}: {ties} exact E2M1 ties in the kernel's own values")
+        assert ties > 0
 
 
 @pytest.mark.parametrize("M,K,r,dtype", [(4096, 2048, 32, "bf16"), (2000, 4096, 32, "bf16"),
@@ -237,13 +365,26 @@ def gemm_cases():
             # the tile kernels' low-rank rows through LDS (r <= 32, r % 8 == 0):
             # 64 x 64 tiles with r = 16; 256 x 192 tiles, ragged N, r = 24
             synth.make_layer("tile64-r16", 1024, 256, 1024, 16, seed=14, dtype="bf16"),
-            synth.make_layer("tile256-r24", 4096, 256, 2000, 24, seed=15, dtype="bf16")]
+            synth.make_layer("tile256-r24", 4096, 256, 2000, 24, seed=15, dtype="bf16"),
+            # 256 x 192 tiles whose last stage is half of one (K % 256 == 128)
+            synth.make_layer("tile256-k384", 4096, 384, 2000, 32, seed=19, dtype="bf16")]
 
 
 @pytest.mark.parametrize("lay", gemm_cases(), ids=lambda l: f"{l.name}-M{l.M}-N{l.N}-K{l.K}-r{l.r}")
 def test_gemm_on_oracle_codes(lay):
     got, want = gemm_on_oracle_codes(lay, "f32")
+    name = B.asp_gemm_kernel_name(lay.M, lay.N, lay.K)
+    pk = OA.pack_weight(lay.w, lay.s, lay.v)
+    act = OA.activation_side(lay.x, lay.s, lay.v)
+    u32 = act["u"].astype(np.float32).astype(np.float64)
+    bound = elementwise_bound(act["x_codes"], act["x_scales"], u32, pk["w_codes"], pk["w_scales"],
+                              pk["wv"], lay.b, lay.K, lay.r)
+    over = int((np.abs(got - want) > bound).sum())
+    print(f"gemm {name} {lay.name}: rel {rel_fro(got, want):.2e}, worst row "
+          f"{row_rel_max(got, want):.2e}, beyond the summation bound: {over}")
     assert rel_fro(got, want) <= 1e-5
+    assert row_rel_max(got, want) <= 1e-5
+    assert over == 0
     got16, _ = gemm_on_oracle_codes(lay, "bf16")
     # the bf16 output is the RNE cast of an fp32 result: within one bf16 step of it
     assert np.all(np.abs(got16 - got) <= np.abs(got) * 2.0 ** -8 + 1e-30)
@@ -283,31 +424,113 @@ def forward_gpu(lay, y_dtype="f32", rows=None):
     return host(y.float()), p
 
 
+E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+CERT_ULPS = 16  # float32 ulps (of the row's largest x_tilde or u) a boundary case may lie within
+
+
+def certify_differences(act, xc, xs, u):
+    """Every activation code, block scale and bf16(u) value of the device
+    that differs from the oracle's must be a boundary decision: the oracle's
+    exact value lies within CERT_ULPS float32 ulps (of its row's largest
+    |x_tilde|, resp. |u|) of the rounding boundary between the two results.
+    The device's pre-quantisation values are within ~1e-7 of that scale, so
+    only such values can be decided differently.  Returns the counts
+    (codes, scales, u) that differ; raises if any is not a boundary case."""
+    xd = act["x_deflated"]
+    M, K = xd.shape
+    tol = CERT_ULPS * 2.0 ** -24 * np.abs(act["x_tilde"]).max(axis=1, keepdims=True)
+    e4 = OF.E4M3_VALUES[:0x7F]
+    e4_mid = (e4[:-1] + e4[1:]) / 2.0
+    # block scales: amax / 6 against the E4M3 rounding boundaries
+    amax = np.abs(act["x_prequant"].astype(np.float64)).reshape(M, -1, 16).max(axis=2)
+    sdiff = xs != act["x_scales"]
+    if sdiff.any():
+        d = np.abs(amax[sdiff][:, None] - 6.0 * e4_mid[None, :]).min(axis=1)
+        bad = d > np.broadcast_to(tol, amax.shape)[sdiff] + 6.0 * 2.0 ** -24 * amax[sdiff]
+        assert not bad.any(), f"{int(bad.sum())} block scales differ away from a boundary"
+    # element codes, in blocks whose scale agrees; a difference in the sign of
+    # a zero decodes to the same value and is not counted
+    gc, oc = OF.unpack_codes(xc), OF.unpack_codes(act["x_codes"])
+    same_scale = np.repeat(~sdiff, 16, axis=1)
+    cdiff = (gc != oc) & ~(((gc | oc) & 7) == 0) & same_scale
+    if cdiff.any():
+        sd = np.repeat(OF.E4M3_VALUES[act["x_scales"]], 16, axis=1)[cdiff]
+        v = np.abs(xd[cdiff])
+        d = np.abs(v[:, None] - E2M1_MIDPOINTS[None, :] * sd[:, None]).min(axis=1)
+        bad = d > np.broadcast_to(tol, xd.shape)[cdiff]
+        assert not bad.any(), f"{int(bad.sum())} codes differ away from an E2M1 boundary"
+    nu = 0
+    if u is not None and act["u"].shape[1]:
+        ub_dev, ub_or = OA.round_bf16(u.astype(np.float64)), OA.round_bf16(act["u"])
+        udiff = ub_dev != ub_or
+        nu = int(udiff.sum())
+        if nu:
+            tol_u = CERT_ULPS * 2.0 ** -24 * np.abs(act["u"]).max(axis=1, keepdims=True)
+            mid = (ub_dev + ub_or) / 2.0           # the bf16 rounding boundary between them
+            d = np.abs(act["u"] - mid)[udiff]
+            bad = d > np.broadcast_to(tol_u, udiff.shape)[udiff]
+            assert not bad.any(), f"{int(bad.sum())} bf16(u) values differ away from a boundary"
+    return int(cdiff.sum()), int(sdiff.sum()), nu
+
+
+def tight_checks(y32, xc, xs, u, pk, bias, K, r):
+    """The device output against the oracle's contraction of the device's own
+    activation codes and u: relative Frobenius norm, per-row maximum and the
+    element-wise float32 summation bound.  Returns (norm, row) errors."""
+    u64 = u.astype(np.float64) if r else np.zeros((len(y32), 0))
+    mine = OA.output_from_codes(xc, xs, u64, pk["w_codes"], pk["w_scales"], pk["wv"], bias)
+    tight, row = rel_fro(y32, mine), row_rel_max(y32, mine)
+    bound = elementwise_bound(xc, xs, u64, pk["w_codes"], pk["w_scales"], pk["wv"], bias, K, r)
+    over = np.abs(y32.astype(np.float64) - mine) > bound
+    assert tight <= 1e-5, tight
+    assert row <= 1e-5, row
+    assert not over.any(), f"{int(over.sum())} outputs beyond the float32 summation bound"
+    return tight, row
+
+
+def oracle_gates(lay, y32, y16=None, rows=None, label="", strict=True):
+    """One layer's device output (fp32, optionally bf16) against the float64
+    oracle: the tight checks on the device's own codes and u, the
+    certification of every decision that differs, and the output gates.
+    strict: the fp32 output within Y32_GATE of the oracle outright.  Otherwise
+    the gate is Y32_GATE plus the exact cost (computed by the oracle) of the
+    certified boundary decisions the device took the other way -- a layer
+    whose few hundred outputs per row rest on one flipped code can exceed
+    1e-4 on that alone."""
+    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
+    xs_ = lay.x if rows is None else lay.x[rows]
+    want = OA.forward(xs_, lay.w, lay.b, lay.s, lay.v)
+    y32 = sel(y32)
+    e32, r32 = rel_fro(y32, want), row_rel_max(y32, want)
+    xc, xs, u, _ = gpu_act_prep(lay)
+    xc, xs, u = sel(xc), sel(xs), None if u is None else sel(u)
+    pk = OA.pack_weight(lay.w, lay.s, lay.v)
+    tight, row = tight_checks(y32, xc, xs, u, pk, lay.b, lay.K, lay.r)
+    act = OA.activation_side(xs_, lay.s, lay.v)
+    nc, ns, nu = certify_differences(act, xc, xs, u)
+    u64 = u.astype(np.float64) if u is not None else np.zeros((len(want), 0))
+    flip_cost = rel_fro(OA.output_from_codes(xc, xs, u64, pk["w_codes"], pk["w_scales"], pk["wv"],
+                                             lay.b), want)
+    msg = f"{label} {lay.name}: rel err fp32 {e32:.3e} (worst row {r32:.2e})"
+    if y16 is not None:
+        e16 = rel_fro(sel(y16), want)
+        msg += f" bf16 {e16:.3e}"
+    print(msg + f" | vs own codes {tight:.2e} (worst row {row:.2e}) | boundary decisions that "
+          f"differ: {nc} codes ({nc / max(xc.size * 2, 1):.1e}), {ns} scales, {nu} bf16(u); "
+          f"their cost {flip_cost:.1e}")
+    assert e32 <= Y32_GATE + (0.0 if strict else flip_cost)
+    if y16 is not None:
+        assert e16 <= Y16_GATE
+    return e32
+
+
 def check_layer(lay, rows=None, label=""):
-    """Gate and tight check of asp_forward on one layer (optionally on sampled rows)."""
+    """Gates and tight checks of asp_forward on one layer (optionally on sampled rows)."""
     p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
     x = x_device(lay)
     y32 = host(p.forward(x, "f32"))
     y16 = host(p.forward(x, "bf16").float())
-    xs_ = lay.x if rows is None else lay.x[rows]
-    want = OA.forward(xs_, lay.w, lay.b, lay.s, lay.v)
-    sel = (lambda a: a) if rows is None else (lambda a: a[rows])
-    e32, e16 = rel_fro(sel(y32), want), rel_fro(sel(y16), want)
-    # tight: the same contraction on the device's own activation codes and u
-    xc, xs, u, _ = gpu_act_prep(lay)
-    pk = OA.pack_weight(lay.w, lay.s, lay.v)
-    u64 = None if u is None else sel(u).astype(np.float64)
-    mine = OA.output_from_codes(sel(xc), sel(xs), u64 if u64 is not None else np.zeros((len(want), 0)),
-                                pk["w_codes"], pk["w_scales"], pk["wv"], lay.b)
-    tight = rel_fro(sel(y32), mine)
-    act = OA.activation_side(xs_, lay.s, lay.v)
-    flips = np.mean(OF.unpack_codes(sel(xc)) != OF.unpack_codes(act["x_codes"]))
-    sflips = np.mean(sel(xs) != act["x_scales"])
-    print(f"{label} {lay.name}: rel err fp32 {e32:.3e} bf16 {e16:.3e} | vs own codes {tight:.2e}"
-          f" | codes off {flips:.2e} scales off {sflips:.2e}")
-    assert e32 <= 2e-3 and e16 <= 2e-3
-    assert tight <= 1e-5
-    assert flips <= 1e-3 and sflips <= 1e-3
+    oracle_gates(lay, y32, y16, rows, label, strict=True)
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
@@ -329,23 +552,13 @@ def test_forward_sampled_rows_of_mot_layers():
 def test_forward_maximum_k():
     """K at the device path's limit (2^20, so 8192 Hadamard blocks and 8
     slices of 131072 for u) with a ragged batch: every output against the
-    float64 oracle at the 2e-3 gate, and against the oracle's contraction of
+    float64 oracle at the fp32-output gate, and against the oracle's contraction of
     the device's own codes at the usual 1e-5 (each of the 8 waves of the
     split-K GEMM adds 8192 K-steps in float32)."""
     lay = synth.make_layer("max-K", 5, 1 << 20, 24, 32, seed=20, dtype="bf16")
     p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV)
     y32 = host(p.forward(x_device(lay), "f32"))
-    want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
-    e32 = rel_fro(y32, want)
-    xc, xs, u, _ = gpu_act_prep(lay)
-    pk = OA.pack_weight(lay.w, lay.s, lay.v)
-    mine = OA.output_from_codes(xc, xs, u.astype(np.float64), pk["w_codes"], pk["w_scales"],
-                                pk["wv"], lay.b)
-    tight = rel_fro(y32, mine)
-    act = OA.activation_side(lay.x, lay.s, lay.v)
-    flips = np.mean(OF.unpack_codes(xc) != OF.unpack_codes(act["x_codes"]))
-    print(f"K = 2^20: rel err {e32:.3e}, vs own codes {tight:.2e}, codes off {flips:.2e}")
-    assert e32 <= 2e-3 and tight <= 1e-5 and flips <= 1e-3
+    oracle_gates(lay, y32, label="K = 2^20", strict=True)
 
 
 def test_forward_large_batch_sampled_rows():
@@ -377,14 +590,13 @@ def test_empty_batch_is_a_noop():
 
 
 def test_no_bias_and_determinism():
-    lay = synth.workload(1)[1]
+    lay = dataclasses.replace(synth.workload(1)[1], b=None)
     p = PackedLayer.pack(lay.w, lay.s, lay.v, None, DEV)
     x = x_device(lay)
     y1 = host(p.forward(x, "f32"))
     y2 = host(p.forward(x, "f32"))
     assert np.array_equal(y1, y2)
-    want = OA.forward(lay.x, lay.w, None, lay.s, lay.v)
-    assert rel_fro(y1, want) <= 2e-3
+    oracle_gates(lay, y1, label="no bias", strict=True)
 
 
 def test_row_independence_bitwise():
@@ -421,7 +633,7 @@ def _group_layers(M, K, r, Ns, dtype, seed):
 ])
 def test_forward_group(M, K, r, Ns, dtype):
     """Each layer of a grouped call against the float64 oracle (fp32 output,
-    the 2e-3 gate) and against a lone asp_forward call; the bf16 output is the
+    the fp32-output gate) and against a lone asp_forward call; the bf16 output is the
     round-to-nearest-even cast of the fp32 one, bit for bit (the same
     accumulators, only the store differs)."""
     lays = _group_layers(M, K, r, Ns, dtype, seed=M + K + r)
@@ -431,10 +643,7 @@ def test_forward_group(M, K, r, Ns, dtype):
     y16 = [host(y.float()) for y in forward_group(packed, x, "bf16")]
     same_kernel = (B.asp_gemm_kernel_name(M, sum(Ns), K) == B.asp_gemm_kernel_name(M, Ns[0], K))
     for lay, p, a, b in zip(lays, packed, y32, y16):
-        want = OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v)
-        e = rel_fro(a, want)
-        print(f"group {Ns} {lay.name}: rel err fp32 {e:.3e}, bf16 {rel_fro(b, want):.3e}")
-        assert e <= 2e-3
+        oracle_gates(lay, a, b, label=f"group {Ns}", strict=False)
         assert np.array_equal(_rne_bf16(a), (b.view(np.uint32) >> 16).astype(np.uint16))
         alone = host(p.forward(x, "f32"))
         if same_kernel:
@@ -466,11 +675,7 @@ def test_forward_group_distinct_inputs(M, K, r, Ns):
     rows = None if M <= 512 else np.sort(np.random.default_rng(M).choice(M, 48, replace=False))
     for lay, p, x, y in zip(lays, packed, xs, ys):
         got = host(y)
-        xo = lay.x if rows is None else lay.x[rows]
-        want = OA.forward(xo, lay.w, lay.b, lay.s, lay.v)
-        e = rel_fro(got if rows is None else got[rows], want)
-        print(f"group with distinct inputs {Ns} {lay.name}: rel err {e:.3e}")
-        assert e <= 2e-3
+        oracle_gates(lay, got, rows=rows, label=f"group with distinct inputs {Ns}", strict=False)
         alone = host(p.forward(x, "f32"))
         if same_kernel:
             assert np.array_equal(got, alone)
@@ -524,7 +729,7 @@ def test_forward_graph_replays_match_eager():
                                  synth.make_layer("ragged", 77, 384, 200, 24, seed=18, dtype="f32")],
                          ids=lambda l: f"{l.name}-M{l.M}-K{l.K}-N{l.N}-r{l.r}")
 def test_forward_shared_weight_arm(lay):
-    """The shared-weight packing through the same device path: the 2e-3 gate
+    """The shared-weight packing through the same device path: the output gates
     against the float64 oracle of that arm, and 1e-5 against the oracle's
     contraction of the device's own activation codes and u."""
     p = PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV, form="shared")
@@ -535,16 +740,13 @@ def test_forward_shared_weight_arm(lay):
     e32, e16 = rel_fro(y32, want), rel_fro(y16, want)
     pk = OA.pack_weight(lay.w, lay.s, lay.v, form="shared")
     xc, xs, u, _ = gpu_act_prep(lay)
-    mine = OA.output_from_codes(xc, xs, u.astype(np.float64), pk["w_codes"], pk["w_scales"],
-                                pk["wv"], lay.b)
-    tight = rel_fro(y32, mine)
+    tight, _ = tight_checks(y32, xc, xs, u, pk, lay.b, lay.K, lay.r)
     dfl = rel_fro(host(PackedLayer.pack(lay.w, lay.s, lay.v, lay.b, DEV).forward(x, "f32")),
                   OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v, quantize=False))
     shr = rel_fro(y32, OA.forward(lay.x, lay.w, lay.b, lay.s, lay.v, quantize=False))
     print(f"shared arm {lay.name}: vs oracle fp32 {e32:.2e} bf16 {e16:.2e}, own codes {tight:.1e}; "
           f"error vs the unquantised layer: shared {shr:.3e}, deflated {dfl:.3e}")
-    assert e32 <= 2e-3 and e16 <= 2e-3
-    assert tight <= 1e-5
+    assert e32 <= Y32_GATE and e16 <= Y16_GATE
 
 
 # ------------------------------------------------- per-layer smoothing search

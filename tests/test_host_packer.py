@@ -136,44 +136,50 @@ def test_packer_rank_zero_and_threads():
     assert np.array_equal(p1["w_scales"], o["w_scales"])
 
 
-def _bf16_pair_value(hi, lo):
+def _bf16_terms_value(*terms):
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return f(hi) + f(lo)
+    return sum(f(t) for t in terms)
 
 
 @pytest.mark.parametrize("K,r", [(512, 32), (384, 17), (256, 0), (1024, 64)])
 def test_prep_pack_constants(K, r):
-    """The prep constants reproduce 1/(s sqrt 128), diag(1/s) H V and V to ~2^-16."""
+    """The prep constants: 1/(s sqrt 128) as float64, diag(1/s) H V as three
+    bf16 terms to 2^-24 (each term the bf16 rounding of what the earlier ones
+    leave, so each cuts the remainder by 2^-8 at least), and V (float32) as
+    three bf16 terms exactly."""
     from oracle import hadamard as OH
     lay = synth.make_layer("p", 4, K, 16, r, seed=K + r, dtype="f32")
     pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
     B.asp_pack_prep(K, r, lay.s, lay.v, pack)
     up = lambda b: (b + 255) // 256 * 256
     rp32 = (r + 31) // 32 * 32
-    off_vth = up(4 * K)
-    off_vtl = off_vth + up(2 * rp32 * K)
-    off_vh = off_vtl + up(2 * rp32 * K)
-    off_vl = off_vh + up(2 * K * rp32)
-    assert pack.nbytes == off_vl + up(2 * K * rp32)
-    cvec = pack[:4 * K].view(np.float32)
-    want_c = (1.0 / (lay.s.astype(np.float64) * np.sqrt(128.0))).astype(np.float32)
+    off_c64 = up(4 * K)
+    off_vt = [off_c64 + up(8 * K) + t * up(2 * rp32 * K) for t in range(3)]
+    off_v = [off_vt[2] + up(2 * rp32 * K) + t * up(2 * K * rp32) for t in range(3)]
+    assert pack.nbytes == off_v[2] + up(2 * K * rp32)
+    cvec = pack[off_c64:off_c64 + 8 * K].view(np.float64)
+    want_c = 1.0 / (lay.s.astype(np.float64) * np.sqrt(128.0))
     assert np.array_equal(cvec, want_c)
+    assert not pack[:4 * K].any()           # the float32 1/s section is the SVDQuant arm's
     if r == 0:
         return
-    vth = pack[off_vth:off_vth + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
-    vtl = pack[off_vtl:off_vtl + 2 * rp32 * K].view(np.uint16).reshape(rp32, K)
-    vh = pack[off_vh:off_vh + 2 * K * rp32].view(np.uint16).reshape(K, rp32)
-    vl = pack[off_vl:off_vl + 2 * K * rp32].view(np.uint16).reshape(K, rp32)
+    vt = [pack[o:o + 2 * rp32 * K].view(np.uint16).reshape(rp32, K) for o in off_vt]
+    vv = [pack[o:o + 2 * K * rp32].view(np.uint16).reshape(K, rp32) for o in off_v]
     v64 = lay.v.astype(np.float64)
     vpp = OH.block_rotate(v64.T).T / lay.s.astype(np.float64)[:, None]   # diag(1/s) H V
-    got = _bf16_pair_value(vth[:r], vtl[:r]).T
-    assert np.abs(got - vpp).max() <= 2.0 ** -15 * np.abs(vpp).max()
-    assert np.all(vth[r:] == 0) and np.all(vtl[r:] == 0)
-    gotv = _bf16_pair_value(vh[:, :r], vl[:, :r])
-    assert np.abs(gotv - v64).max() <= 2.0 ** -15 * np.abs(v64).max()
-    assert np.all(vh[:, r:] == 0)
+    got = _bf16_terms_value(*[t[:r] for t in vt]).T
+    assert np.all(np.abs(got - vpp) <= 2.0 ** -24 * np.abs(vpp))
+    # each term is the bf16 rounding of the remainder (8 significant bits):
+    # hi alone is within 2^-8, hi + mid within 2^-16 (relative, elementwise)
+    hi = _bf16_terms_value(vt[0][:r]).T
+    assert np.all(np.abs(hi - vpp) <= 2.0 ** -8 * np.abs(vpp))
+    assert np.all(np.abs(_bf16_terms_value(vt[0][:r], vt[1][:r]).T - vpp) <= 2.0 ** -16 * np.abs(vpp))
+    assert all(np.all(t[r:] == 0) for t in vt)
+    gotv = _bf16_terms_value(*[t[:, :r] for t in vv])
+    assert np.array_equal(gotv, v64)                  # float32 V is held exactly
+    assert all(np.all(t[:, r:] == 0) for t in vv)
     # u from the constants equals the oracle's x_tilde V
     x = lay.x.astype(np.float64)
     from oracle import asp as OAsp
     act = OAsp.activation_side(lay.x, lay.s, lay.v)
-    assert np.abs(x @ got - act["u"]).max() <= 1e-4 * np.abs(act["u"]).max()
+    assert np.abs(x @ got - act["u"]).max() <= 1e-6 * np.abs(act["u"]).max()

@@ -21,6 +21,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // 16 bytes as a native vector: unlike HIP's uint4 (a struct of unions), it
 // stays in registers when carried around a loop
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef double f64x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1/sqrt(128), rounded to float32
 

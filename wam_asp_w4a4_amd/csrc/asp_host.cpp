@@ -80,6 +80,20 @@ static uint16_t bf16_from_double(double v) {
   return (uint16_t)(f32_bits((float)r) >> 16) | sign;
 }
 
+static double bf16_value(uint16_t b) { return (double)bits_f32((uint32_t)b << 16); }
+
+// v as the sum of three bf16 numbers, each the RNE bf16 rounding of what the
+// earlier ones leave (computed in float64, where every difference is exact
+// for the magnitudes met here): about 26 significant bits, and every float32
+// value exactly.
+void split_bf16x3(double v, uint16_t (&out)[kSplit]) {
+  double rest = v;
+  for (int t = 0; t < kSplit; ++t) {
+    out[t] = bf16_from_double(rest);
+    rest -= bf16_value(out[t]);
+  }
+}
+
 // In-place Sylvester-ordered Walsh-Hadamard transform of 128 doubles,
 // scaled by 1/sqrt(128).
 static void fwht128(double* a) {
@@ -200,28 +214,26 @@ int32_t asp_pack_prep(int64_t K, int32_t r, const float* s, const float* v, uint
       return fail(ASP_ERR_ARG, "s[%lld]=%g must be finite and > 0", (long long)k, (double)s[k]);
   const PrepPackLayout L = prep_pack_layout(K, r);
   memset(prep_pack, 0, L.total);
-  float* cvec = reinterpret_cast<float*>(prep_pack + L.cvec);
-  uint16_t* vth = reinterpret_cast<uint16_t*>(prep_pack + L.vt_hi);
-  uint16_t* vtl = reinterpret_cast<uint16_t*>(prep_pack + L.vt_lo);
-  uint16_t* vh = reinterpret_cast<uint16_t*>(prep_pack + L.v_hi);
-  uint16_t* vl = reinterpret_cast<uint16_t*>(prep_pack + L.v_lo);
+  double* cvec = reinterpret_cast<double*>(prep_pack + L.cvec64);
+  uint16_t* vt[kSplit];
+  uint16_t* vs[kSplit];
+  for (int t = 0; t < kSplit; ++t) {
+    vt[t] = reinterpret_cast<uint16_t*>(prep_pack + L.vt[t]);
+    vs[t] = reinterpret_cast<uint16_t*>(prep_pack + L.v[t]);
+  }
   const double root = sqrt(128.0);
-  for (int64_t k = 0; k < K; ++k) cvec[k] = (float)(1.0 / ((double)s[k] * root));
-  auto bf16_value = [](uint16_t b) { return (double)bits_f32((uint32_t)b << 16); };
+  for (int64_t k = 0; k < K; ++k) cvec[k] = 1.0 / ((double)s[k] * root);
   std::vector<double> col(K);
+  uint16_t parts[kSplit];
   for (int c = 0; c < r; ++c) {
     // V'' = diag(1/s) H V, one column at a time
     for (int64_t k = 0; k < K; ++k) col[k] = (double)v[k * r + c];
     for (int64_t b = 0; b < K; b += 128) fwht128(&col[b]);
     for (int64_t k = 0; k < K; ++k) {
-      const double vpp = col[k] / (double)s[k];
-      const uint16_t hi = bf16_from_double(vpp);
-      vth[(int64_t)c * K + k] = hi;
-      vtl[(int64_t)c * K + k] = bf16_from_double(vpp - bf16_value(hi));
-      const double vv = (double)v[k * r + c];
-      const uint16_t vhi = bf16_from_double(vv);
-      vh[k * L.rp32 + c] = vhi;
-      vl[k * L.rp32 + c] = bf16_from_double(vv - bf16_value(vhi));
+      split_bf16x3(col[k] / (double)s[k], parts);
+      for (int t = 0; t < kSplit; ++t) vt[t][(int64_t)c * K + k] = parts[t];
+      split_bf16x3((double)v[k * r + c], parts);
+      for (int t = 0; t < kSplit; ++t) vs[t][k * L.rp32 + c] = parts[t];
     }
   }
   return ASP_OK;

@@ -28,14 +28,22 @@ int32_t check_rank(int32_t r);
 // Byte layout of a layer's prep constants (written by asp_pack_prep on the
 // host, read by the activation-prep kernels).  Each section starts on a
 // 256-byte boundary.
-//   cvec   K float32          1 / (s_k * sqrt(128))
-//   vt_hi  rp32 x K bf16      V'' = diag(1/s) H V, transposed, high part
-//   vt_lo  rp32 x K bf16      V'' low part (V'' - hi, rounded to bf16)
-//   v_hi   K x rp32 bf16      V, high part
-//   v_lo   K x rp32 bf16      V, low part
-// with rp32 = r rounded up to 32 and the padding zero.
+//   cvec      K float32          the SVDQuant-style arm's 1 / s_k (unused by
+//                                the NVFP4 arm)
+//   cvec64    K float64          1 / (s_k * sqrt(128)), the NVFP4 arm's
+//                                smoothing and Hadamard normalisation
+//   vt[0..2]  rp32 x K bf16      V'' = diag(1/s) H V, transposed, as three
+//                                bf16 terms (hi, mid, lo: each the bf16
+//                                rounding of what the earlier terms leave)
+//   v[0..2]   K x rp32 bf16      V as three bf16 terms (exact for float32 V)
+// with rp32 = r rounded up to 32 and the padding zero.  Three bf16 terms hold
+// 24 or more significant bits, so products on bf16 MFMA reach float32
+// accuracy when every cross term of combined order <= 2 is formed.
+constexpr int kSplit = 3;
+
 struct PrepPackLayout {
-  size_t cvec, vt_hi, vt_lo, v_hi, v_lo, total;
+  size_t cvec, cvec64, vt[kSplit], v[kSplit], total;
+  size_t plane_bytes;  // distance between consecutive term planes (V'' and V alike)
   int rp16, rp32;
 };
 
@@ -45,12 +53,22 @@ inline PrepPackLayout prep_pack_layout(int64_t K, int32_t r) {
   L.rp16 = (r + 15) / 16 * 16;
   L.rp32 = (r + 31) / 32 * 32;
   L.cvec = 0;
-  L.vt_hi = up((size_t)K * 4);
-  L.vt_lo = L.vt_hi + up((size_t)L.rp32 * K * 2);
-  L.v_hi = L.vt_lo + up((size_t)L.rp32 * K * 2);
-  L.v_lo = L.v_hi + up((size_t)K * L.rp32 * 2);
-  L.total = L.v_lo + up((size_t)K * L.rp32 * 2);
+  L.cvec64 = up((size_t)K * 4);
+  size_t at = L.cvec64 + up((size_t)K * 8);
+  L.plane_bytes = up((size_t)L.rp32 * K * 2);  // rp32 x K and K x rp32 planes alike
+  for (int t = 0; t < kSplit; ++t) {
+    L.vt[t] = at;
+    at += L.plane_bytes;
+  }
+  for (int t = 0; t < kSplit; ++t) {
+    L.v[t] = at;
+    at += L.plane_bytes;
+  }
+  L.total = at;
   return L;
 }
+
+// v as three bf16 terms (host side of the prep and SVDQuant-style packers).
+void split_bf16x3(double v, uint16_t (&out)[kSplit]);
 
 }  // namespace asp

@@ -13,16 +13,21 @@
 //            the raw input: workgroup = 64 rows x one of S slices of K, the
 //            slice's V'' staged in LDS by direct global-to-LDS copies issued
 //            all at once, MFMA 16x16x32 bf16 with x exact in bf16 (an fp32 x
-//            split into bf16 high + low) and V'' high + low (about 16
-//            significant bits; the dropped low*low term lies below float32
-//            rounding).  Writes S partial sums of u.
+//            split exactly into three bf16 terms) and V'' as three bf16
+//            terms (hi, mid, lo; about 26 significant bits).  Every cross
+//            term of combined order <= 2 is formed (the dropped ones lie
+//            below 2^-26 of the product), so u is a float32-accurate
+//            product.  Writes S partial sums of u.
 //  k_prep_q  workgroup = 64 rows x one 128-column Hadamard block.  Each wave
 //            loads its 16 rows of x, the block's 1/(s sqrt 128), its share of
 //            the block's V rows and the S partial sums of u for its rows, all
 //            at once into registers; it transforms x while the rest arrives,
 //            puts V in LDS for the workgroup, adds the partial sums in a fixed
-//            order (so results are deterministic), then deflates on MFMA,
-//            quantises and stores.  For r == 0 it runs alone, without u and V.
+//            order (so results are deterministic), then deflates on MFMA
+//            (V and -u each as three bf16 terms, the six cross terms of
+//            order <= 2 summed from zero and added to x_tilde once, a
+//            float32-accurate x_tilde - u V^T), quantises and stores.  For
+//            r == 0 it runs alone, without u and V.
 //
 // S depends on K only, so a row's results do not depend on the batch it is in.
 #include "asp_device.h"
@@ -52,18 +57,25 @@ __device__ __forceinline__ void swap16(float& x, float& y) {
   y = bitsf(r[1]);
 }
 
-// The same exchange followed by the butterfly (a + b, a - b) of the pair that
-// now sits in one lane: one Sylvester stage across lanes.
-__device__ __forceinline__ void swap32_butterfly(float& x, float& y) {
-  swap32(x, y);
-  const float a = x, b = y;
+// The same exchanges on float64 values (each half separately), followed by
+// the butterfly (a + b, a - b) of the pair that now sits in one lane: one
+// Sylvester stage across lanes.
+__device__ __forceinline__ void swap32_butterfly(double& x, double& y) {
+  const u32x2_t xs = __builtin_bit_cast(u32x2_t, x), ys = __builtin_bit_cast(u32x2_t, y);
+  const auto lo = __builtin_amdgcn_permlane32_swap(xs[0], ys[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(xs[1], ys[1], false, false);
+  const double a = __builtin_bit_cast(double, u32x2_t{lo[0], hi[0]});
+  const double b = __builtin_bit_cast(double, u32x2_t{lo[1], hi[1]});
   x = a + b;
   y = a - b;
 }
 
-__device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
-  swap16(x, y);
-  const float a = x, b = y;
+__device__ __forceinline__ void swap16_butterfly(double& x, double& y) {
+  const u32x2_t xs = __builtin_bit_cast(u32x2_t, x), ys = __builtin_bit_cast(u32x2_t, y);
+  const auto lo = __builtin_amdgcn_permlane16_swap(xs[0], ys[0], false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(xs[1], ys[1], false, false);
+  const double a = __builtin_bit_cast(double, u32x2_t{lo[0], hi[0]});
+  const double b = __builtin_bit_cast(double, u32x2_t{lo[1], hi[1]});
   x = a + b;
   y = a - b;
 }
@@ -71,9 +83,14 @@ __device__ __forceinline__ void swap16_butterfly(float& x, float& y) {
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8_t, q); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t q) { return __builtin_bit_cast(bf16x8_t, q); }
 
-__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
-  hi = bf16_rne(v);
-  lo = bf16_rne(v - bits_f32((uint32_t)hi << 16));
+// A float32 value as three bf16 terms: each the RNE bf16 rounding of what the
+// earlier terms leave.  Both differences are exact in float32, and the third
+// term is exact too, so v == t[0] + t[1] + t[2] for every normal float32 v.
+__device__ __forceinline__ void split_bf16x3(float v, uint16_t (&t)[kSplit]) {
+  t[0] = bf16_rne(v);
+  const float r1 = v - bits_f32((uint32_t)t[0] << 16);
+  t[1] = bf16_rne(r1);
+  t[2] = bf16_rne(r1 - bits_f32((uint32_t)t[1] << 16));
 }
 
 // Raw x of one (16 rows, 128 columns) unit as this lane loads it: columns
@@ -176,7 +193,7 @@ __device__ __forceinline__ void XFrag<float>::load_lds(const u32x4_t* t, int q, 
 // column l%16, the same 8 columns).  Output lane layout: u row 4q + i, column
 // l%16.
 //
-// LDS per round: up to CHUNKS chunks (128-column blocks) of V''^T (hi and lo;
+// LDS per round: up to CHUNKS chunks (128-column blocks) of V''^T (three terms;
 // RP rows of 128 bf16 = 16 pieces of 16 bytes) and of every wave's x rows
 // (XStage), all staged at once with lds_copy16.  Piece p of V''^T row `row`
 // sits in slot p ^ (row & 15), so the 16 lanes of a quarter, which read the
@@ -192,7 +209,7 @@ constexpr int max_slices(int ks) { return ks <= 1 ? 8 : 4; }
 template <typename XT, int KS>
 struct UStage {
   static constexpr int RP = 32 * KS;
-  static constexpr int CHUNK_PIECES = 2 * RP * 16;            // hi + lo, 16 pieces per row
+  static constexpr int CHUNK_PIECES = kSplit * RP * 16;       // 3 terms, 16 pieces per row
   static constexpr int X_PIECES = 4 * XStage<XT>::PIECES;     // the 4 waves' x
   static constexpr int CHUNKS = 8192 / (CHUNK_PIECES + X_PIECES);  // up to 128 KB per round
   static_assert(CHUNKS >= 1, "one chunk must fit");
@@ -200,8 +217,7 @@ struct UStage {
 
 template <typename XT, int KS>
 __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int K, int r,
-                                            const uint16_t* __restrict__ vth,
-                                            const uint16_t* __restrict__ vtl,
+                                            const uint16_t* __restrict__ vt, int64_t tstride,
                                             float* __restrict__ u_part, int bps) {
   using St = UStage<XT, KS>;
   constexpr int RP = St::RP, CT = KS * 2, NC = St::CHUNKS;
@@ -223,13 +239,14 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
   const int ncmax = min(NC, bps);
   for (int rb = b0; rb < b1; rb += ncmax) {
     const int nc = min(ncmax, b1 - rb);
-    // stage chunks rb .. rb+nc-1: slot P = (chunk*2 + hl)*RP*16 + row*16 + slot
+    // stage chunks rb .. rb+nc-1: slot P = (chunk*3 + term)*RP*16 + row*16 + slot
     const int pieces = nc * St::CHUNK_PIECES;
     for (int base = 64 * wave; base < pieces; base += 256) {
       const int P = base + lane;
       const int c = P / St::CHUNK_PIECES, rem = P % St::CHUNK_PIECES;
-      const int hl = rem / (RP * 16), row = (rem / 16) % RP, slot = rem % 16;
-      const uint16_t* src = (hl ? vtl : vth) + (int64_t)row * K + (rb + c) * 128 + 8 * (slot ^ (row & 15));
+      const int term = rem / (RP * 16), row = (rem / 16) % RP, slot = rem % 16;
+      const uint16_t* src = vt + term * tstride + (int64_t)row * K + (rb + c) * 128 +
+                            8 * (slot ^ (row & 15));
       lds_copy16(src, &sv[base]);
     }
     u32x4_t* sx = sv + ncmax * St::CHUNK_PIECES;  // chunk c, wave w: sx + (4c + w) * PIECES
@@ -246,30 +263,37 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int piece = 8 * (g >> 1) + 2 * q + (g & 1);
-        bf16x8_t a_hi, a_lo;
+        // x as bf16 terms: one (exact) for bf16 x, three for float32 x
+        bf16x8_t xa[fp32_x ? kSplit : 1];
         if constexpr (!fp32_x) {
-          a_hi = as_bf16x8(xc.f[g]);
+          xa[0] = as_bf16x8(xc.f[g]);
         } else {
           float f[8];
           xc.get(g, f);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            uint16_t hi, lo;
-            split_bf16(f[e], hi, lo);
-            a_hi[e] = bf16_from_bits(hi);
-            a_lo[e] = bf16_from_bits(lo);
+            uint16_t t[kSplit];
+            split_bf16x3(f[e], t);
+#pragma unroll
+            for (int i = 0; i < kSplit; ++i) xa[i][e] = bf16_from_bits(t[i]);
           }
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int row = 16 * ct + l16;
           const int slot = row * 16 + (piece ^ (row & 15));
-          const bf16x8_t b_hi = as_bf16x8(ch[slot]);
-          const bf16x8_t b_lo = as_bf16x8(ch[RP * 16 + slot]);
-          ah[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, ah[ct], 0, 0, 0);
-          al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, al[ct], 0, 0, 0);
-          if constexpr (fp32_x)
-            al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b_hi, al[ct], 0, 0, 0);
+          bf16x8_t b[kSplit];
+#pragma unroll
+          for (int i = 0; i < kSplit; ++i) b[i] = as_bf16x8(ch[i * RP * 16 + slot]);
+          // hi * hi alone; the smaller cross terms (order 1 and 2) together
+          ah[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], b[0], ah[ct], 0, 0, 0);
+          al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], b[1], al[ct], 0, 0, 0);
+          al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0], b[2], al[ct], 0, 0, 0);
+          if constexpr (fp32_x) {
+            al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1], b[0], al[ct], 0, 0, 0);
+            al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1], b[1], al[ct], 0, 0, 0);
+            al[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2], b[0], al[ct], 0, 0, 0);
+          }
         }
       }
     }
@@ -288,13 +312,13 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
 // ---------------------------------------------------------------------------
 // k_prep_q.  Workgroup = 4 waves x 16 rows and one 128-column block.  Lane l
 // of wave w: row m0 + 16w + l%16, lane quarter q = l/16.
-//  staging:    the block's V rows (hi, lo; 128 rows of RP bf16 = PPR pieces
-//              of 16 bytes) with lds_copy16, piece p of row `row` in slot
+//  staging:    the block's V rows (three bf16 terms; 128 rows of RP bf16 =
+//              PPR pieces of 16 bytes each) through registers, piece p of row `row` in slot
 //              p ^ ((row / (16/PPR)) % PPR) -- the 16 lanes of a quarter read
 //              one piece of 16 consecutive rows and hit 16 different bank
-//              groups; 1/(s sqrt 128) of the block by ordinary loads.
+//              groups; 1/(s sqrt 128) (float64) of the block by ordinary loads.
 //  u:          the S partial sums for the wave's rows added in slice order.
-//  transform:  the lane's 32 values are columns 64*bb + 16*q + j (bb = 0..1,
+//  transform:  in float64; the lane's 32 values are columns 64*bb + 16*q + j (bb = 0..1,
 //              j = 0..15).  Column bits 0..3 (j) and 6 (bb) are butterflied in
 //              registers; bit 4 (lane bit q0) against register bit j2 with
 //              v_permlane16_swap, bit 5 (lane bit q1) against j3 with
@@ -302,8 +326,10 @@ __device__ __forceinline__ void prep_u_body(const XT* __restrict__ x, int M, int
 //              the register bit, leaving tile t = (j >> 2) + 4*bb, columns
 //              16t + 4q + (j & 3): the output layout of a 16x16 MFMA with the
 //              block's columns as its rows and the 16 rows of x as its columns.
-//  deflation:  acc_t += V[cols of tile t] (-u)^T, v_mfma_f32_16x16x32_bf16 with
-//              bf16 hi/lo splits (hi*hi + hi*lo + lo*hi).
+//  deflation:  d_t = V[cols of tile t] (-u)^T on v_mfma_f32_16x16x32_bf16,
+//              V and -u as three bf16 terms each (the six cross terms of
+//              order <= 2, from zero, smallest first); x_d = float32(x_tilde
+//              (float64) + d_t), one rounding.
 //  transpose:  two more swap stages (tile bit 2 with lane bit q1, tile bit 1
 //              with q0) give each lane the whole of tiles 2q and 2q+1, i.e. two
 //              complete NVFP4 blocks: column c of tile 2q+b sits in
@@ -339,41 +365,43 @@ struct QUnit {
   }
 };
 
-// 1/(s sqrt 128) of the lane's 32 columns 64*bb + 16*q + j of the block
-__device__ __forceinline__ void load_col_scales(const float* __restrict__ cvec, int col0, int q,
-                                                f32x4_t (&cq)[2][4]) {
+// 1/(s sqrt 128) (float64) of the lane's 32 columns 64*bb + 16*q + j of the block
+__device__ __forceinline__ void load_col_scales(const double* __restrict__ cvec, int col0, int q,
+                                                f64x2_t (&cq)[2][8]) {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      cq[bb][k] = reinterpret_cast<const f32x4_t*>(cvec + col0 + 64 * bb + 16 * q)[k];
+    for (int k = 0; k < 8; ++k)
+      cq[bb][k] = reinterpret_cast<const f64x2_t*>(cvec + col0 + 64 * bb + 16 * q)[k];
 }
 
-// The block's V rows (hi, lo) through registers, 16 bytes per thread and
-// copy; written to LDS by store_v.  (A pending direct global-to-LDS copy
-// would make the compiler wait for every load before the first use of any.)
+// The block's V rows (three bf16 terms) through registers, 16 bytes per
+// thread and copy; written to LDS by store.  (A pending direct global-to-LDS
+// copy would make the compiler wait for every load before the first use of
+// any.)
 template <int KS>
 struct VRows {
   static constexpr int RP = KS * 32;
   static constexpr int PPR = KS > 0 ? RP / 8 : 1;          // 16-byte pieces per V row
-  static constexpr int PIECES = KS > 0 ? 2 * 128 * PPR : 1;
+  static constexpr int TERM = 128 * PPR;                    // pieces per term plane
+  static constexpr int PIECES = KS > 0 ? kSplit * TERM : 1;
   static constexpr int RDIV = 16 / PPR;                     // rows sharing a swizzle key
   static constexpr int COPIES = KS > 0 ? PIECES / 256 : 1;
   static_assert(KS == 0 || PIECES % 256 == 0, "whole copies per thread");
   u32x4_t reg[COPIES];
-  // piece p of row `row` (hi rows first, then lo) sits in slot
-  // p ^ ((row / RDIV) % PPR): the 16 lanes of a quarter read one piece of 16
-  // consecutive rows and hit 16 different bank groups
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ vh,
-                                        const uint16_t* __restrict__ vl, int bq, int tid) {
+  // piece p of row `row` of term plane t sits in slot t * TERM + row * PPR +
+  // (p ^ ((row / RDIV) % PPR)): the 16 lanes of a quarter read one piece of
+  // 16 consecutive rows and hit 16 different bank groups
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ v, int64_t tstride, int bq,
+                                        int tid) {
     if constexpr (KS > 0) {
 #pragma unroll
       for (int j = 0; j < COPIES; ++j) {
         const int P = tid + 256 * j;
-        const int hl = P / (128 * PPR), row = (P / PPR) % 128, slot = P % PPR;
+        const int t = P / TERM, row = (P / PPR) % 128, slot = P % PPR;
         const int piece = slot ^ ((row / RDIV) % PPR);
-        reg[j] = *reinterpret_cast<const u32x4_t*>((hl ? vl : vh) +
-                                                   (int64_t)(bq * 128 + row) * RP + 8 * piece);
+        reg[j] = *reinterpret_cast<const u32x4_t*>(v + t * tstride + (int64_t)(bq * 128 + row) * RP +
+                                                   8 * piece);
       }
     }
   }
@@ -385,27 +413,27 @@ struct VRows {
   }
 };
 
-// Smoothing and the Sylvester transform of one unit: w[bb][j] is afterwards
-// column 16*t + 4*q + (j & 3) of the block, tile t = (j >> 2) + 4*bb.
+// Smoothing and the Sylvester transform of one unit, in float64 (x and
+// 1/(s sqrt 128) exact, every stage rounded to 53 bits, so the result is
+// x_tilde to far below a float32 ulp; it is rounded to float32 once, when the
+// deflation is added): w[bb][j] is afterwards column 16*t + 4*q + (j & 3) of
+// the block, tile t = (j >> 2) + 4*bb.
 template <typename XT>
-__device__ __forceinline__ void q_transform(const XFrag<XT>& xr, const f32x4_t (&cq)[2][4],
-                                            float (&w)[2][16]) {
+__device__ __forceinline__ void q_transform(const XFrag<XT>& xr, const f64x2_t (&cq)[2][8],
+                                            double (&w)[2][16]) {
   // column 64*bb + 16*q + j of the block times 1/(s sqrt 128); the scaling
   // is folded into the first butterfly stage (pairs j, j+1)
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    float cv[16], xv[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cv[4 * k + e] = cq[bb][k][e];
+    float xv[16];
     xr.get(2 * bb, xv);
     xr.get(2 * bb + 1, xv + 8);
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
-      const float t = xv[j + 1] * cv[j + 1];
-      w[bb][j] = __builtin_fmaf(xv[j], cv[j], t);
-      w[bb][j + 1] = __builtin_fmaf(xv[j], cv[j], -t);
+      const double c0 = cq[bb][j >> 1][0], c1 = cq[bb][j >> 1][1];
+      const double t = (double)xv[j + 1] * c1;
+      w[bb][j] = __builtin_fma((double)xv[j], c0, t);
+      w[bb][j + 1] = __builtin_fma((double)xv[j], c0, -t);
     }
   }
   // Sylvester butterflies on column bits 1..3 (j) and 6 (bb)
@@ -416,13 +444,13 @@ __device__ __forceinline__ void q_transform(const XFrag<XT>& xr, const f32x4_t (
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if ((j & hs) == 0) {
-          const float a = w[bb][j], c = w[bb][j + hs];
+          const double a = w[bb][j], c = w[bb][j + hs];
           w[bb][j] = a + c;
           w[bb][j + hs] = a - c;
         }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float a = w[0][j], c = w[1][j];
+    const double a = w[0][j], c = w[1][j];
     w[0][j] = a + c;
     w[1][j] = a - c;
   }
@@ -445,7 +473,7 @@ __device__ __forceinline__ void q_transform(const XFrag<XT>& xr, const f32x4_t (
 // transpose to whole NVFP4 blocks per lane, quantisation and the stores.
 // Row m of this lane (mc = min(m, M - 1)), block bq at column col0.
 template <typename XT, int KS, int SMAX>
-__device__ __forceinline__ void q_finish(float (&w)[2][16], const QUnit<XT, KS, SMAX>& U, int S,
+__device__ __forceinline__ void q_finish(const double (&w)[2][16], const QUnit<XT, KS, SMAX>& U, int S,
                                          const u32x4_t* sv, int M, int K, int r, int bq, int m,
                                          int64_t mc, int q, int l16,
                                          uint8_t* __restrict__ codes,
@@ -455,9 +483,9 @@ __device__ __forceinline__ void q_finish(float (&w)[2][16], const QUnit<XT, KS, 
   constexpr int MS = QUnit<XT, KS, SMAX>::MS;
   const bool mok = m < M;
   const int col0 = bq * 128;
-  // -u for the 16 rows as the bf16 hi/lo B operand of the deflation MFMA:
-  // lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
-  bf16x8_t nuh[KS > 0 ? KS : 1], nul[KS > 0 ? KS : 1];
+  // -u for the 16 rows as the B operand of the deflation MFMA, three bf16
+  // terms: lane supplies row l16, k-elements 8q .. 8q+7 of each 32-step
+  bf16x8_t nu[kSplit][KS > 0 ? KS : 1];
   if constexpr (KS > 0) {
     float us[KS][8];
 #pragma unroll
@@ -485,38 +513,46 @@ __device__ __forceinline__ void q_finish(float (&w)[2][16], const QUnit<XT, KS, 
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint16_t hi, lo;
-        split_bf16(-us[kk][e], hi, lo);
-        nuh[kk][e] = bf16_from_bits(hi);
-        nul[kk][e] = bf16_from_bits(lo);
+        uint16_t t[kSplit];
+        split_bf16x3(-us[kk][e], t);
+#pragma unroll
+        for (int i = 0; i < kSplit; ++i) nu[i][kk][e] = bf16_from_bits(t[i]);
       }
   }
   f32x4_t acc[8];
+  if constexpr (KS == 0) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[t][e] = w[t >> 2][4 * (t & 3) + e];
-  if constexpr (KS > 0) {
+      for (int e = 0; e < 4; ++e) acc[t][e] = (float)w[t >> 2][4 * (t & 3) + e];
+  } else {
+    // -u V^T from zero: the six cross terms (V term i, u term j) with i + j
+    // <= 2, smallest first; x_tilde + that, rounded to float32 once
+    f32x4_t d[8];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      bf16x8_t a_hi[8], a_lo[8];
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int row = 16 * t + l16, piece = 4 * kk + q;
-        const int slot = row * VR::PPR + (piece ^ ((row / VR::RDIV) % VR::PPR));
-        a_hi[t] = as_bf16x8(sv[slot]);
-        a_lo[t] = as_bf16x8(sv[128 * VR::PPR + slot]);
+      for (int e = 0; e < 4; ++e) d[t][e] = 0.0f;
+#pragma unroll
+    for (int i = kSplit - 1; i >= 0; --i)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        bf16x8_t a[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = 16 * t + l16, piece = 4 * kk + q;
+          a[t] = as_bf16x8(sv[i * VR::TERM + row * VR::PPR + (piece ^ ((row / VR::RDIV) % VR::PPR))]);
+        }
+#pragma unroll
+        for (int j = kSplit - 1 - i; j >= 0; --j)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], nu[j][kk], d[t], 0, 0, 0);
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nuh[kk], acc[t], 0, 0, 0);
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], nul[kk], acc[t], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], nuh[kk], acc[t], 0, 0, 0);
-    }
+      for (int e = 0; e < 4; ++e) acc[t][e] = (float)(w[t >> 2][4 * (t & 3) + e] + (double)d[t][e]);
   }
   // lane quarters against tile bits: afterwards the lane holds tiles 2q and
   // 2q+1 whole
@@ -563,9 +599,8 @@ __device__ __forceinline__ void q_finish(float (&w)[2][16], const QUnit<XT, KS, 
 // one barrier once V is in LDS.
 template <typename XT, int KS, int SMAX>
 __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int K, int r,
-                                            const float* __restrict__ cvec,
-                                            const uint16_t* __restrict__ vh,
-                                            const uint16_t* __restrict__ vl,
+                                            const double* __restrict__ cvec,
+                                            const uint16_t* __restrict__ vv, int64_t tstride,
                                             const float* __restrict__ u_part, int S,
                                             uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales,
@@ -579,14 +614,14 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
   const int bq = blockIdx.y;
 
   QUnit<XT, KS, SMAX> U;
-  f32x4_t cq[2][4];
+  f64x2_t cq[2][8];
   VRows<KS> V;
   U.x.load(x + mc * K, bq * 128, q);
   load_col_scales(cvec, bq * 128, q, cq);
-  V.issue(vh, vl, bq, tid);
+  V.issue(vv, tstride, bq, tid);
   U.issue_u(M, u_part, S, mc, q);
   __builtin_amdgcn_sched_barrier(0);  // every load is issued before the transform
-  float w[2][16];
+  double w[2][16];
   q_transform(U.x, cq, w);
   V.store(sv, tid);
   __syncthreads();  // V is in LDS for every wave
@@ -597,11 +632,10 @@ __device__ __forceinline__ void prep_q_body(const XT* __restrict__ x, int M, int
 template <typename XT>
 struct PrepLayerArgs {
   const XT* x;
-  const float* cvec;
-  const uint16_t* vth;
-  const uint16_t* vtl;
-  const uint16_t* vh;
-  const uint16_t* vl;
+  const double* cvec;
+  const uint16_t* vt;  // V'' terms (u stage), term t at vt + t * tstride
+  const uint16_t* v;   // V terms (deflation), term t at v + t * tstride
+  int64_t tstride;     // elements between consecutive term planes
   float* u_part;
   uint8_t* xc;
   uint8_t* xs;
@@ -618,14 +652,14 @@ template <typename XT, int KS>
 __global__ void __launch_bounds__(256) k_prep_u(const PrepArgs<XT> a, int M, int K, int r,
                                                 int bps) {
   const PrepLayerArgs<XT>& L = a.l[blockIdx.z];
-  prep_u_body<XT, KS>(L.x, M, K, r, L.vth, L.vtl, L.u_part, bps);
+  prep_u_body<XT, KS>(L.x, M, K, r, L.vt, L.tstride, L.u_part, bps);
 }
 
 template <typename XT, int KS, int SMAX>
 __global__ void __launch_bounds__(256) k_prep_q(const PrepArgs<XT> a, int M, int K, int r,
                                                 int S) {
   const PrepLayerArgs<XT>& L = a.l[blockIdx.z];
-  prep_q_body<XT, KS, SMAX>(L.x, M, K, r, L.cvec, L.vh, L.vl, L.u_part, S, L.xc, L.xs, L.u,
+  prep_q_body<XT, KS, SMAX>(L.x, M, K, r, L.cvec, L.v, L.tstride, L.u_part, S, L.xc, L.xs, L.u,
                             L.pre);
 }
 
@@ -693,11 +727,10 @@ int32_t launch_prep(int stages, int n, const PrepCall* calls, int64_t M, int64_t
     const uint8_t* pack = calls[i].prep_pack;
     PrepLayerArgs<XT>& L = a.l[i];
     L.x = static_cast<const XT*>(calls[i].x);
-    L.cvec = reinterpret_cast<const float*>(pack + P.cvec);
-    L.vth = reinterpret_cast<const uint16_t*>(pack + P.vt_hi);
-    L.vtl = reinterpret_cast<const uint16_t*>(pack + P.vt_lo);
-    L.vh = reinterpret_cast<const uint16_t*>(pack + P.v_hi);
-    L.vl = reinterpret_cast<const uint16_t*>(pack + P.v_lo);
+    L.cvec = reinterpret_cast<const double*>(pack + P.cvec64);
+    L.vt = reinterpret_cast<const uint16_t*>(pack + P.vt[0]);
+    L.v = reinterpret_cast<const uint16_t*>(pack + P.v[0]);
+    L.tstride = (int64_t)(P.plane_bytes / 2);
     L.u_part = static_cast<float*>(calls[i].scratch);
     L.xc = calls[i].x_codes;
     L.xs = calls[i].x_scales;

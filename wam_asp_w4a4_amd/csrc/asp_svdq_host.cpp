@@ -178,19 +178,18 @@ int32_t asp_svdq_pack_weight(int64_t N, int64_t K, int32_t r, const float* w, co
       }
     }
   });
-  // activation side: 1/s (float32), V'' = diag(1/s) V transposed, as bf16 hi + lo
+  // activation side: 1/s (float32), V'' = diag(1/s) V transposed, as three bf16 terms
   std::memset(prep, 0, P.total);
   float* cvec = reinterpret_cast<float*>(prep + P.cvec);
-  uint16_t* vth = reinterpret_cast<uint16_t*>(prep + P.vt_hi);
-  uint16_t* vtl = reinterpret_cast<uint16_t*>(prep + P.vt_lo);
+  uint16_t* vt[kSplit];
+  for (int t = 0; t < kSplit; ++t) vt[t] = reinterpret_cast<uint16_t*>(prep + P.vt[t]);
+  uint16_t parts[kSplit];
   for (int64_t k = 0; k < K; ++k) {
     const float rs = (float)(1.0 / (double)s[k]);
     cvec[k] = rs;
     for (int j = 0; j < r; ++j) {
-      const double vv = (double)v[k * r + j] * (double)rs;
-      const uint16_t hi = bf16_of_double(vv);
-      vth[(int64_t)j * K + k] = hi;
-      vtl[(int64_t)j * K + k] = bf16_of_double(vv - (double)bf16_value(hi));
+      split_bf16x3((double)v[k * r + j] * (double)rs, parts);
+      for (int t = 0; t < kSplit; ++t) vt[t][(int64_t)j * K + k] = parts[t];
     }
   }
   return ASP_OK;
