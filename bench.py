@@ -1,22 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the deflated-ASP NVFP4 W4A4 linear on one MI355X.
 
-One step = the whole per-call path (the two activation-prep kernels, then the
-4-bit GEMM with the low-rank/bias epilogue) for every layer of the workload;
-layers that read the same input (the attention projection pair) run as one
-group, each kernel launched once for the group, on inputs and
-packed weights already resident in HBM.  The weight packing is offline (once
-per layer) and outside the timed region.  Steps rotate through replicas of
-every buffer (>= 1 GiB in total) so that each step reads from HBM rather than
-from the 256 MB Infinity Cache.
+Default workload: the 600-layer two-expert set (30 blocks x 10 linears per
+expert; video d 3072 / ffn 14336 at M = 4096 tokens, rank 0; action d 1024 /
+ffn 4096 at M = 256 tokens, rank 32).  One step = one denoising step: the
+whole per-call path (activation prep, then the 4-bit GEMM with its
+low-rank/bias epilogue) for all 600 linears as one stream, every weight and
+input resident in HBM (each layer its own, about 24 GB in all, so every read
+comes from HBM).  W eager warm-up steps, then exactly K steps captured in one
+HIP graph and replayed once between synchronize() and HIP events on the
+launch stream.  The same K steps then run once more, eagerly, with HIP
+events around every launch of the dominant kernel (the video expert's 4-bit
+GEMM): its per-launch durations in the step's own sequence give the roofline
+figure.
 
-Timing: W warm-up steps, then exactly K steps replayed from one HIP graph,
-bracketed by synchronize() and HIP events on the launch stream.  For the
-roofline figure each kernel is then timed alone: a graph of its launches over
-the replicas, replayed between two events, gives its average duration.
+--workload 0..3 times one of the smaller workloads instead (layers that read
+one input run as one group; steps rotate through replicas of every buffer,
+>= 1 GiB, so reads come from HBM rather than the 256 MB Infinity Cache; each
+kernel is then also timed alone for its roofline figure).  --eigen, --svdq
+and --search time the adjacent parts.
 
-Prints one JSON line.  Default workload: the action-expert attention
-projection pair (two layers, M=256 tokens, K=N=1024, rank 32, bf16 in and out).
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -113,9 +117,12 @@ def roofline_of(nbytes, nflops, ms):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 10 denoising steps of the 600-layer set, or "
+                         "400 steps of a --workload)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", type=int, default=None, choices=[0, 1, 2, 3],
+                    help="time one of the smaller workloads instead of the 600-layer set")
     ap.add_argument("--min-replica-gib", type=float, default=1.0)
     ap.add_argument("--kernel-timing-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -130,14 +137,20 @@ def parse():
                     help="time the SVDQuant-style INT4 (group 64) W4A4 arm on the workload's "
                          "layer shapes instead of the deflated-ASP NVFP4 path")
     ap.add_argument("--mot", action="store_true",
-                    help="time the 600-layer two-expert set (30 blocks per expert, 10 linears "
-                         "each) as one stream of quantised linears per denoising step")
-    ap.add_argument("--mot-steps", type=int, default=10,
-                    help="denoising steps timed by --mot (the set's own count is 10)")
+                    help="the 600-layer two-expert set (the default workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (the reference "
                          "kernel that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    small = args.workload is not None or args.search or args.svdq
+    if args.workload is None:
+        args.workload = 1
+    if args.steps is None:
+        args.steps = 400 if small else 10
+    if args.warmup is None:
+        args.warmup = 40 if small else 2
+    args.mot = not small and not args.eigen
+    return args
 
 
 def kernel_source_digest(kernel):
@@ -765,15 +778,31 @@ def svdq_bench(args, dev):
 MOT_GROUPS = [("self_attn.q", "self_attn.k", "self_attn.v"), ("self_attn.o",),
               ("cross_attn.q",), ("cross_attn.k", "cross_attn.v"), ("cross_attn.o",),
               ("ffn.0",), ("ffn.2",)]
+MOT_SLUG = "mot_600_layers"
+MOT_WORKLOAD = ("600-layer two-expert MoT set: 30 blocks x {self_attn q/k/v/o, cross_attn "
+                "q/k/v/o, ffn.0, ffn.2} per expert, run as one stream of quantised linears; "
+                "video d 3072, ffn 14336, M 4096, r 0 (smoothed + Hadamard NVFP4); action "
+                "d 1024, ffn 4096, M 256, r 32 (deflated ASP); one step = one denoising step "
+                "of all 600 linears; bf16 in and out")
 
 
 def mot_bench(args, dev):
     """The 600-layer two-expert set (video: d 3072, ffn 14336, M 4096, r 0;
     action: d 1024, ffn 4096, M 256, r 32) as one stream of quantised linears
-    per denoising step, all weights and inputs resident in HBM.  Every layer
-    has its own packed weight, prep pack, input and output; the inputs and
-    weights are random device tensors (the kernels' timing does not depend on
-    the values; parity on sampled layers of this set is in the GPU tests)."""
+    per denoising step, every weight and input resident in HBM.  Every layer
+    has its own packed weight, prep pack, input and output; the inputs are
+    random device tensors drawn like the workloads' (N(0, 1), a fraction of
+    channels scaled as outliers) and the packed weights random codes and
+    scales (the kernels' timing does not depend on the values; parity on
+    sampled layers of this set is in the GPU tests).
+
+    Timing: W eager warm-up steps, then K steps captured in one HIP graph and
+    replayed once between synchronisations and events (value).  The same K
+    steps then run once more eagerly with HIP events around every launch of
+    the video expert's 4-bit GEMM (the dominant kernel): the per-kernel
+    figures (roofline).  The experts' split comes from a graph of each expert's half alone.  The
+    rocprofv3 kernel trace of the same command gives the kernel's average
+    over the graph's and the eager pass's launches alike."""
     import torch
     from wam_asp_w4a4_amd import binding as B
     from wam_asp_w4a4_amd import synth
@@ -785,21 +814,26 @@ def mot_bench(args, dev):
         if (K, r) not in prep_host:
             rng = np.random.default_rng(K + r)
             s_ = (1.0 + rng.random(K)).astype(np.float32)
-            v = (rng.standard_normal((K, r)) / np.sqrt(K)).astype(np.float32) if r else None
+            v = np.linalg.qr(rng.standard_normal((K, r)))[0].astype(np.float32) if r else None
             pack = np.empty(B.asp_prep_pack_bytes(K, r), np.uint8)
             B.asp_pack_prep(K, r, s_, v, pack)
             prep_host[(K, r)] = torch.from_numpy(pack)
         return prep_host[(K, r)].to(dev)
 
     layers = {}
-    for (name, M, K, N, r, *_rest) in synth.mot_shapes():
-        x = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
+    for (name, M, K, N, r, frac, gain, gelu) in synth.mot_shapes():
+        x = torch.randn(M, K, generator=gen, device=dev)
+        if gelu:
+            x = torch.nn.functional.gelu(x)
+        n_out = int(round(frac * K))
+        if n_out:
+            x[:, torch.randperm(K, generator=gen, device=dev)[:n_out]] *= gain
         wv = None
         if r:
             wv = (torch.randn(N, r, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
             wv = wv.view(torch.int16).contiguous()
         layers[name] = {
-            "M": M, "K": K, "N": N, "r": r, "x": x, "wv": wv,
+            "M": M, "K": K, "N": N, "r": r, "x": x.to(torch.bfloat16), "wv": wv,
             "codes": torch.randint(0, 256, (N, K // 2), generator=gen, device=dev,
                                    dtype=torch.uint8),
             "scales": torch.randint(0x30, 0x40, (N, K // 16), generator=gen, device=dev,
@@ -807,6 +841,7 @@ def mot_bench(args, dev):
             "bias": torch.randn(N, generator=gen, device=dev) * 0.1,
             "prep": prep_pack(K, r),
             "y": torch.empty(M, N, dtype=torch.bfloat16, device=dev)}
+        del x
     # workspaces (no dependence on N), one set per (M, K, r), reused by every
     # call in stream order
     wspool = {}
@@ -826,84 +861,256 @@ def mot_bench(args, dev):
                 calls[expert].append([layers[f"{expert}.{blk}.{p}"] for p in grp])
     flops = {e: sum(layer_flops(L["M"], L["N"], L["K"], L["r"]) for c in cs for L in c)
              for e, cs in calls.items()}
+    hbm_bytes = {e: sum(layer_bytes(L["M"], L["N"], L["K"], L["r"], 2, 2) for c in cs for L in c)
+                 for e, cs in calls.items()}
+    gemm_kernel = {B.asp_gemm_kernel_name(c[0]["M"], sum(L["N"] for L in c), c[0]["K"])
+                   for c in calls["video"]}
+    assert len(gemm_kernel) == 1, gemm_kernel
+    gemm_kernel = gemm_kernel.pop()
 
-    def run(c):
+    def run(c, stages):
         L0 = c[0]
         ws = workspaces(L0["M"], L0["K"], L0["r"], len(c))
         B.asp_forward_group_stages(
-            7, [L["x"] for L in c], B.DTYPES["bf16"], L0["M"], L0["K"], L0["r"],
+            stages, [L["x"] for L in c], B.DTYPES["bf16"], L0["M"], L0["K"], L0["r"],
             [L["prep"] for L in c], [L["codes"] for L in c], [L["scales"] for L in c],
             [L["wv"] for L in c] if L0["r"] else None, [L["bias"] for L in c],
             [L["N"] for L in c], [L["y"] for L in c], B.DTYPES["bf16"], ws,
             [w.numel() for w in ws])
 
-    def step(experts):
-        for e in experts:
-            for c in calls[e]:
-                run(c)
+    def step(ev=None):
+        """One denoising step.  ev: one (a, b) pair of HIP events per video call,
+        recorded around its GEMM launch."""
+        for i, c in enumerate(calls["video"]):
+            if ev:
+                run(c, 3)               # the activation prep
+                ev[i][0].record()
+                run(c, 4)               # the 4-bit GEMM with its epilogue
+                ev[i][1].record()
+            else:
+                run(c, 7)
+        for c in calls["action"]:
+            run(c, 7)
 
-    step(("video", "action"))  # warm-up (code objects, launch paths)
-    torch.cuda.synchronize()
-    graphs = {}
-    for key, experts in (("both", ("video", "action")), ("video", ("video",)),
-                         ("action", ("action",))):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(experts)
-        graphs[key] = g
+    def new_events():
+        mk = lambda: torch.cuda.Event(enable_timing=True)
+        return [(mk(), mk()) for _ in calls["video"]]
+
+    K_steps, W_steps = args.steps, args.warmup
+    for _ in range(max(1, W_steps)):
+        step()
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-
-    def timed(g, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timing = "one HIP graph of K denoising steps, replayed once; events on the capture stream"
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(K_steps):
+            step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    # Per-launch durations: the same K steps once more, launched eagerly on the
+    # same stream with HIP events around every launch of the video GEMM and
+    # around each expert's half (torch declines external events on ROCm, and
+    # the runtime rejects event-record nodes in an instantiated graph, so the
+    # graph itself carries none).
+    evs = [new_events() for _ in range(K_steps)]
+    for i in range(K_steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    per_gemm = [a.elapsed_time(b) for ev in evs for a, b in ev]
+    kernel_timing = ("HIP events on the launch stream around every launch of the video GEMM in an "
+                     "eager pass of the same K steps right after the timed graph")
+    # each expert's half of a step alone, as a graph of its own (3 replays)
+    half_ms = {}
+    for expert in ("video", "action"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls[expert]:
+                run(c, 7)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(n):
+        for _ in range(3):
             g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    graphs["both"].replay()
-    ms = timed(graphs["both"], args.mot_steps)
-    ms_video = timed(graphs["video"], 3)
-    ms_action = timed(graphs["action"], 3)
+        half_ms[expert] = e0.elapsed_time(e1) / 3
+        del g
+    ms = ms_total / K_steps
+    ms_video, ms_action = half_ms["video"], half_ms["action"]
     total = flops["video"] + flops["action"]
-    tf_video = flops["video"] / (ms_video * 1e-3) / 1e12
+
+    # ---- the dominant kernel: the video expert's 4-bit GEMM, per launch
+    gflops = [sum(gemm_flops(L["M"], L["N"], L["K"], L["r"]) for L in c) for c in calls["video"]]
+    gbytes = [sum(gemm_bytes(L["M"], L["N"], L["K"], L["r"], 2) for L in c) for c in calls["video"]]
+    n_launch = len(per_gemm)
+    fl_all = sum(gflops) * K_steps
+    by_all = sum(gbytes) * K_steps
+    dur_ms = float(np.sum(per_gemm))
+    tfs = fl_all / (dur_ms * 1e-3) / 1e12
+    shapes = {}
+    for i, c in enumerate(calls["video"]):
+        key = f"{len(c)} x {c[0]['M']}x{c[0]['K']}->{c[0]['N']}"
+        d = shapes.setdefault(key, {"launches": 0, "ms": 0.0, "flops": 0})
+        for s_ in range(K_steps):
+            d["launches"] += 1
+            d["ms"] += per_gemm[s_ * len(calls["video"]) + i]
+            d["flops"] += gflops[i]
+    per_shape = {k: {"launches": v["launches"],
+                     "avg_launch_us": round(v["ms"] / v["launches"] * 1e3, 2),
+                     "TFLOPs": round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 1),
+                     "frac": round(v["flops"] / (v["ms"] * 1e-3) / 1e12 / F16_PEAK_TFLOPS, 4)}
+                 for k, v in shapes.items()}
+    roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tfs / F16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("k_gemm", MOT_SLUG),
+            "kernel": gemm_kernel,
+            "source_digest": kernel_source_digest("k_gemm"),
+            "avg_launch_us": round(dur_ms / n_launch * 1e3, 3),
+            "launches": n_launch,
+            "algorithmic_flops_per_launch": fl_all // n_launch,
+            "algorithmic_bytes_per_launch": by_all // n_launch,
+            "share_of_step": round(dur_ms / ms_total, 4),
+            "per_shape": per_shape,
+            "timing": kernel_timing,
+            "counters": measured_counters("k_gemm", MOT_SLUG),
+            "action_expert": {
+                "ms_per_step": round(ms_action, 4),
+                "algorithmic_bytes_per_step": hbm_bytes["action"],
+                "GBps": round(hbm_bytes["action"] / (ms_action * 1e-3) / 1e9, 1),
+                "hbm_frac": round(hbm_bytes["action"] / (ms_action * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "TFLOPs": round(flops["action"] / (ms_action * 1e-3) / 1e12, 2),
+                "note": "the 300 rank-32 layers at M = 256 (the north star's small-M target is "
+                        "60% of HBM bandwidth); bytes are the layers' algorithmic minimum"}}
     cpu = None
     if args.cpu_seconds > 0:
-        sample = [synth.make_layer("action.attn", 256, 1024, 1024, 32),
-                  synth.make_layer("video.attn (64 rows)", 64, 3072, 3072, 0,
-                                   outlier_frac=0.005, outlier_gain=30.0)]
-        cpu = cpu_baseline(sample, args.cpu_seconds)
-        cpu["sample"] = ("the oracle's rate on one action attention layer and 64 rows of a video "
-                         "attention layer (TFLOP/s, the same unit as value): " + cpu["sample"])
+        cpu = mot_cpu_baseline(args.cpu_seconds, total)
     out = {
-        "metric": "deflated-ASP NVFP4 linear effective TFLOP/s, 600-layer two-expert set, 1 MI355X",
+        "metric": METRIC,
         "value": round(total / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.mot_steps, "warmup": 1, "ms_per_step": round(ms, 4),
+        "steps": K_steps, "warmup": W_steps, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic (random device-resident inputs and packed weights)",
+        "data": "synthetic: random device-resident bf16 inputs (outlier channels as in the "
+                "workloads) and random packed NVFP4 weights",
         "config": {
-            "workload": "600-layer two-expert set: 30 blocks x {self_attn q/k/v/o, cross_attn "
-                        "q/k/v/o, ffn.0, ffn.2} per expert; video d 3072, ffn 14336, M 4096, "
-                        "r 0; action d 1024, ffn 4096, M 256, r 32; one step = all 600 linears",
-            "calls_per_step": sum(len(v) for v in calls.values()),
+            "workload": MOT_WORKLOAD,
+            "layers": 600, "calls_per_step": sum(len(v) for v in calls.values()),
             "flops_per_step": total,
+            "algorithmic_bytes_per_step": hbm_bytes["video"] + hbm_bytes["action"],
             "video_ms": round(ms_video, 4), "action_ms": round(ms_action, 4),
-            "video_TFLOPs": round(tf_video, 1),
+            "video_TFLOPs": round(flops["video"] / (ms_video * 1e-3) / 1e12, 1),
             "action_TFLOPs": round(flops["action"] / (ms_action * 1e-3) / 1e12, 2),
-            "timing": "one HIP graph per denoising step, replayed; events on the capture stream",
+            # the model card's inference schedule: the video expert once, the action
+            # expert for each of the 10 denoising steps (3 300 GEMM calls)
+            "schedule_video1_action10_ms": round(ms_video + 10 * ms_action, 3),
+            "operands": "NVFP4 (E2M1, block 16, E4M3 scales) decoded to exact fp16 for MFMA, "
+                        "fp32 accumulate",
+            "timing": timing,
         },
-        "roofline": {"bound": "mfma", "achieved": round(tf_video, 1), "peak": F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf_video / F16_PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "kernel": "all launches of the video expert's 300 layers (aggregate, not one "
-                               "kernel): prep and the 4-bit GEMM"},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_counters(kernel, slug):
+    """MFMA-utilisation figures from the committed counter summary, or None when
+    there is none or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{slug}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    if not sha or sha.group(1) != kernel_source_digest(kernel):
+        return None
+    out = {}
+    for key in ("mfma_busy_frac", "mfma_f16_mops_frac", "lds_bank_conflict_per_launch"):
+        m = re.search(rf"^{key}:\s*(\S+)", text, re.M)
+        if m:
+            out[key] = float(m.group(1))
+    return out or None
+
+
+def mot_cpu_baseline(budget_s, step_flops):
+    """The oracle on sampled layers of the 600-layer set, its FLOP rate taken
+    as the rate of the whole set (extrapolated by FLOPs, stated so), plus the
+    single-thread figure for workloads 0-2 and the weight-packing time of the
+    oracle against the C++ packer."""
+    from oracle import asp as oracle_asp
+    from wam_asp_w4a4_amd import synth
+    from wam_asp_w4a4_amd.layer import PackedLayer
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits, threads = None, 1
+    # one attention projection and both FFN layers of each expert at block 0,
+    # each on 256 rows (all of an action layer's; 256 of a video layer's 4096 --
+    # rows are independent, but the oracle decodes the whole weight once per
+    # call, which 256 rows amortise less than 4096)
+    pick = {"video.0.self_attn.q", "video.0.ffn.0", "video.0.ffn.2",
+            "action.0.self_attn.q", "action.0.ffn.0", "action.0.ffn.2"}
+    sample = []
+    for i, (name, M, K, N, r, frac, gain, gelu) in enumerate(synth.mot_shapes()):
+        if name in pick:
+            rows = 256
+            sample.append(synth.make_layer(name, rows, K, N, r, seed=synth.DEFAULT_SEED + i,
+                                           outlier_frac=frac, outlier_gain=gain, gelu=gelu))
+    # weight packing, timed once per sampled layer of each expert: oracle vs C++
+    pack = {}
+    for lay in (sample[1], sample[4]):   # video ffn.0 (14336 x 3072), action ffn.0
+        t0 = time.perf_counter()
+        oracle_asp.pack_weight(lay.w, lay.s, lay.v)
+        t1 = time.perf_counter()
+        PackedLayer.pack_host(lay.w, lay.s, lay.v)
+        t2 = time.perf_counter()
+        pack[lay.name] = {"N": lay.N, "K": lay.K, "r": lay.r, "oracle_s": round(t1 - t0, 3),
+                          "cpp_packer_s": round(t2 - t1, 3)}
+    packed = [oracle_asp.pack_weight(l.w, l.s, l.v) for l in sample]
+    flops = sum(layer_flops(l.M, l.N, l.K, l.r) for l in sample)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for lay, pk in zip(sample, packed):
+            oracle_asp.forward(lay.x, lay.w, lay.b, lay.s, lay.v, packed=pk)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    rate = flops * n / el
+    # single-thread oracle on workloads 0-2 (one pass each)
+    single = {}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            for w in (0, 1, 2):
+                lays = synth.workload(w)
+                pks = [oracle_asp.pack_weight(l.w, l.s, l.v) for l in lays]
+                t0 = time.perf_counter()
+                for l, pk in zip(lays, pks):
+                    oracle_asp.forward(l.x, l.w, l.b, l.s, l.v, packed=pk)
+                dt = time.perf_counter() - t0
+                fl = sum(layer_flops(l.M, l.N, l.K, l.r) for l in lays)
+                single[f"workload_{w}"] = {"seconds": round(dt, 4),
+                                           "GFLOPs": round(fl / dt / 1e9, 3)}
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": (f"{n} passes over 6 sampled layers of the set (the self-attention q "
+                       "projection, ffn.0 and ffn.2 of block 0 of each expert; the video "
+                       f"layers on 256 of their 4096 rows), {el:.1f} s on {threads} BLAS "
+                       "threads, weights pre-packed; extrapolated by FLOPs to the whole "
+                       f"set: {step_flops / rate:.0f} s per denoising step"),
+            "single_thread": single,
+            "weight_pack_seconds": pack}
 
 
 def cpu_baseline(layers, budget_s):

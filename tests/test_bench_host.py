@@ -48,3 +48,27 @@ def test_traffic_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic(kernel, slug) is None
     f.unlink()
     assert bench.measured_traffic(kernel, slug) is None
+
+
+def test_counters_only_for_matching_sources(tmp_path, monkeypatch):
+    kernel, slug = "k_gemm", "probe_slug"
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    digest = bench.kernel_source_digest(kernel)
+    f = prof / f"counters_{kernel}_{slug}.md"
+    f.write_text(f"mfma_busy_frac: 0.4632\nlds_bank_conflict_per_launch: 9748480\nsource_digest: {digest}\n")
+    assert bench.measured_counters(kernel, slug) == {"mfma_busy_frac": 0.4632,
+                                                      "lds_bank_conflict_per_launch": 9748480.0}
+    f.write_text("mfma_busy_frac: 0.4632\nsource_digest: 0000000000000000\n")
+    assert bench.measured_counters(kernel, slug) is None
+
+
+def test_default_is_the_layer_set(monkeypatch):
+    # no flags: the 600-layer set, 10 denoising steps; --workload picks a small one
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert a.mot and a.steps == 10 and a.warmup == 2
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "3"])
+    a = bench.parse()
+    assert not a.mot and a.workload == 3 and a.steps == 400
