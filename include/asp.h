@@ -79,6 +79,11 @@ extern "C" {
 /* ABI revision of this header; bumps on any signature change. */
 int32_t asp_abi_version(void);
 
+/* Digest of the sources this library was built from (16 hex digits: sha256
+ * of csrc/ and include/, as the build computes it), so that a caller holding
+ * the sources can refuse a stale build.  Static text; never fails. */
+const char* asp_source_digest(void);
+
 /* Static text for a status code. */
 const char* asp_status_string(int32_t status);
 

@@ -39,10 +39,30 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert B.asp_abi_version() == B.ABI_VERSION == 7
+    assert B.asp_abi_version() == B.ABI_VERSION == 8
     assert B.asp_status_string(0) == "ASP_OK"
     assert B.asp_status_string(5) == "ASP_ERR_WORKSPACE"
     assert B.asp_status_string(99) == "ASP_ERR_UNKNOWN"
+
+
+def test_library_was_built_from_these_sources(tmp_path, monkeypatch):
+    """The digest compiled into the library matches the sources beside it, and
+    a changed source makes lib() refuse the build instead of loading it."""
+    from wam_asp_w4a4_amd import build as BB
+    assert B.asp_source_digest() == BB.source_digest()
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    for name in os.listdir(BB.CSRC):
+        (csrc / name).write_bytes(open(os.path.join(BB.CSRC, name), "rb").read())
+    with open(csrc / "asp_host.cpp", "a") as f:
+        f.write("\n// edited\n")
+    monkeypatch.setattr(BB, "CSRC", str(csrc))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="other sources"):
+        B.lib()
+    monkeypatch.undo()
+    B._lib = None
+    assert B.asp_abi_version() == 8
 
 
 def test_sizes_are_four_and_a_half_bits_per_weight():

@@ -774,3 +774,35 @@ def test_smoothing_search_against_oracle(lay, step):
     assert best == obest or omse[best] <= omse[obest] * (1 + 2e-3)
     assert (a, b) == cands[best]
 
+
+
+# ------------------------------------------------------ installed module
+
+
+def test_installed_two_layer_module_matches_oracle_per_layer():
+    """Two nn.Linear layers of a model swapped by install() for ASPLinear: each
+    layer's output (float32) against the float64 oracle on that layer's own
+    input, under the same gates as a lone forward; the model's output equals
+    the two modules applied in turn, bit for bit."""
+    from wam_asp_w4a4_amd.linear import ASPLinear, install
+    M, K, N1, N2 = 96, 512, 384, 256
+    l1 = synth.make_layer("lin.0", M, K, N1, 32, seed=71, dtype="f32")
+    # the second layer's input is the first one's float32 output (row-major,
+    # computed here by the oracle's unquantised layer for its smoothing vector)
+    h_ref = (l1.x.astype(np.float64) @ l1.w.T.astype(np.float64) + l1.b).astype(np.float32)
+    l2 = synth.make_layer("lin.1", M, N1, N2, 32, seed=72, dtype="f32", x=h_ref)
+    model = torch.nn.Sequential(torch.nn.Linear(K, N1), torch.nn.Linear(N1, N2)).to(DEV)
+    packed = {"0": PackedLayer.pack(l1.w, l1.s, l1.v, l1.b, DEV),
+              "1": PackedLayer.pack(l2.w, l2.s, l2.v, l2.b, DEV)}
+    assert install(model, packed) == ["0", "1"]
+    assert isinstance(model[0], ASPLinear) and isinstance(model[1], ASPLinear)
+    x = dev(l1.x)
+    h = model[0](x)
+    y = model[1](h)
+    oracle_gates(l1, host(h), label="installed", strict=True)
+    lay2 = dataclasses.replace(l2, x=host(h))
+    oracle_gates(lay2, host(y), label="installed", strict=True)
+    assert torch.equal(model(x), y)
+    # leading dimensions are kept: (2, 48, K) -> (2, 48, N2)
+    y3 = model(x.reshape(2, 48, K))
+    assert y3.shape == (2, 48, N2) and torch.equal(y3.reshape(M, N2), y)

@@ -149,7 +149,9 @@ def test_forward_matches_oracle(name, M, K, N, r, dtype):
     print(f"svdq forward {name} M={M} K={K} N={N} r={r}", flush=True)
     # the planted low-rank part covers the rank, so the top-r subspace has a gap
     lay = synth.make_svdq_layer(name, M, K, N, r, seed=M + K + N, dtype=dtype, planted=max(32, r))
-    v = SvdqLayer.right_basis(lay.w, lay.s, r)
+    info = {}
+    v = SvdqLayer.right_basis(lay.w, lay.s, r, info=info)
+    print(f"  basis: {info['iters']} products, largest relative residual {info['rel_residual']:.2e}")
     h = SvdqLayer.pack_host(lay.w, lay.s, r, v, lay.b)
     pk = SQ.pack_weight(lay.w, lay.s, r)
     diff = unpack_codes(h.codes, N, K).astype(np.int16) - pk["codes"]
@@ -169,6 +171,21 @@ def test_forward_matches_oracle(name, M, K, N, r, dtype):
     assert err <= 2e-3
     np.testing.assert_array_equal(yb.cpu().view(torch.int16).numpy().view(np.uint16),
                                   rne_bf16_bits(y.cpu().numpy()))
+
+
+def test_basis_convergence_is_checked():
+    """Too few products for the planted gap: with the iteration count capped
+    there, the packer's basis solve raises instead of returning an unresolved
+    subspace; uncapped, it doubles the count until the residuals fall below
+    the tolerance."""
+    print("svdq basis convergence check", flush=True)
+    lay = synth.make_svdq_layer("conv", 64, 1024, 512, 32, seed=5)
+    with pytest.raises(RuntimeError, match="did not converge"):
+        SvdqLayer.right_basis(lay.w, lay.s, 32, iters=1, max_iters=1, tol=1e-6)
+    info = {}
+    SvdqLayer.right_basis(lay.w, lay.s, 32, iters=1, info=info)
+    print(f"  converged after {info['iters']} products (residual {info['rel_residual']:.2e})")
+    assert info["iters"] > 1 and info["rel_residual"] <= 1e-3
 
 
 def test_forward_empty_and_deterministic():

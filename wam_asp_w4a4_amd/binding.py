@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libasp.so")
 
 ASP_F32 = 0
@@ -29,6 +29,7 @@ _i32, _i64, _sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_
 _psz = ctypes.POINTER(ctypes.c_size_t)
 SIGNATURES = {
     "asp_abi_version": (_i32, []),
+    "asp_source_digest": (ctypes.c_char_p, []),
     "asp_status_string": (ctypes.c_char_p, [_i32]),
     "asp_last_error": (ctypes.c_char_p, []),
     "asp_gemm_kernel_name": (ctypes.c_char_p, [_i64, _i64, _i64]),
@@ -79,7 +80,9 @@ class ASPError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libasp (raises if it has not been built)."""
+    """The loaded libasp.  Raises if it has not been built, if its ABI
+    revision differs from this binding's, or if it was built from sources
+    other than the ones beside it (a stale build)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -92,6 +95,12 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
         if handle.asp_abi_version() != ABI_VERSION:
             raise RuntimeError("libasp ABI version mismatch")
+        from .build import source_digest
+        built, current = handle.asp_source_digest().decode(), source_digest()
+        if built != current:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (digest {built}, "
+                               f"sources {current}): rebuild it with "
+                               "`python -m wam_asp_w4a4_amd.build`")
         _lib = handle
     return _lib
 
@@ -129,6 +138,10 @@ def _stream(stream, *tensors):
 
 def asp_abi_version() -> int:
     return lib().asp_abi_version()
+
+
+def asp_source_digest() -> str:
+    return lib().asp_source_digest().decode()
 
 
 def asp_status_string(status: int) -> str:

@@ -7,6 +7,7 @@ IEEE float32 division and exact comparisons.
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -36,6 +37,20 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-pthread",
               "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
+def source_digest() -> str:
+    """sha256 (first 16 hex digits) of every source the library is built from:
+    the files of csrc/ and include/ in name order.  Compiled into the library
+    (asp_source_digest) so that a stale build can be told from a fresh one."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".cpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def _run(cmd):
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if proc.returncode != 0:
@@ -47,6 +62,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libasp.so next to this file; returns its path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
+    digest = [f"-DASP_SOURCE_DIGEST=\"{source_digest()}\""]
     with tempfile.TemporaryDirectory(prefix="asp_build_") as tmp:
         objs = []
         jobs = []
@@ -56,7 +72,7 @@ def build(verbose: bool = False) -> str:
             if name.endswith(".hip"):
                 jobs.append([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj])
             elif name.endswith(".cpp"):
-                jobs.append(["g++", *HOST_FLAGS, "-c", src, "-o", obj])
+                jobs.append(["g++", *HOST_FLAGS, *digest, "-c", src, "-o", obj])
             else:
                 continue
             objs.append(obj)

@@ -162,7 +162,12 @@ using namespace asp;
 
 extern "C" {
 
-int32_t asp_abi_version(void) { return 7; }
+int32_t asp_abi_version(void) { return 8; }
+
+#ifndef ASP_SOURCE_DIGEST
+#define ASP_SOURCE_DIGEST "unknown"
+#endif
+const char* asp_source_digest(void) { return ASP_SOURCE_DIGEST; }
 
 const char* asp_status_string(int32_t status) {
   switch (status) {

@@ -14,6 +14,46 @@ import torch
 
 from . import binding as B
 
+_Y_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _check_x(x, K, device):
+    """x must be a 2-D (M, K) float32 or bfloat16 tensor on the weights' device."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch tensor")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"x must be float32 or bfloat16, not {x.dtype}")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be (M, {K}), got {tuple(x.shape)}")
+    if x.device != device:
+        raise ValueError(f"x is on {x.device}, the layer on {device}")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+
+
+def _check_y(y, M, N, y_dtype, device):
+    """A caller's y must be (M, N) of the dtype y_dtype names, on the device."""
+    if y_dtype not in _Y_DTYPES:
+        raise ValueError(f"y_dtype must be 'f32' or 'bf16', not {y_dtype!r}")
+    if y is None:
+        return
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be ({M}, {N}), got {tuple(y.shape)}")
+    if y.dtype != _Y_DTYPES[y_dtype]:
+        raise TypeError(f"y_dtype {y_dtype!r} needs a {_Y_DTYPES[y_dtype]} y, got {y.dtype}")
+    if y.device != device or not y.is_contiguous():
+        raise ValueError("y must be contiguous and on the layer's device")
+
+
+def _check_ws(ws, need, device):
+    """A caller's workspace: uint8, on the device, at least ``need`` bytes."""
+    if ws.dtype != torch.uint8:
+        raise TypeError(f"the workspace must be uint8 (its size is passed in bytes), not {ws.dtype}")
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("the workspace must be contiguous and on the layer's device")
+    if ws.numel() < need:
+        raise ValueError(f"the workspace holds {ws.numel()} bytes, the call needs {need}")
+
 
 @dataclass
 class PackedLayer:
@@ -80,16 +120,24 @@ class PackedLayer:
         n = B.asp_workspace_bytes(M, self.N, self.K, self.r)
         return torch.empty(max(n, 256), dtype=torch.uint8, device=self.w_codes.device)
 
+    @property
+    def device(self) -> torch.device:
+        return self.w_codes.device
+
     def forward(self, x: torch.Tensor, y_dtype: str = "f32", workspace=None, y=None,
                 stream=None) -> torch.Tensor:
+        """y = the layer applied to x (M x K, float32 or bfloat16, on the layer's
+        device); y_dtype 'f32' or 'bf16'.  Shapes, dtypes and devices are
+        checked here: the C ABI sees only pointers."""
+        _check_x(x, self.K, self.device)
         M = x.shape[0]
+        _check_y(y, M, self.N, y_dtype, self.device)
         x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
-        if x.dtype not in (torch.bfloat16, torch.float32):
-            raise TypeError("x must be float32 or bfloat16")
         if y is None:
-            y = torch.empty((M, self.N), device=x.device,
-                            dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16)
+            y = torch.empty((M, self.N), device=x.device, dtype=_Y_DTYPES[y_dtype])
+        need = B.asp_workspace_bytes(M, self.N, self.K, self.r)
         ws = self.workspace(M) if workspace is None else workspace
+        _check_ws(ws, need, self.device)
         B.asp_forward(x, x_dtype, M, self.N, self.K, self.r, self.prep, self.w_codes,
                       self.w_scales, self.wv, self.bias, y, B.DTYPES[y_dtype], ws, ws.numel(),
                       stream)
@@ -99,19 +147,27 @@ class PackedLayer:
 def forward_group(layers, x, y_dtype: str = "f32", workspaces=None, ys=None, stream=None):
     """Run several layers with the same K and rank over one input x as one
     grouped call (one launch per kernel for the whole group)."""
-    M = x.shape[0]
-    if x.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("x must be float32 or bfloat16")
-    x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
     K, r = layers[0].K, layers[0].r
     if any(l.K != K or l.r != r for l in layers):
         raise ValueError("a group needs one K and one rank")
+    if any(l.device != layers[0].device for l in layers):
+        raise ValueError("a group's layers must sit on one device")
+    _check_x(x, K, layers[0].device)
+    M = x.shape[0]
+    x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
     if ys is None:
-        ys = [torch.empty((M, l.N), device=x.device,
-                          dtype=torch.float32 if y_dtype == "f32" else torch.bfloat16)
+        ys = [torch.empty((M, l.N), device=x.device, dtype=_Y_DTYPES.get(y_dtype, torch.float32))
               for l in layers]
+    if len(ys) != len(layers):
+        raise ValueError("one y per layer")
+    for l, y in zip(layers, ys):
+        _check_y(y, M, l.N, y_dtype, l.device)
     if workspaces is None:
         workspaces = [l.workspace(M) for l in layers]
+    if len(workspaces) != len(layers):
+        raise ValueError("one workspace per layer")
+    for l, w in zip(layers, workspaces):
+        _check_ws(w, B.asp_workspace_bytes(M, l.N, K, r), l.device)
     B.asp_forward_group([x] * len(layers), x_dtype, M, K, r, [l.prep for l in layers],
                         [l.w_codes for l in layers], [l.w_scales for l in layers],
                         [l.wv for l in layers] if r else None,
@@ -174,18 +230,42 @@ class SvdqLayer:
     bias: object = None
 
     @staticmethod
-    def right_basis(w, s, r, iters=24, block=64, seed=0, device="cuda"):
+    def right_basis(w, s, r, iters=24, block=64, seed=0, device="cuda", tol=1e-3,
+                    max_iters=384, info=None):
         """Top-r right singular vectors of W diag(s) (K x r float32): the Gram
-        matrix on the host, its top-r eigenspace on the device."""
+        matrix G on the host, its top-r eigenspace on the device.
+
+        Convergence is checked, not assumed: every returned Ritz pair must have
+        a residual |G v - theta v| <= tol * theta_1.  While one does not, the
+        iteration count doubles (from the same start block) up to max_iters;
+        a basis still short of that raises RuntimeError -- the top-r subspace
+        is then not resolved (the singular spectrum has no clear gap at r), so
+        no rank-r branch is well defined.  ``info`` (a dict) receives the
+        iteration count used and the largest relative residual."""
         w = np.ascontiguousarray(w, np.float32)
         s = np.ascontiguousarray(s, np.float32)
         N, K = w.shape
         g = np.empty((K, K), np.float32)
         B.asp_svdq_gram(N, K, w, s, g)
         v0 = np.random.default_rng(seed).standard_normal((K, block)).astype(np.float32)
-        v, _, _ = top_eigenspace(torch.from_numpy(g).to(device), torch.from_numpy(v0).to(device),
-                                 r, iters)
-        return v.cpu().numpy()
+        gd, vd = torch.from_numpy(g).to(device), torch.from_numpy(v0).to(device)
+        it = iters
+        while True:
+            v, evals, resid = top_eigenspace(gd, vd, r, it)
+            ev, rs = evals.cpu().numpy(), resid.cpu().numpy()
+            top = float(ev[0]) if ev.size else 0.0
+            worst = float(rs.max() / top) if top > 0 else 0.0
+            if info is not None:
+                info.update(iters=it, rel_residual=worst)
+            if not np.isfinite(worst):
+                raise RuntimeError("basis solve: non-finite eigenpairs (non-finite W or s)")
+            if worst <= tol:
+                return v.cpu().numpy()
+            if it >= max_iters:
+                raise RuntimeError(f"basis solve: the top-{r} subspace did not converge "
+                                   f"(largest residual {worst:.2e} of the leading eigenvalue "
+                                   f"after {it} products, tolerance {tol:.0e})")
+            it = min(2 * it, max_iters)
 
     @classmethod
     def pack_host(cls, w, s, r, v, bias=None):
@@ -208,14 +288,17 @@ class SvdqLayer:
                          t(self.prep), t(self.bias))
 
     def forward(self, x, y_dtype="f32", workspace=None, y=None, stream=None):
+        dev = self.codes.device
+        _check_x(x, self.K, dev)
         M = x.shape[0]
+        _check_y(y, M, self.N, y_dtype, dev)
         x_dtype = B.ASP_BF16 if x.dtype == torch.bfloat16 else B.ASP_F32
         nbytes = B.asp_svdq_workspace_bytes(M, self.N, self.K, self.r)
         if workspace is None:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+        _check_ws(workspace, nbytes, dev)
         if y is None:
-            y = torch.empty((M, self.N), dtype=torch.bfloat16 if y_dtype == "bf16" else torch.float32,
-                            device=x.device)
+            y = torch.empty((M, self.N), dtype=_Y_DTYPES[y_dtype], device=x.device)
         B.asp_svdq_forward(x, x_dtype, M, self.K, self.r, self.prep, self.codes, self.scales,
                            self.l1 if self.r else None, self.bias, self.N, y, B.DTYPES[y_dtype],
                            workspace, nbytes, stream)
