@@ -271,6 +271,31 @@ int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N,
                     int32_t y_dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Bytes of the device-resident workspace of asp_forward_noalloc (48 MiB per
+ * GPU): enough for M x K up to about 4096 x 14336 at r = 0. */
+#define ASP_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+/*
+ * asp_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace is a file-scope device array of
+ * ASP_NOALLOC_SCRATCH_BYTES, one per GPU, whose address the library takes on
+ * its first call on that GPU and which lives until the process ends; this
+ * call allocates and frees nothing.  Inputs, outputs, their layout and the
+ * result are exactly those of asp_forward (the same kernels, the same bits).
+ *   stream  selects the GPU (its device; NULL: the current device)
+ * Errors: as asp_forward, and ASP_ERR_WORKSPACE (before anything is enqueued)
+ * when asp_workspace_bytes(M, N, K, r) exceeds ASP_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other threads, before an earlier one has finished)
+ * race and corrupt each other's results; serialise them on one stream.
+ */
+int32_t asp_forward_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t N,
+                            int64_t K, int32_t r, const uint8_t* prep_pack,
+                            const uint8_t* w_codes, const uint8_t* w_scales,
+                            const uint16_t* wv, const float* bias, void* y,
+                            int32_t y_dtype, void* stream);
+
 /*
  * Several layers that share M, K and r (for example projections that read
  * the same input) in one call: each of the three kernels is launched once

@@ -64,6 +64,8 @@ SIGNATURES = {
     "asp_svdq_gemm": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i32, _p]),
     "asp_svdq_forward": (_i32, [_p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i64, _p, _i32,
                                 _p, _sz, _p]),
+    "asp_forward_noalloc": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
+                                   _i32, _p]),
     "asp_forward_group": (_i32, [_i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p,
                                  _i32, _p, _p, _p]),
     "asp_forward_group_stages": (_i32, [_i32, _i32, _p, _i32, _i64, _i64, _i32, _p, _p, _p, _p,
@@ -361,6 +363,13 @@ def asp_forward_group_stages(stages, x, x_dtype, M, K, r, prep_pack, w_codes, w_
         stages, n, arr(x), x_dtype, M, K, r, arr(prep_pack), arr(w_codes), arr(w_scales), arr(wv),
         arr(bias), ctypes.cast(nn, ctypes.c_void_p).value, arr(y), y_dtype, arr(workspace),
         ctypes.cast(nb, ctypes.c_void_p).value, _stream(stream, *y)))
+
+
+def asp_forward_noalloc(x, x_dtype, M, N, K, r, prep_pack, w_codes, w_scales, wv, bias, y,
+                        y_dtype, stream=None):
+    _check(lib().asp_forward_noalloc(_ptr(x), x_dtype, M, N, K, r, _ptr(prep_pack),
+                                     _ptr(w_codes), _ptr(w_scales), _ptr(wv), _ptr(bias), _ptr(y),
+                                     y_dtype, _stream(stream, y)))
 
 
 def asp_forward(x, x_dtype, M, N, K, r, prep_pack, w_codes, w_scales, wv, bias, y, y_dtype,

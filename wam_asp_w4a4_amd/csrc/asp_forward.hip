@@ -5,6 +5,8 @@
 // projections that read one input) runs as one launch per kernel.
 #include "asp_device.h"
 
+#include <mutex>
+
 namespace asp {
 namespace {
 
@@ -21,6 +23,46 @@ WsLayout ws_layout(int64_t M, int64_t K, int32_t r) {
   L.scratch = L.u + up((size_t)M * r * 4);
   L.total = L.scratch + up(act_prep_scratch_bytes(M, K, r));
   return L;
+}
+
+}  // namespace
+}  // namespace asp
+
+// The allocation-free forward's workspace: one array per GPU, held for the
+// life of the process.  In host code `scratch` names a host-side stand-in, so
+// its device address is taken with hipGetSymbolAddress once per device and
+// only that address is used.
+static __device__ __align__(256) uint8_t scratch[ASP_NOALLOC_SCRATCH_BYTES];
+
+namespace asp {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev`, resolved on the first call
+// for that device with the device current (the caller's current device is
+// restored), then cached.
+int32_t scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ASP_ERR_ARG, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return fail(ASP_ERR_HIP, "hipGetDevice failed");
+    if (prev != dev && hipSetDevice(dev) != hipSuccess)
+      return fail(ASP_ERR_HIP, "hipSetDevice(%d) failed", dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess || !p)
+      return fail(ASP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ASP_OK;
 }
 
 }  // namespace
@@ -93,6 +135,30 @@ int32_t asp_forward_group(int32_t n_layers, const void* const* x, int32_t x_dtyp
                           const size_t* workspace_bytes, void* stream) {
   return asp_forward_group_stages(7, n_layers, x, x_dtype, M, K, r, prep_pack, w_codes, w_scales,
                                   wv, bias, N, y, y_dtype, workspace, workspace_bytes, stream);
+}
+
+int32_t asp_forward_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t N, int64_t K,
+                            int32_t r, const uint8_t* prep_pack, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const uint16_t* wv, const float* bias,
+                            void* y, int32_t y_dtype, void* stream) {
+  clear_error();
+  ASP_TRY(gemm_check(M, N, K, r, y_dtype));
+  const size_t need = ws_layout(M, K, r).total;
+  if (need > (size_t)ASP_NOALLOC_SCRATCH_BYTES)
+    return fail(ASP_ERR_WORKSPACE,
+                "M=%lld K=%lld r=%d needs %zu bytes of workspace, above the %zu the "
+                "allocation-free forward holds; call asp_forward with a workspace",
+                (long long)M, (long long)K, r, need, (size_t)ASP_NOALLOC_SCRATCH_BYTES);
+  if (M == 0) return ASP_OK;
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ASP_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  void* ws = nullptr;
+  ASP_TRY(scratch_on(dev, &ws));
+  // the same launches as asp_forward; every byte of the workspace they read
+  // is written earlier in the same call, so nothing needs clearing
+  return asp_forward_group_stages(7, 1, &x, x_dtype, M, K, r, &prep_pack, &w_codes, &w_scales,
+                                  &wv, &bias, &N, &y, y_dtype, &ws, &need, stream);
 }
 
 int32_t asp_forward(const void* x, int32_t x_dtype, int64_t M, int64_t N, int64_t K, int32_t r,
