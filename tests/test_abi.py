@@ -129,7 +129,9 @@ def test_act_prep_pointer_validation():
 
 
 def test_gemm_kernel_name_follows_tile_choice():
-    assert B.asp_gemm_kernel_name(4096, 3072, 3072) == "k_gemm<4, 2, 2, 3>"
+    assert B.asp_gemm_kernel_name(4096, 3072, 3072) == "k_gemm_wb"
+    assert B.asp_gemm_kernel_name(4096, 3072, 384) == "k_gemm<4, 2, 2, 3>"   # K % 256 != 0
+    assert B.asp_gemm_kernel_name(2048, 3072, 3072) == "k_gemm<4, 2, 2, 3>"  # 128 tiles of 512 x 96
     assert B.asp_gemm_kernel_name(1024, 1024, 256) == "k_gemm<2, 2, 1, 1>"
     assert B.asp_gemm_kernel_name(256, 1024, 1024) == "k_gemm_sk<1, 1, 4>"
     assert B.asp_gemm_kernel_name(64, 64, 2048) == "k_gemm_sk<1, 1, 8>"

@@ -367,7 +367,11 @@ def gemm_cases():
             synth.make_layer("tile64-r16", 1024, 256, 1024, 16, seed=14, dtype="bf16"),
             synth.make_layer("tile256-r24", 4096, 256, 2000, 24, seed=15, dtype="bf16"),
             # 256 x 192 tiles whose last stage is half of one (K % 256 == 128)
-            synth.make_layer("tile256-k384", 4096, 384, 2000, 32, seed=19, dtype="bf16")]
+            synth.make_layer("tile256-k384", 4096, 384, 2000, 32, seed=19, dtype="bf16"),
+            # 512 x 96 tiles (k_gemm_wb): whole tiles with r = 32; ragged M and N
+            # with r % 8 != 0 (scalar low-rank loads) over a single stage
+            synth.make_layer("wb-r32", 4096, 512, 3072, 32, seed=21, dtype="bf16"),
+            synth.make_layer("wb-ragged-r33", 4000, 256, 3000, 33, seed=22, dtype="bf16")]
 
 
 @pytest.mark.parametrize("lay", gemm_cases(), ids=lambda l: f"{l.name}-M{l.M}-N{l.N}-K{l.K}-r{l.r}")
@@ -391,8 +395,9 @@ def test_gemm_on_oracle_codes(lay):
     assert rel_fro(got16, want) <= 2e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (1024, 1024, 256), (1024, 6144, 512)],
-                         ids=["split-k", "64x64-tiles", "256x192-tiles"])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 2048), (1024, 1024, 256), (1024, 6144, 512),
+                                   (4096, 3072, 768)],
+                         ids=["split-k", "64x64-tiles", "256x192-tiles", "512x96-tiles"])
 def test_gemm_every_scale_code(M, N, K):
     """Random codes under every finite E4M3 scale code (subnormal to 448) on
     both operands: the device's scale decoding and contraction against the

@@ -81,6 +81,128 @@ __device__ __forceinline__ uint32_t scale_pair_f16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
+// Low-rank branch straight from memory: bf16(u) (M x r) times wv^T (r x N)
+// in K-steps of 16 into the wave's accumulators, for its tile rows rb + 32 i +
+// l32 and columns cb + 32 j + l32.  Addresses are clamped (always valid) and
+// columns past r are zeroed after the load, so no lane-dependent branch sits
+// around a load; when r % 8 == 0 a lane's 8 columns are one 16-byte-aligned
+// piece (u and wv are) lying wholly inside or wholly past the row.
+template <int TM, int TN>
+__device__ __forceinline__ void lowrank_from_memory(f32x16_t (&acc)[TM][TN],
+                                                    const float* __restrict__ u,
+                                                    const uint16_t* __restrict__ wv, int M, int N,
+                                                    int r, int rb, int cb0, int half, int l32) {
+  for (int c0 = 0; c0 < r; c0 += 16) {
+    bf16x8_t la[TM], lb[TN];
+    const int cb = c0 + half * 8;                      // this lane's 8 columns
+    const bool in = cb < r;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float f[8];
+      const int64_t m = min(rb + i * 32 + l32, M - 1);
+      if ((r & 7) == 0) {
+        const float* pu = u + m * r + (in ? cb : 0);
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(pu);
+        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(pu + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = in ? a[e] : 0.0f;
+          f[4 + e] = in ? b[e] : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = u[m * r + min(cb + e, r - 1)];
+          f[e] = cb + e < r ? v : 0.0f;
+        }
+      }
+      la[i] = bf16x8_rne(f);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = min(cb0 + j * 32 + l32, N - 1);
+      if ((r & 7) == 0) {
+        u32x4_t q = *reinterpret_cast<const u32x4_t*>(wv + n * r + (in ? cb : 0));
+        if (!in) q = u32x4_t{0, 0, 0, 0};
+        lb[j] = __builtin_bit_cast(bf16x8_t, q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = wv[n * r + min(cb + e, r - 1)];
+          lb[j][e] = bf16_from_bits(cb + e < r ? v : (uint16_t)0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Bias and store of a workgroup's BM x BN tile (origin m0, n0); the wave holds
+// rows wr0 + 32 i and columns wc0 + 32 j of it.  Accumulator element v of lane
+// l is row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of its 32 x 32 tile.  A
+// bf16 output goes through LDS (smem, free once every wave is past its K loop:
+// the barrier below) so that each thread writes 16 consecutive bytes of a row.
+template <int TM, int TN, int BM, int BN, int NT>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TM][TN],
+                                           const float* __restrict__ bias, void* __restrict__ y,
+                                           int y_bf16, int M, int N, int m0, int n0, int wr0,
+                                           int wc0, int half, int l32, int tid, uint8_t* smem) {
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wc0 + j * 32 + l32;
+    bj[j] = (bias && col < N) ? bias[col] : 0.0f;
+  }
+  if (y_bf16) {
+    __syncthreads();
+    uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wr0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const int col = wc0 + j * 32 + l32;
+          ot[row * BN + col] = bf16_rne(acc[i][j][v] + bj[j]);
+        }
+    __syncthreads();
+    uint16_t* yo = reinterpret_cast<uint16_t*>(y);
+    constexpr int CHUNKS = BM * BN / 8;
+    for (int c = tid; c < CHUNKS; c += NT) {
+      const int row = c / (BN / 8), col = (c % (BN / 8)) * 8;
+      const int gm = m0 + row, gn = n0 + col;
+      if (gm >= M) continue;
+      const int64_t off = (int64_t)gm * N + gn;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + row * BN + col);
+      if (gn + 8 <= N && (off & 7) == 0) {
+        *reinterpret_cast<u32x4_t*>(yo + off) = val;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gn + e < N) yo[off + e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wc0 + j * 32 + l32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wr0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (row < M) reinterpret_cast<float*>(y)[(int64_t)row * N + col] = acc[i][j][v] + bj[j];
+        }
+    }
+  }
+}
+
 template <int WM, int WN, int TM, int TN>
 __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
                                           const uint8_t* __restrict__ xs,
@@ -292,136 +414,48 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
 
   // low-rank branch: bf16(u) (M x r) times wv^T (r x N), K-steps of 16.  The
   // operand rows come from the staging buffer filled during the last stage
-  // (lr_lds), else straight from memory (vector loads when r % 8 == 0).
-  const uint8_t* lrb = smem + (nk & 1) * C::STAGE;
+  // (lr_lds), else straight from memory.
+  const int wr0 = wm * TM * 32, wc0 = wn * TN * 32;
   if (lr_lds) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies have landed
     __syncthreads();                                   // and every other wave's
-  }
-  for (int c0 = 0; c0 < r; c0 += 16) {
-    bf16x8_t la[TM], lb[TN];
-    const int cb = c0 + half * 8;                      // this lane's 8 columns
-    const bool in = cb < r;
+    const uint8_t* lrb = smem + (nk & 1) * C::STAGE;
+    for (int c0 = 0; c0 < r; c0 += 16) {
+      bf16x8_t la[TM], lb[TN];
+      const int cb = c0 + half * 8;                    // this lane's 8 columns
+      const bool in = cb < r;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float f[8];
-      if (lr_lds) {
-        const int row = (wm * TM + i) * 32 + l32, p0 = cb >> 2;
+      for (int i = 0; i < TM; ++i) {
+        const int row = wr0 + i * 32 + l32, p0 = cb >> 2;
         const f32x4_t a = *reinterpret_cast<const f32x4_t*>(lrb + row * 128 + 16 * ((p0 ^ (row & 7)) & 7));
         const f32x4_t b = *reinterpret_cast<const f32x4_t*>(lrb + row * 128 + 16 * (((p0 + 1) ^ (row & 7)) & 7));
+        float f[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           f[e] = in ? a[e] : 0.0f;
           f[4 + e] = in ? b[e] : 0.0f;
         }
-      } else {
-        // clamped, always valid addresses, columns past r zeroed afterwards
-        // (no lane-dependent branch around a load); when r % 8 == 0 the 8
-        // columns lie wholly inside or wholly past the row
-        const int64_t m = min(m0 + (wm * TM + i) * 32 + l32, M - 1);
-        if ((r & 7) == 0) {
-          const float* pu = u + m * r + (in ? cb : 0);
-          const f32x4_t a = *reinterpret_cast<const f32x4_t*>(pu);
-          const f32x4_t b = *reinterpret_cast<const f32x4_t*>(pu + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f[e] = in ? a[e] : 0.0f;
-            f[4 + e] = in ? b[e] : 0.0f;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = u[m * r + min(cb + e, r - 1)];
-            f[e] = cb + e < r ? v : 0.0f;
-          }
-        }
+        la[i] = bf16x8_rne(f);
       }
-      la[i] = bf16x8_rne(f);
-    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if (lr_lds) {
-        const int row = (wn * TN + j) * 32 + l32;
+      for (int j = 0; j < TN; ++j) {
+        const int row = wc0 + j * 32 + l32;
         u32x4_t q = *reinterpret_cast<const u32x4_t*>(lrb + C::BM * 128 + row * 64 + 16 * (((cb >> 3) ^ (row & 3)) & 3));
         if (!in) q = u32x4_t{0, 0, 0, 0};
         lb[j] = __builtin_bit_cast(bf16x8_t, q);
-      } else {
-        const int64_t n = min(n0 + (wn * TN + j) * 32 + l32, N - 1);
-        if ((r & 7) == 0) {
-          u32x4_t q = *reinterpret_cast<const u32x4_t*>(wv + n * r + (in ? cb : 0));
-          if (!in) q = u32x4_t{0, 0, 0, 0};
-          lb[j] = __builtin_bit_cast(bf16x8_t, q);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint16_t v = wv[n * r + min(cb + e, r - 1)];
-            lb[j][e] = bf16_from_bits(cb + e < r ? v : (uint16_t)0);
-          }
-        }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
-  }
-
-  // bias and store; accumulator element v of lane l is row 8*(v/4) + 4*(l/32)
-  // + v%4 and column l%32 of its 32 x 32 tile
-  float bj[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + (wn * TN + j) * 32 + l32;
-    bj[j] = (bias && col < N) ? bias[col] : 0.0f;
-  }
-  if (y_bf16) {
-    // through LDS (the staging buffers are free once every wave is past the
-    // K loop), so that each thread writes 16 consecutive bytes of a row
-    static_assert(C::BM * C::BN * 2 <= C::LDS, "output tile must fit the staging LDS");
-    __syncthreads();
-    uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const int col = (wn * TN + j) * 32 + l32;
-          ot[row * C::BN + col] = bf16_rne(acc[i][j][v] + bj[j]);
-        }
-    __syncthreads();
-    uint16_t* yo = reinterpret_cast<uint16_t*>(y);
-    constexpr int CHUNKS = C::BM * C::BN / 8;
-    for (int c = tid; c < CHUNKS; c += C::NT) {
-      const int row = c / (C::BN / 8), col = (c % (C::BN / 8)) * 8;
-      const int gm = m0 + row, gn = n0 + col;
-      if (gm >= M) continue;
-      const int64_t off = (int64_t)gm * N + gn;
-      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + row * C::BN + col);
-      if (gn + 8 <= N && (off & 7) == 0) {
-        *reinterpret_cast<u32x4_t*>(yo + off) = val;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gn + e < N) yo[off + e] = (uint16_t)(val[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + (wn * TN + j) * 32 + l32;
-      if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + (wm * TM + i) * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (row < M) reinterpret_cast<float*>(y)[(int64_t)row * N + col] = acc[i][j][v] + bj[j];
-        }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], lb[j], acc[i][j], 0, 0, 0);
     }
+  } else {
+    lowrank_from_memory<TM, TN>(acc, u, wv, M, N, r, m0 + wr0, n0 + wc0, half, l32);
   }
+  static_assert(C::BM * C::BN * 2 <= C::LDS, "a bf16 output tile must fit the staging LDS");
+  store_tile<TM, TN, C::BM, C::BN, C::NT>(acc, bias, y, y_bf16, M, N, m0, n0, wr0, wc0, half, l32,
+                                          tid, smem);
 }
 
 // Per-layer pointers of a (grouped) launch; layer = blockIdx.y.  A layer
@@ -482,6 +516,198 @@ int32_t launch_gemm(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t 
                      0, stream, a, (int)M, (int)K, (int)r, (int)(y_dtype == ASP_BF16),
                      (int)tiles_m);
   return launch_status("gemm");
+}
+
+// ---------------------------------------------------------------------------
+// k_gemm_wb: the path for large layers with K % 256 == 0.  Eight waves stacked
+// in M (512 x 96 workgroup tile, 64 x 96 per wave).  The weight tile is
+// decoded once per workgroup into LDS as exact fp16 (in K order, rows padded
+// to 528 bytes so the 16-byte fragment reads of 16 consecutive rows hit
+// distinct banks) and shared by all eight waves; each wave streams its own
+// activation rows from memory straight into registers and decodes them there,
+// so no activation fragment is decoded twice and none passes through LDS.
+// Stages of 256 K-elements, double-buffered, one barrier each.
+//
+// K-slot mapping: per group of 64 K-elements (32 code bytes a row), lane half
+// h holds bytes 16h .. 16h+15 (elements 32h .. 32h+31: blocks 2h and 2h+1 of
+// the group) and K-step t of the group uses its word t (elements 32h + 8t ..
+// +7); the weight fragment of that K-step is the 16 bytes of fp16 at element
+// 64g + 32h + 8t of its row.  Products thus pair equal K indices, and a lane's
+// 8 values of a K-step share one block scale.
+namespace wb {
+constexpr int NW = 8, NT = NW * 64, TM = 2, TN = 3;
+constexpr int BM = NW * TM * 32, BN = TN * 32;         // 512 x 96
+constexpr int BK = 256, KST = BK / 16, GPS = BK / 64;  // 16 K-steps, 4 groups of 64 a stage
+constexpr int BROWB = BK * 2 + 16;                     // padded fp16 weight row (528 B)
+constexpr int STAGE = BN * BROWB;
+constexpr int LDS = 2 * STAGE;
+constexpr int B_PAIRS = BN * (BK / 16) / NT;           // (row, block) pairs a thread decodes
+static_assert(BN * (BK / 16) % NT == 0, "weight staging split");
+static_assert(BM * BN * 2 <= LDS, "a bf16 output tile must fit the staging LDS");
+}  // namespace wb
+
+__device__ __forceinline__ void gemm_wb_body(const uint8_t* __restrict__ xc,
+                                             const uint8_t* __restrict__ xs,
+                                             const float* __restrict__ u, int M, int N, int K,
+                                             int r, const uint8_t* __restrict__ wc,
+                                             const uint8_t* __restrict__ ws,
+                                             const uint16_t* __restrict__ wv,
+                                             const float* __restrict__ bias,
+                                             void* __restrict__ y, int y_bf16, int tiles_m,
+                                             int tiles_n) {
+  using wb::NT, wb::TM, wb::TN, wb::BM, wb::BN, wb::BK, wb::KST, wb::GPS, wb::BROWB, wb::STAGE,
+      wb::LDS, wb::B_PAIRS;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t KB = K / 2, KS = K / 16;
+
+  // this wave's activation rows (clamped to M - 1; their results are not stored)
+  const uint8_t* arow[TM];
+  const uint8_t* asrow[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t m = min(m0 + wave * TM * 32 + i * 32 + l32, M - 1);
+    arow[i] = xc + m * KB + 16 * half;
+    asrow[i] = xs + m * KS;
+  }
+  // weight staging: pair p = tid + j * NT is block p % 16 of tile row p / 16,
+  // so 16 consecutive threads read one row's 128 code bytes of the stage
+  const uint8_t* bsrc[B_PAIRS];
+  const uint8_t* bssrc[B_PAIRS];
+  int bdst[B_PAIRS];
+#pragma unroll
+  for (int j = 0; j < B_PAIRS; ++j) {
+    const int p = tid + j * NT, row = p >> 4, blk = p & 15;
+    const int64_t n = min(n0 + row, N - 1);
+    bsrc[j] = wc + n * KB + blk * 8;
+    bssrc[j] = ws + n * KS + blk;
+    bdst[j] = row * BROWB + blk * 32;
+  }
+  uint2 rb[B_PAIRS];
+  uint32_t rbs[B_PAIRS];
+  auto bload = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < B_PAIRS; ++j) {
+      rb[j] = *reinterpret_cast<const uint2*>(bsrc[j] + (int64_t)kc * (BK / 2));
+      rbs[j] = bssrc[j][(int64_t)kc * KST];
+    }
+  };
+  auto bstore = [&](int buf) {
+    uint8_t* base = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < B_PAIRS; ++j) {
+      const _Float16 sc = __builtin_bit_cast(half2_t, scale_pair_f16<false>(rbs[j]))[0];
+      *reinterpret_cast<half8_t*>(base + bdst[j]) = decode8(rb[j].x, sc);
+      *reinterpret_cast<half8_t*>(base + bdst[j] + 16) = decode8(rb[j].y, sc);
+    }
+  };
+  // a stage's activation codes (per group and fragment) and scales (per fragment)
+  u32x4_t ac[GPS][TM];
+  u32x4_t as[TM];
+  auto aload_group = [&](int kc, int g) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      ac[g][i] = *reinterpret_cast<const u32x4_t*>(arow[i] + (int64_t)kc * (BK / 2) + 32 * g);
+  };
+  auto aload_scales = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      as[i] = *reinterpret_cast<const u32x4_t*>(asrow[i] + (int64_t)kc * KST);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  int boff[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) boff[j] = (j * 32 + l32) * BROWB + 64 * half;
+
+  const int nk = K / BK;
+  bload(0);
+#pragma unroll
+  for (int g = 0; g < GPS; ++g) aload_group(0, g);
+  aload_scales(0);
+  bstore(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const uint8_t* base = smem + (kc & 1) * STAGE;
+    const bool more = kc + 1 < nk;
+    if (more) bload(kc + 1);
+    u32x4_t asc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) asc[i] = as[i];
+    if (more) aload_scales(kc + 1);
+    half8_t bf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = *reinterpret_cast<const half8_t*>(base + boff[j]);
+#pragma unroll
+    for (int g = 0; g < GPS; ++g) {
+      // this lane's two block scales of the group, as fp16
+      half2_t sp[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        sp[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i][g] >> (16 * half), 1.0f, false);
+      u32x4_t cur[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) cur[i] = ac[g][i];
+      if (more) aload_group(kc + 1, g);  // the group's registers, refilled for the next stage
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ks = 4 * g + t;
+        half8_t bn[TN];
+        if (ks + 1 < KST)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bn[j] = *reinterpret_cast<const half8_t*>(base + boff[j] + 128 * ((ks + 1) >> 2) +
+                                                      16 * ((ks + 1) & 3));
+        half8_t af[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = decode8(cur[i][t], sp[i][t >> 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        if (ks + 1 < KST)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bf[j] = bn[j];
+      }
+      // the other buffer held stage kc - 1, which every wave finished reading
+      // before the barrier that ended the previous stage
+      if (g == 2 && more) bstore((kc + 1) & 1);
+    }
+    if (more) __syncthreads();
+  }
+
+  const int wr0 = wave * TM * 32;
+  lowrank_from_memory<TM, TN>(acc, u, wv, M, N, r, m0 + wr0, n0, half, l32);
+  store_tile<TM, TN, BM, BN, NT>(acc, bias, y, y_bf16, M, N, m0, n0, wr0, 0, half, l32, tid, smem);
+}
+
+__global__ void __launch_bounds__(wb::NT)
+    k_gemm_wb(const GemmArgs a, int M, int K, int r, int y_bf16, int tiles_m) {
+  const GemmLayerArgs& L = a.l[blockIdx.y];
+  if ((int)blockIdx.x >= tiles_m * L.tiles_n) return;
+  gemm_wb_body(L.xc, L.xs, L.u, M, L.N, K, r, L.wc, L.ws, L.wv, L.bias, L.y, y_bf16, tiles_m,
+               L.tiles_n);
+}
+
+int32_t launch_gemm_wb(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r,
+                       int32_t y_dtype, hipStream_t stream) {
+  GemmArgs a;
+  int64_t tiles_m, max_tiles;
+  ASP_TRY(group_args(n, calls, M, wb::BM, wb::BN, a, tiles_m, max_tiles));
+  hipLaunchKernelGGL(k_gemm_wb, dim3((unsigned)max_tiles, (unsigned)n), dim3(wb::NT), 0, stream, a,
+                     (int)M, (int)K, (int)r, (int)(y_dtype == ASP_BF16), (int)tiles_m);
+  return launch_status("gemm_wb");
 }
 
 // ---------------------------------------------------------------------------
@@ -812,18 +1038,24 @@ int32_t gemm_check(int64_t M, int64_t N, int64_t K, int32_t r, int32_t y_dtype) 
   return ASP_OK;
 }
 
-enum GemmVariant { kGemm256x192, kGemm64x64, kGemmSplitK8, kGemmSplitK4, kGemmSplitK2,
-                   kGemmSplitK1 };
+enum GemmVariant { kGemm512x96, kGemm256x192, kGemm64x64, kGemmSplitK8, kGemmSplitK4,
+                   kGemmSplitK2, kGemmSplitK1 };
 
-// Tile choice.  Large layers: 256 x 192 workgroup tiles (256 tiles, one per
-// CU, for a 4096 x 3072 output) of 8 waves with 64 x 96 per-wave tiles: five
-// fragment decodes feed six MFMAs per K-step, and two waves per SIMD overlap
-// one wave's decode with the other's MFMAs.  Mid-size layers with at least
+// Tile choice.  Large layers with K % 256 == 0 and at least 256 tiles of 512
+// x 96 (one per CU for a 4096 x 3072 output): k_gemm_wb, whose weight tile is
+// decoded once per workgroup and whose activation fragments are decoded once,
+// by the one wave that uses them (two decodes per six MFMAs a K-step, plus the
+// workgroup's share of the weight decode).  Other large layers: 256 x 192
+// workgroup tiles of 8 waves with 64 x 96 per-wave tiles (five fragment
+// decodes feed six MFMAs per K-step); in both, two waves per SIMD overlap one
+// wave's decode with the other's MFMAs.  Mid-size layers with at least
 // 256 tiles of 64 x 64: those tiles, 4 waves each.  Fewer tiles (small M):
 // 32 x 32 tiles with K split over the workgroup's waves (k_gemm_sk), so that
 // more waves share the work and each one's chain of dependent K-steps is
 // shorter.
 GemmVariant gemm_variant(int64_t M, int64_t N, int64_t K) {
+  if (K % wb::BK == 0 && ((M + wb::BM - 1) / wb::BM) * ((N + wb::BN - 1) / wb::BN) >= 256)
+    return kGemm512x96;
   if (((M + 255) / 256) * ((N + 191) / 192) >= 128) return kGemm256x192;
   if (((M + 63) / 64) * ((N + 63) / 64) >= 256) return kGemm64x64;
   switch (sk_waves(K)) {
@@ -836,6 +1068,7 @@ GemmVariant gemm_variant(int64_t M, int64_t N, int64_t K) {
 
 const char* gemm_variant_name(GemmVariant v) {
   switch (v) {
+    case kGemm512x96: return "k_gemm_wb";
     case kGemm256x192: return "k_gemm<4, 2, 2, 3>";
     case kGemm64x64: return "k_gemm<2, 2, 1, 1>";
     case kGemmSplitK8: return "k_gemm_sk<1, 1, 8>";
@@ -867,6 +1100,7 @@ int32_t gemm_impl(int n, const GemmCall* calls, int64_t M, int64_t K, int32_t r,
   }
   // one kernel for the whole group, chosen for its total output width
   switch (gemm_variant(M, n_total, K)) {
+    case kGemm512x96: return launch_gemm_wb(n, calls, M, K, r, y_dtype, stream);
     case kGemm256x192: return launch_gemm<4, 2, 2, 3>(n, calls, M, K, r, y_dtype, stream);
     case kGemm64x64: return launch_gemm<2, 2, 1, 1>(n, calls, M, K, r, y_dtype, stream);
     case kGemmSplitK8: return launch_gemm_sk<1, 1, 8>(n, calls, M, K, r, y_dtype, stream);
