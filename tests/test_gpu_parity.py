@@ -659,7 +659,10 @@ def test_forward_group(M, K, r, Ns, dtype):
 
 @pytest.mark.parametrize("M,K,r,Ns", [(256, 1024, 32, (1024, 1024, 1024)),   # q, k, v of a block
                                       (300, 512, 0, (128, 96)),             # rank 0, ragged M
-                                      (4096, 256, 32, (1536, 1536))])       # 256 x 192 tiles
+                                      # the group on 512 x 96 tiles, each layer alone on 256 x 192
+                                      (4096, 256, 32, (1536, 1536)),
+                                      # group and lone calls both on 512 x 96 tiles (k_gemm_wb)
+                                      (4096, 512, 0, (3072, 3072))])
 def test_forward_group_distinct_inputs(M, K, r, Ns):
     """A grouped call whose layers read different inputs (the per-layer x
     pointers of the group): each layer against the float64 oracle on its own
