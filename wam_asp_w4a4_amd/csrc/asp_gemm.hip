@@ -141,11 +141,17 @@ __device__ __forceinline__ void lowrank_from_memory(f32x16_t (&acc)[TM][TN],
   }
 }
 
+// Bytes of LDS a bf16 output tile takes in store_tile: rows padded by 8
+// elements (16 bytes), so the two lane halves of a store, 4 rows apart, fall
+// in different banks.
+constexpr int out_tile_bytes(int BM, int BN) { return BM * (BN + 8) * 2; }
+
 // Bias and store of a workgroup's BM x BN tile (origin m0, n0); the wave holds
 // rows wr0 + 32 i and columns wc0 + 32 j of it.  Accumulator element v of lane
 // l is row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of its 32 x 32 tile.  A
 // bf16 output goes through LDS (smem, free once every wave is past its K loop:
-// the barrier below) so that each thread writes 16 consecutive bytes of a row.
+// the barrier below; out_tile_bytes of it) so that each thread writes 16
+// consecutive bytes of a row.
 template <int TM, int TN, int BM, int BN, int NT>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TM][TN],
                                            const float* __restrict__ bias, void* __restrict__ y,
@@ -168,7 +174,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TM][TN],
         for (int v = 0; v < 16; ++v) {
           const int row = wr0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
           const int col = wc0 + j * 32 + l32;
-          ot[row * BN + col] = bf16_rne(acc[i][j][v] + bj[j]);
+          ot[row * (BN + 8) + col] = bf16_rne(acc[i][j][v] + bj[j]);
         }
     __syncthreads();
     uint16_t* yo = reinterpret_cast<uint16_t*>(y);
@@ -178,7 +184,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TM][TN],
       const int gm = m0 + row, gn = n0 + col;
       if (gm >= M) continue;
       const int64_t off = (int64_t)gm * N + gn;
-      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + row * BN + col);
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ot + row * (BN + 8) + col);
       if (gn + 8 <= N && (off & 7) == 0) {
         *reinterpret_cast<u32x4_t*>(yo + off) = val;
       } else {
@@ -453,7 +459,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ xc,
   } else {
     lowrank_from_memory<TM, TN>(acc, u, wv, M, N, r, m0 + wr0, n0 + wc0, half, l32);
   }
-  static_assert(C::BM * C::BN * 2 <= C::LDS, "a bf16 output tile must fit the staging LDS");
+  static_assert(out_tile_bytes(C::BM, C::BN) <= C::LDS, "a bf16 output tile must fit the staging LDS");
   store_tile<TM, TN, C::BM, C::BN, C::NT>(acc, bias, y, y_bf16, M, N, m0, n0, wr0, wc0, half, l32,
                                           tid, smem);
 }
@@ -540,10 +546,9 @@ constexpr int BM = NW * TM * 32, BN = TN * 32;         // 512 x 96
 constexpr int BK = 256, KST = BK / 16, GPS = BK / 64;  // 16 K-steps, 4 groups of 64 a stage
 constexpr int BROWB = BK * 2 + 16;                     // padded fp16 weight row (528 B)
 constexpr int STAGE = BN * BROWB;
-constexpr int LDS = 2 * STAGE;
+constexpr int LDS = 2 * STAGE > out_tile_bytes(BM, BN) ? 2 * STAGE : out_tile_bytes(BM, BN);
 constexpr int B_PAIRS = BN * (BK / 16) / NT;           // (row, block) pairs a thread decodes
 static_assert(BN * (BK / 16) % NT == 0, "weight staging split");
-static_assert(BM * BN * 2 <= LDS, "a bf16 output tile must fit the staging LDS");
 }  // namespace wb
 
 __device__ __forceinline__ void gemm_wb_body(const uint8_t* __restrict__ xc,
