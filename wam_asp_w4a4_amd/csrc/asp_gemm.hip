@@ -9,21 +9,26 @@
 //
 // gfx950's block-scaled FP4 MFMA takes one power-of-two (E8M0) scale per 32
 // K-elements; NVFP4 has one E4M3 scale (4 significant bits) per 16.  Both
-// operands are therefore decoded in registers to exact fp16 (E2M1 value x
-// E4M3 scale has at most 6 significant bits and lies in [2^-10, 2688]) and
-// contracted on v_mfma_f32_32x32x16_f16: one MFMA K-step is exactly one NVFP4
-// block, and only fp32 accumulation order differs from exact arithmetic.  The
-// low-rank branch adds ceil(r/16) bf16 MFMA K-steps into the same
-// accumulators; bias and the output cast follow.
+// operands are therefore decoded to exact fp16 (E2M1 value x E4M3 scale has at
+// most 6 significant bits and lies in [2^-10, 2688]) and contracted on
+// v_mfma_f32_32x32x16_f16: one MFMA K-step is exactly one NVFP4 block, and only
+// fp32 accumulation order differs from exact arithmetic.  The low-rank branch
+// adds ceil(r/16) bf16 MFMA K-steps into the same accumulators; bias and the
+// output cast follow.
 //
-// Decoding a lane's 8 elements of a fragment costs 8 VALU instructions (four
-// 2-code conversions, four packed fp16 scale multiplies); two waves share each
-// SIMD so that one wave's decode overlaps the other's MFMAs.  Codes and scales are staged through double-buffered LDS in stages of
-// 256 K-elements (16 MFMA K-steps per workgroup barrier).  Tile rows are padded
-// so that the 32 rows a fragment reads hit distinct banks, and each lane reads
-// the one 32-bit code word it needs per K-step one step ahead of its use, so
-// the LDS latency hides behind the current K-step's decode and MFMAs.  Scale
-// bytes are converted to fp16 once, when a stage is written to LDS.
+// Decoding 8 elements costs 8 VALU instructions (four 2-code conversions, four
+// packed fp16 scale multiplies), so the kernels differ mainly in how often a
+// fragment is decoded:
+//  k_gemm_wb   (large layers, K % 256 == 0) decodes the weight tile once per
+//              workgroup into LDS as fp16 and each activation fragment once,
+//              in the registers of the one wave that uses it;
+//  k_gemm      (other large and mid-size layers) stages codes and scales in
+//              double-buffered LDS (256 K-elements a stage) and decodes both
+//              operands in every wave's registers;
+//  k_gemm_sk   (small M) splits K over the waves of a workgroup, each wave
+//              staging its own K range of both operands.
+// Two waves share each SIMD so that one wave's decode overlaps the other's
+// MFMAs.
 #include "asp_device.h"
 
 #include <algorithm>
