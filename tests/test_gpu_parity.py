@@ -545,9 +545,10 @@ def test_forward_workloads(cfg):
 
 
 def test_forward_sampled_rows_of_mot_layers():
-    # one attention and one FFN layer of each expert, oracle on sampled rows
-    # (rows are independent, so a row subset of y is the oracle of that subset)
-    idx = [0, 8, 9, 300 + 150, 300 + 158, 300 + 159]
+    # every projection of one block of each expert (video block 0, action block
+    # 15) and the action expert's last FFN pair, oracle on sampled rows (rows
+    # are independent, so a row subset of y is the oracle of that subset)
+    idx = list(range(10)) + list(range(450, 460)) + [598, 599]
     rng = np.random.default_rng(0)
     for lay in synth.mot_layer_set(only=set(idx)):
         rows = np.sort(rng.choice(lay.M, size=min(48, lay.M), replace=False))
