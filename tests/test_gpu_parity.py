@@ -368,10 +368,11 @@ def gemm_cases():
             synth.make_layer("tile256-r24", 4096, 256, 2000, 24, seed=15, dtype="bf16"),
             # 256 x 192 tiles whose last stage is half of one (K % 256 == 128)
             synth.make_layer("tile256-k384", 4096, 384, 2000, 32, seed=19, dtype="bf16"),
-            # 512 x 96 tiles (k_gemm_wb): whole tiles with r = 32; ragged M and N
-            # with r % 8 != 0 (scalar low-rank loads) over a single stage
+            # 512 x 96 tiles (k_gemm_wb): whole tiles with r = 32; M and N ragged
+            # inside a 32-row fragment and a 16-byte store (M % 32 == 31, N % 8
+            # == 7) with r % 8 != 0 (scalar low-rank loads) over a single stage
             synth.make_layer("wb-r32", 4096, 512, 3072, 32, seed=21, dtype="bf16"),
-            synth.make_layer("wb-ragged-r33", 4000, 256, 3000, 33, seed=22, dtype="bf16")]
+            synth.make_layer("wb-ragged-r33", 3999, 256, 2999, 33, seed=22, dtype="bf16")]
 
 
 @pytest.mark.parametrize("lay", gemm_cases(), ids=lambda l: f"{l.name}-M{l.M}-N{l.N}-K{l.K}-r{l.r}")
