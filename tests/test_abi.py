@@ -86,6 +86,27 @@ def test_bad_k_rejected_everywhere(K):
         assert ei.value.status == 2 and "K=" in str(ei.value)
 
 
+def test_noalloc_validates_before_touching_the_device():
+    """The allocation-free forward checks the shape and its workspace need
+    against the array's size before any device call (null pointers here)."""
+    def call(M, N, K, r, y_dtype=B.DTYPES["f32"]):
+        B.asp_forward_noalloc(None, B.ASP_BF16, M, N, K, r, None, None, None, None, None, None,
+                              y_dtype)
+    with pytest.raises(B.ASPError) as ei:       # 8192 x 14336: 66 MB of codes and scales
+        call(8192, 16, 14336, 0)
+    assert ei.value.status == 5 and "allocation-free" in str(ei.value)
+    with pytest.raises(B.ASPError) as ei:
+        call(4, 16, 100, 0)
+    assert ei.value.status == 2 and "K=" in str(ei.value)
+    with pytest.raises(B.ASPError) as ei:
+        call(4, 16, 128, 65)
+    assert ei.value.status == 2
+    with pytest.raises(B.ASPError) as ei:
+        call(4, 16, 128, 0, y_dtype=7)
+    assert ei.value.status == 1
+    assert B.asp_workspace_bytes(4096, 16, 14336, 0) <= 48 << 20   # the largest video input fits
+
+
 def test_bad_rank_and_dtype():
     with pytest.raises(B.ASPError) as ei:
         B.asp_packed_sizes(16, 128, 65)
