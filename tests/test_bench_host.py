@@ -72,3 +72,21 @@ def test_default_is_the_layer_set(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py", "--workload", "3"])
     a = bench.parse()
     assert not a.mot and a.workload == 3 and a.steps == 400
+
+
+def test_every_profile_summary_names_its_command_and_kernel_sources():
+    # each committed summary gives the rocprofv3 command that made it; the
+    # traffic and counter summaries also carry the figure bench.py reads and
+    # the digest of the kernel sources they were taken on
+    prof = os.path.join(ROOT, "profiles")
+    names = sorted(os.listdir(prof))
+    assert names, "no profile summaries"
+    for name in names:
+        text = open(os.path.join(prof, name)).read()
+        assert name.endswith(".md"), name
+        assert "rocprofv3 " in text, name
+        assert len(text) < 16_000, name
+        if name.startswith("traffic_"):
+            assert "traffic_bytes_per_launch:" in text and "source_digest:" in text, name
+        if name.startswith("counters_"):
+            assert "mfma_busy_frac:" in text and "source_digest:" in text, name
