@@ -665,10 +665,7 @@ __device__ __forceinline__ void gemm_wb_body(const uint8_t* __restrict__ xc,
 #pragma unroll
       for (int i = 0; i < TM; ++i)
         sp[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(asc[i][g] >> (16 * half), 1.0f, false);
-      u32x4_t cur[TM];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) cur[i] = ac[g][i];
-      if (more) aload_group(kc + 1, g);  // the group's registers, refilled for the next stage
+      const u32x4_t (&cur)[TM] = ac[g];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int ks = 4 * g + t;
@@ -690,6 +687,9 @@ __device__ __forceinline__ void gemm_wb_body(const uint8_t* __restrict__ xc,
 #pragma unroll
           for (int j = 0; j < TN; ++j) bf[j] = bn[j];
       }
+      // the group's registers, refilled for the next stage once its four
+      // K-steps are issued (no copy of the codes is kept meanwhile)
+      if (more) aload_group(kc + 1, g);
       // the other buffer held stage kc - 1, which every wave finished reading
       // before the barrier that ended the previous stage
       if (g == 2 && more) bstore((kc + 1) & 1);
