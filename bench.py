@@ -772,12 +772,14 @@ def svdq_bench(args, dev):
     print(json.dumps(out), flush=True)
 
 
-# Calls per block of one expert in the 600-layer set: projections that read
-# one input in a real block go together (self-attention q, k, v; cross-attention
-# k, v), the others alone.
-MOT_GROUPS = [("self_attn.q", "self_attn.k", "self_attn.v"), ("self_attn.o",),
-              ("cross_attn.q",), ("cross_attn.k", "cross_attn.v"), ("cross_attn.o",),
-              ("ffn.0",), ("ffn.2",)]
+# Calls per block of one expert in the 600-layer set, in the order a block's
+# data dependencies allow.  The first call holds every projection whose input
+# is ready when the block starts: self-attention q, k and v read the block's
+# input, and cross-attention k and v read the conditioning context, which no
+# projection of the block produces.  Each later projection reads the output of
+# the attention or residual step before it, so it is a call of its own.
+MOT_GROUPS = [("self_attn.q", "self_attn.k", "self_attn.v", "cross_attn.k", "cross_attn.v"),
+              ("self_attn.o",), ("cross_attn.q",), ("cross_attn.o",), ("ffn.0",), ("ffn.2",)]
 MOT_SLUG = "mot_600_layers"
 MOT_WORKLOAD = ("600-layer two-expert MoT set: 30 blocks x {self_attn q/k/v/o, cross_attn "
                 "q/k/v/o, ffn.0, ffn.2} per expert, run as one stream of quantised linears; "
@@ -851,7 +853,7 @@ def mot_bench(args, dev):
         if key not in wspool:
             nb = B.asp_workspace_bytes(M, 1, K, r)
             wspool[key] = [torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-                           for _ in range(3)]
+                           for _ in range(max(len(g) for g in MOT_GROUPS))]
         return wspool[key][:n]
 
     calls = {"video": [], "action": []}

@@ -675,6 +675,10 @@ def test_forward_group(M, K, r, Ns, dtype):
 
 
 @pytest.mark.parametrize("M,K,r,Ns", [(256, 1024, 32, (1024, 1024, 1024)),   # q, k, v of a block
+                                      # a block's first call in the benchmark: self-attention
+                                      # q, k, v and cross-attention k, v, two inputs
+                                      (256, 1024, 32, (1024,) * 5),
+                                      (4096, 3072, 0, (3072,) * 5),
                                       (300, 512, 0, (128, 96)),             # rank 0, ragged M
                                       # the group on 512 x 96 tiles, each layer alone on 256 x 192
                                       (4096, 256, 32, (1536, 1536)),
