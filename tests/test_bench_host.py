@@ -90,3 +90,35 @@ def test_every_profile_summary_names_its_command_and_kernel_sources():
             assert "traffic_bytes_per_launch:" in text and "source_digest:" in text, name
         if name.startswith("counters_"):
             assert "mfma_busy_frac:" in text and "source_digest:" in text, name
+
+
+def test_calls_of_a_block_follow_its_data_flow():
+    # what each projection of a transformer block reads: the block's input,
+    # the conditioning context, or the output of other projections (through
+    # attention, a residual add or an activation)
+    needs = {
+        "self_attn.q": set(), "self_attn.k": set(), "self_attn.v": set(),
+        "self_attn.o": {"self_attn.q", "self_attn.k", "self_attn.v"},
+        "cross_attn.q": {"self_attn.o"},
+        "cross_attn.k": set(), "cross_attn.v": set(),   # the context
+        "cross_attn.o": {"cross_attn.q", "cross_attn.k", "cross_attn.v"},
+        "ffn.0": {"cross_attn.o"},
+        "ffn.2": {"ffn.0"},
+    }
+    done = set()
+    seen = [p for call in bench.MOT_GROUPS for p in call]
+    assert sorted(seen) == sorted(needs), "every projection exactly once"
+    for call in bench.MOT_GROUPS:
+        for p in call:
+            assert needs[p] <= done, f"{p} runs before {needs[p] - done}"
+        done |= set(call)
+    # one call per dependency level: nothing that could join an earlier call
+    # is left for a later one
+    level = {}
+
+    def lvl(p):
+        if p not in level:
+            level[p] = 1 + max((lvl(q) for q in needs[p]), default=-1)
+        return level[p]
+    first = set(bench.MOT_GROUPS[0])
+    assert first == {p for p in needs if lvl(p) == 0}
