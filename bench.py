@@ -992,7 +992,7 @@ def mot_bench(args, dev):
                 "GBps": round(hbm_bytes["action"] / (ms_action * 1e-3) / 1e9, 1),
                 "hbm_frac": round(hbm_bytes["action"] / (ms_action * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "TFLOPs": round(flops["action"] / (ms_action * 1e-3) / 1e12, 2),
-                "note": "the 300 rank-32 layers at M = 256 (the north star's small-M target is "
+                "note": "the 300 rank-32 layers at M = 256 (the small-M target is "
                         "60% of HBM bandwidth); bytes are the layers' algorithmic minimum"}}
     cpu = None
     if args.cpu_seconds > 0:
