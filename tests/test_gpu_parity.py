@@ -69,7 +69,7 @@ def rel_fro(a, b):
 
 
 Y32_GATE = 1e-4   # fp32 output against the float64 oracle
-Y16_GATE = 2e-3   # bf16 output (spec tolerance; the cast alone costs ~1.7e-3)
+Y16_GATE = 2e-3   # bf16 output (the stated tolerance; the cast alone costs ~1.7e-3)
 
 
 def row_rel_max(a, b):
